@@ -1,0 +1,365 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused residual-add + RMSNorm row kernels on one MI355X.
+
+One step = one call of the fused add+RMSNorm entry point over the prefill
+workload 16384 rows x 8192 (bf16 x, f32 residual stream in and out, bf16
+weight, bf16 out), inputs resident in HBM.  The JSON line's ``value`` is the
+achieved HBM bandwidth in GB/s over the algorithmic bytes of one step (every
+input read once, every output written once, the weight once), from HIP events
+on the stream the kernel runs on.
+
+The same line carries:
+  * ``roofline``: the kernel against MI355X's 8 TB/s HBM peak, plus the HBM
+    bytes measured by rocprofv3 counters when a counter summary for the
+    current kernel sources is present under profiles/;
+  * ``cpu_baseline``: the CPU oracle (numpy, float64) timed on a bounded
+    sample of the same workload on this host;
+  * ``secondary``: the other workloads -- decode calls (us/call against an
+    empty kernel launched the same way), per-head QK-norm and the fp8-output
+    prefill (GB/s, with rotating buffer sets larger than the 256 MB
+    Infinity Cache so that every call streams from HBM).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused add+RMSNorm achieved HBM GB/s (% of peak) prefill; decode us/call"
+PEAK_HBM_GBS = 8000.0  # MI355X published HBM3E bandwidth, 8 TB/s
+MAIN = "prefill_16384x8192"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    """sha256 over the library's kernel and ABI sources (which counter summaries refer to)."""
+    h = hashlib.sha256()
+    paths = []
+    for d in (os.path.join(ROOT, "residual_add_rmsnorm_rows_amd", "csrc"), os.path.join(ROOT, "include")):
+        for name in sorted(os.listdir(d)):
+            if name.endswith((".hip", ".h", ".cpp")):
+                paths.append(os.path.join(d, name))
+    for p in paths:
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != source_digest():
+        return None
+    try:
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def rownorm_bytes(wl, rows=None) -> int:
+    """Algorithmic bytes: x, residual read once; out, residual_out written once; weight once; fp8 scale."""
+    import workloads as WL  # noqa: F401
+
+    r = wl.rows if rows is None else rows
+    size = {"bf16": 2, "f32": 4, "fp8_e4m3fn": 1}
+    per_row = wl.hidden * (size[wl.x_dtype] + size[wl.out_dtype])
+    if wl.res_dtype is not None:
+        per_row += 2 * wl.hidden * size[wl.res_dtype]
+    if wl.out_dtype == "fp8_e4m3fn":
+        per_row += 4
+    return r * per_row + wl.hidden * size[wl.w_dtype]
+
+
+def qknorm_bytes(wl) -> int:
+    size = {"bf16": 2, "f32": 4}
+    n = wl.tokens * (wl.num_q_heads + wl.num_k_heads) * wl.head_dim
+    return 2 * n * size[wl.dtype] + wl.head_dim * size[wl.w_dtype] * (2 if wl.num_k_heads else 1)
+
+
+class RowCall:
+    """Device buffers of one fused add+RMSNorm workload and a raw C-ABI call over them."""
+
+    def __init__(self, wl, inputs, sets: int = 1):
+        import torch
+        from residual_add_rmsnorm_rows_amd import _lib as L
+        from tests.gpu_util import TORCH_DTYPES, to_dev
+
+        self.wl = wl
+        self.L = L.lib()
+        x = to_dev(inputs["x"], wl.x_dtype)
+        res = None if inputs["residual"] is None else to_dev(inputs["residual"], wl.res_dtype)
+        self.w = to_dev(inputs["weight"], wl.w_dtype)
+        self.sets = []
+        for i in range(sets):
+            xs = x if i == 0 else x.clone()
+            rs = None if res is None else (res if i == 0 else res.clone())
+            out = torch.empty(x.shape, dtype=TORCH_DTYPES[wl.out_dtype], device="cuda")
+            ro = None if rs is None else torch.empty_like(rs)
+            sc = torch.empty(wl.rows, dtype=torch.float32, device="cuda") if wl.out_dtype == "fp8_e4m3fn" else None
+            self.sets.append((xs, rs, out, ro, sc))
+        self.flags = L.make_flags(wl.x_dtype, wl.res_dtype, wl.w_dtype, wl.out_dtype, wl.weight_plus_one)
+        self.i = 0
+
+    def __call__(self, stream: int) -> None:
+        xs, rs, out, ro, sc = self.sets[self.i]
+        self.i = (self.i + 1) % len(self.sets)
+        st = self.L.rmsnorm_fwd(xs.data_ptr(), None if rs is None else rs.data_ptr(), self.w.data_ptr(),
+                                out.data_ptr(), None if ro is None else ro.data_ptr(),
+                                None if sc is None else sc.data_ptr(), self.wl.rows, self.wl.hidden,
+                                self.wl.eps, self.flags, stream)
+        if st != 0:
+            from residual_add_rmsnorm_rows_amd._lib import check
+            check(st)
+
+
+def time_stream_loop(fn, steps: int, warmup: int) -> float:
+    """Average milliseconds per call of fn(stream) over `steps` back-to-back calls (HIP events)."""
+    import torch
+
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(warmup):
+        fn(stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn(stream)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def time_graph_loop(fn, calls: int = 200, replays: int = 10) -> float:
+    """Average microseconds per call with `calls` calls captured in one HIP graph."""
+    import torch
+
+    fn(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=s):
+        cs = torch.cuda.current_stream().cuda_stream
+        for _ in range(calls):
+            fn(cs)
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1000.0 / (replays * calls)
+
+
+def decode_metrics(name: str) -> dict:
+    import workloads as WL
+    from residual_add_rmsnorm_rows_amd import _lib as L
+
+    wl = WL.WORKLOADS[name]
+    call = RowCall(wl, WL.generate_rownorm(wl, seed=0))
+    lib = L.lib()
+
+    def empty(stream):
+        lib.rn_launch_empty(stream)
+
+    eager = time_stream_loop(call, 2000, 100) * 1000.0
+    eager_empty = time_stream_loop(empty, 2000, 100) * 1000.0
+    graph = time_graph_loop(call)
+    graph_empty = time_graph_loop(empty)
+    return {
+        "workload": wl.description, "rows": wl.rows, "hidden": wl.hidden,
+        "us_per_call_eager": round(eager, 3), "empty_us_per_call_eager": round(eager_empty, 3),
+        "ratio_eager": round(eager / eager_empty, 3),
+        "us_per_call_graph": round(graph, 3), "empty_us_per_call_graph": round(graph_empty, 3),
+        "ratio_graph": round(graph / graph_empty, 3),
+        "algorithmic_bytes": rownorm_bytes(wl),
+    }
+
+
+def stream_metrics(name: str, steps: int, warmup: int, sets: int) -> dict:
+    import workloads as WL
+
+    wl = WL.WORKLOADS[name]
+    call = RowCall(wl, WL.generate_rownorm(wl, seed=0), sets=sets)
+    ms = time_stream_loop(call, steps, warmup)
+    b = rownorm_bytes(wl)
+    return {"workload": wl.description, "us_per_call": round(ms * 1000, 3), "algorithmic_bytes": b,
+            "GBps": round(b / (ms * 1e-3) / 1e9, 1), "frac_of_peak": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "buffer_sets": sets}
+
+
+def qknorm_metrics(steps: int, warmup: int, sets: int = 8) -> dict:
+    import torch
+
+    import workloads as WL
+    from residual_add_rmsnorm_rows_amd import _lib as L
+    from tests.gpu_util import to_dev
+
+    wl = WL.WORKLOADS["qknorm_4096x32x128"]
+    inp = WL.generate_qknorm(wl, seed=0)
+    q0 = to_dev(inp["q"].reshape(wl.tokens, -1), wl.dtype)
+    w = to_dev(inp["q_weight"], wl.w_dtype)
+    bufs = [(q0 if i == 0 else q0.clone(), torch.empty_like(q0)) for i in range(sets)]
+    lib = L.lib()
+    flags = L.DTYPE_CODES[wl.dtype] | (L.DTYPE_CODES[wl.w_dtype] << L.RN_FLAGS_W_SHIFT)
+    state = {"i": 0}
+
+    def call(stream):
+        q, o = bufs[state["i"]]
+        state["i"] = (state["i"] + 1) % sets
+        st = lib.qknorm_fwd(q.data_ptr(), None, w.data_ptr(), None, o.data_ptr(), None, wl.tokens,
+                            wl.num_q_heads, 0, wl.head_dim, 0, 0, wl.eps, flags, stream)
+        if st != 0:
+            L.check(st)
+
+    ms = time_stream_loop(call, steps, warmup)
+    b = qknorm_bytes(wl)
+    return {"workload": wl.description, "us_per_call": round(ms * 1000, 3), "algorithmic_bytes": b,
+            "GBps": round(b / (ms * 1e-3) / 1e9, 1), "frac_of_peak": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "buffer_sets": sets}
+
+
+def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
+    """The oracle as it stands, timed on a bounded sample of the workload's rows."""
+    import numpy as np
+
+    import workloads as WL
+    from oracle import rownorm as O
+
+    chunk = 64
+    inputs = WL.generate_rownorm(wl, seed=0, row_range=(0, chunk))
+    X = inputs["x"]
+    RES = inputs["residual"]
+    W = inputs["weight"]
+    done_rows = 0
+    t0 = time.perf_counter()
+    while True:
+        x = O.decode(X, wl.x_dtype)
+        res = None if RES is None else O.decode(RES, wl.res_dtype)
+        w = O.decode(W, wl.w_dtype)
+        ref = O.rmsnorm_rows(x, w, wl.eps, 1.0 if wl.weight_plus_one else 0.0, residual=res,
+                             res_dtype=wl.res_dtype)
+        if res is not None:
+            O.encode(ref["h"], wl.res_dtype)
+        O.encode(ref["y"], wl.out_dtype)
+        done_rows += chunk
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    b = rownorm_bytes(wl, rows=done_rows)
+    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done_rows} rows x {wl.hidden} of the {wl.rows}-row workload "
+                      f"({chunk}-row batches, decode + residual add + norm + output rounding, float64 numpy, "
+                      f"one thread), {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only; the row kernels shard over rows with no exchange, "
+              "so a multi-GPU figure is the one-GPU figure times the GPU count and is not measured here. "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import workloads as WL
+    from residual_add_rmsnorm_rows_amd import _lib as L
+    import residual_add_rmsnorm_rows_amd as R
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    L.lib()  # fails loudly if the HIP library is not built
+    torch.cuda.set_device(0)
+
+    wl = WL.WORKLOADS[MAIN]
+    log(f"generating {MAIN}")
+    call = RowCall(wl, WL.generate_rownorm(wl, seed=0))
+    cfg = R.query_config(wl.rows, wl.hidden, x_dtype=wl.x_dtype, w_dtype=wl.w_dtype, out_dtype=wl.out_dtype,
+                         weight_plus_one=wl.weight_plus_one, num_cus=0)
+    log(f"timing {MAIN}: warmup {args.warmup}, steps {args.steps}, config {cfg}")
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(args.warmup):
+        call(stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        call(stream)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    nbytes = rownorm_bytes(wl)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"{MAIN}: {ms * 1000:.1f} us/step, {gbs:.1f} GB/s")
+    traffic = read_traffic(MAIN)
+    result = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{MAIN}: {wl.description}", "rows": wl.rows, "hidden": wl.hidden,
+                   "x": wl.x_dtype, "residual": wl.res_dtype, "weight": wl.w_dtype, "out": wl.out_dtype,
+                   "eps": wl.eps, "launch": cfg, "algorithmic_bytes_per_step": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic},
+    }
+    del call
+    torch.cuda.empty_cache()
+    if not args.no_secondary:
+        sec = {}
+        for name in ("decode_8x1024", "decode_256x4096"):
+            log(f"decode {name}")
+            sec[name] = decode_metrics(name)
+        log("qknorm_4096x32x128")
+        sec["qknorm_4096x32x128"] = qknorm_metrics(args.steps * 4, args.warmup)
+        log("prefill_fp8_8192x7168")
+        sec["prefill_fp8_8192x7168"] = stream_metrics("prefill_fp8_8192x7168", args.steps, args.warmup, sets=3)
+        result["secondary"] = sec
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

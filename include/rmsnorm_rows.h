@@ -1,0 +1,201 @@
+/*
+ * rmsnorm_rows.h -- C ABI of the MI355X (gfx950) row-normalization library.
+ *
+ * Operations
+ * ----------
+ * RMSNorm of a row x of length H with weight w:
+ *     y_i = (w_i + b) * x_i * rsqrt( (1/H) * sum_j x_j^2 + eps ),   b in {0, 1}
+ * as computed by the _qk_norm_kernel listing in the "QK Norm" section of
+ * "CuTeDSL at Perplexity" (Perplexity blog): sum of squares accumulated in
+ * float32, eps added to the mean inside the rsqrt, (w + WEIGHT_BIAS) times the
+ * normalized row, one cast back to the storage type.  The page's "Inference at
+ * Perplexity" section names the weight bias (plain w, or 1 + w) as a knob of
+ * RMS norm; here it is the RN_FLAG_WEIGHT_PLUS_ONE flag and is specialized at
+ * compile time.
+ *
+ * rmsnorm_fwd adds an optional residual stream in front of the norm (fused
+ * residual add): h = round_res(x + residual) is written to residual_out and the
+ * norm is taken over that rounded h.  It can also quantize y to OCP fp8 E4M3FN
+ * with one dynamic scale per row: scale = amax / 448, amax = max_i |y_i|,
+ * code_i = round_nearest_even(y_i / scale) saturated to +-448.  Neither the
+ * residual add nor the fp8 output is on the pages; both follow the plain
+ * reading stated for each entry point below.
+ *
+ * qknorm_fwd applies the same RMSNorm to every (token, head) row of Q and K
+ * over head_dim, with one weight vector per tensor shared by all heads, as in
+ * the "QK Norm" section's kernel (heads of Q first, then heads of K, per token).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are caller-owned DEVICE memory on the current HIP
+ *    device, row-major and contiguous unless a stride argument says otherwise,
+ *    and 16-byte aligned.  The library never allocates, frees or synchronizes;
+ *    work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    null stream).  The only global state is a per-device cache of the compute
+ *    unit count, filled on first use (thread-safe).  Entry points are
+ *    re-entrant.
+ *  - Arguments are checked on the host before any HIP call, so every error in
+ *    the table below is reported synchronously and without a GPU:
+ *        RN_ERR_INVALID_ARG  missing pointer, bad size, bad eps, unknown flag
+ *                            bits, inconsistent optional arguments;
+ *        RN_ERR_UNSUPPORTED  a dtype combination or size this build does not
+ *                            provide (e.g. H not a multiple of the 16-byte vector);
+ *        RN_ERR_MISALIGNED   a pointer or row stride that is not 16-byte aligned;
+ *        RN_ERR_HIP          a HIP runtime call failed (device query or launch).
+ *    A fault inside a kernel surfaces asynchronously, at the caller's next
+ *    synchronization.  rn_last_error() returns a message for the last non-OK
+ *    status on the calling thread.
+ *  - rows == 0 (or tokens == 0) is a valid no-op: RN_OK, nothing launched,
+ *    pointers may then be NULL.
+ */
+#ifndef RMSNORM_ROWS_H
+#define RMSNORM_ROWS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RN_ABI_VERSION 1
+
+typedef enum rn_status {
+  RN_OK = 0,
+  RN_ERR_INVALID_ARG = 1,
+  RN_ERR_UNSUPPORTED = 2,
+  RN_ERR_MISALIGNED = 3,
+  RN_ERR_HIP = 4
+} rn_status;
+
+/* Element types. */
+#define RN_DTYPE_BF16 0u       /* bfloat16 */
+#define RN_DTYPE_F32 1u        /* IEEE binary32 */
+#define RN_DTYPE_FP8_E4M3FN 2u /* OCP fp8 E4M3FN, outputs only, with a float32 scale per row */
+
+/* flags: bits 0-1 dtype of x, bits 2-3 dtype of residual and residual_out,
+ * bits 4-5 dtype of weight, bits 6-7 dtype of out, bit 8 weight form (1 + w).
+ * qknorm_fwd uses bits 0-1 for q/k (in and out), bits 4-5 for the weights and
+ * bit 8; its other bits must be zero. */
+#define RN_FLAGS_X_SHIFT 0
+#define RN_FLAGS_RES_SHIFT 2
+#define RN_FLAGS_W_SHIFT 4
+#define RN_FLAGS_OUT_SHIFT 6
+#define RN_FLAG_WEIGHT_PLUS_ONE (1u << 8)
+#define RN_FLAGS_KNOWN_MASK 0x1FFu
+#define RN_MAKE_FLAGS(x_dt, res_dt, w_dt, out_dt, plus_one)                                   \
+  (((uint32_t)(x_dt) << RN_FLAGS_X_SHIFT) | ((uint32_t)(res_dt) << RN_FLAGS_RES_SHIFT) |     \
+   ((uint32_t)(w_dt) << RN_FLAGS_W_SHIFT) | ((uint32_t)(out_dt) << RN_FLAGS_OUT_SHIFT) |     \
+   ((plus_one) ? RN_FLAG_WEIGHT_PLUS_ONE : 0u))
+
+/* Kernel families reported by the query functions. */
+#define RN_KERNEL_ROWS 0  /* one workgroup of waves_per_row wave64s per row */
+#define RN_KERNEL_HEADS 1 /* lanes_per_row lanes per (token, head) row, several rows per wave */
+
+/* Launch configuration chosen by the host-side selector (or given explicitly). */
+typedef struct rn_launch_config {
+  int32_t kernel;        /* RN_KERNEL_ROWS or RN_KERNEL_HEADS */
+  int32_t vec;           /* elements per lane vector: 16 bytes of x (8 bf16 or 4 f32) */
+  int32_t waves_per_row; /* RN_KERNEL_ROWS: wave64s sharing one row (1..16); 1 = no LDS, no barrier */
+  int32_t vecs_per_lane; /* RN_KERNEL_ROWS: vectors each lane holds (1, 2, 4 or 8) */
+  int32_t lanes_per_row; /* RN_KERNEL_HEADS: lanes per head (head_dim / vec); ROWS: 64 * waves_per_row */
+  int32_t rows_per_lane; /* RN_KERNEL_HEADS: heads each lane group normalizes (1, 2 or 4); ROWS: 1 */
+  int32_t block_threads; /* workgroup size */
+  int32_t reserved;      /* zero */
+  int64_t grid;          /* workgroups launched; ROWS: at most rows, each workgroup strides over rows */
+} rn_launch_config;
+
+/*
+ * Fused residual add + RMSNorm over rows.
+ *
+ *   x            [rows, hidden] of dtype flags.x                       (read)
+ *   residual     [rows, hidden] of dtype flags.res, or NULL for no residual add (read)
+ *   weight       [hidden] of dtype flags.w                             (read)
+ *   out          [rows, hidden] of dtype flags.out; for fp8, one byte per element (write)
+ *   residual_out [rows, hidden] of dtype flags.res; must be NULL iff residual is NULL (write)
+ *   out_scale    [rows] float32, fp8 output only (else must be NULL)   (write)
+ *   rows         >= 0;  hidden >= 1, a multiple of the lane vector (8 for bf16 x,
+ *                4 for f32 x) and at most 32768 (bf16 x) / 16384 (f32 x): the
+ *                whole row is held in registers, 4096 lane vectors at most
+ *   eps          finite, >= 0, used as given (a float32)
+ *   flags        RN_MAKE_FLAGS(...); x is bf16 or f32; the residual dtype is the
+ *                x dtype or f32; weight bf16 or f32; out bf16, f32 or fp8.
+ *
+ * Residual reading (not on the pages): h = x + residual is rounded once to the
+ * residual dtype, written to residual_out, and normalized; out == RMSNorm(h).
+ * fp8 reading: amax and every y_i are float32 values computed from the same
+ * products, scale = amax / 448 is an IEEE float32 division, an all-zero row has
+ * scale 0 and all-zero codes.
+ * Aliasing: out may equal x (in place) and residual_out may equal residual;
+ * any other overlap is undefined, and out == residual_out is rejected.
+ */
+rn_status rmsnorm_fwd(const void* x, const void* residual, const void* weight, void* out,
+                      void* residual_out, float* out_scale, int64_t rows, int64_t hidden, float eps,
+                      uint32_t flags, void* stream);
+
+/* As rmsnorm_fwd; for fp8 output, out_amax (may be NULL) also receives each
+ * row's float32 amax, from which out_scale was computed.  out_amax must be NULL
+ * for other outputs. */
+rn_status rmsnorm_fwd_ex(const void* x, const void* residual, const void* weight, void* out,
+                         void* residual_out, float* out_scale, float* out_amax, int64_t rows,
+                         int64_t hidden, float eps, uint32_t flags, void* stream);
+
+/* As rmsnorm_fwd_ex, with an explicit launch configuration instead of the
+ * selector's (for tuning and for testing every kernel variant).  cfg->kernel
+ * must be RN_KERNEL_ROWS; waves_per_row in 1..16, vecs_per_lane in {1,2,4,8},
+ * 64 * waves_per_row * vecs_per_lane * vec >= hidden, 1 <= grid <= rows;
+ * block_threads, lanes_per_row and rows_per_lane are derived and ignored. */
+rn_status rmsnorm_fwd_config(const void* x, const void* residual, const void* weight, void* out,
+                             void* residual_out, float* out_scale, float* out_amax, int64_t rows,
+                             int64_t hidden, float eps, uint32_t flags,
+                             const rn_launch_config* cfg, void* stream);
+
+/*
+ * Per-head RMSNorm of Q and K ("CuTeDSL at Perplexity", section "QK Norm").
+ *
+ *   q          [tokens, num_q_heads, head_dim], token stride q_token_stride elements
+ *   k          [tokens, num_k_heads, head_dim] or NULL when num_k_heads == 0
+ *   q_weight   [head_dim], k_weight [head_dim] (k_weight NULL iff k is NULL)
+ *   q_out      same layout (token stride) as q; may equal q (in place, the page's form)
+ *   k_out      same layout as k; may equal k; NULL iff k is NULL
+ *   tokens     >= 0; num_q_heads >= 1; num_k_heads >= 0;
+ *              tokens * (num_q_heads + num_k_heads) < 2^31
+ *   head_dim   64, 128 or 256
+ *   *_token_stride  elements between consecutive tokens; 0 means contiguous
+ *              (heads * head_dim); otherwise >= heads * head_dim and 16-byte aligned
+ *   flags      bits 0-1: dtype of q, k and outputs (bf16 or f32); bits 4-5:
+ *              weight dtype (bf16 or f32); bit 8: weight form (1 + w)
+ */
+rn_status qknorm_fwd(const void* q, const void* k, const void* q_weight, const void* k_weight,
+                     void* q_out, void* k_out, int64_t tokens, int32_t num_q_heads,
+                     int32_t num_k_heads, int32_t head_dim, int64_t q_token_stride,
+                     int64_t k_token_stride, float eps, uint32_t flags, void* stream);
+
+/* Host-only: the launch configuration rmsnorm_fwd would use for these sizes on
+ * a device with num_cus compute units (num_cus <= 0: query the current device). */
+rn_status rmsnorm_query_config(int64_t rows, int64_t hidden, uint32_t flags, int32_t num_cus,
+                               rn_launch_config* cfg);
+
+/* Host-only: the launch configuration qknorm_fwd would use. */
+rn_status qknorm_query_config(int64_t tokens, int32_t num_q_heads, int32_t num_k_heads,
+                              int32_t head_dim, uint32_t flags, int32_t num_cus,
+                              rn_launch_config* cfg);
+
+/* Enqueues one wave64 of a kernel that does nothing, through the same launch
+ * path as the entry points above: the reference for bare kernel-launch latency
+ * when decode-sized calls are timed. */
+rn_status rn_launch_empty(void* stream);
+
+/* Static description of a status code. */
+const char* rn_status_string(rn_status status);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* rn_last_error(void);
+
+/* RN_ABI_VERSION of the built library. */
+int32_t rn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RMSNORM_ROWS_H */

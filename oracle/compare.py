@@ -1,0 +1,71 @@
+"""Acceptance rules for comparing an implementation's outputs with the oracle.
+
+TEST INFRASTRUCTURE ONLY (like the rest of ``oracle``).
+
+Tolerances (the stated target of the work):
+  * bf16 outputs: within one bf16 ulp of the exact value, ulp(v) =
+    2**(floor(log2|v|) - 7) (so either neighbour of a value near a rounding
+    midpoint is accepted);
+  * f32 outputs: relative error at most 1e-5;
+  * fp8 e4m3fn codes: at most one step apart, counting steps on the signed
+    magnitude index (code & 0x7F, negated for negative codes), so +0 and -0
+    are the same point and crossing zero costs the steps on either side;
+  * bit-exact where one correctly rounded operation fixes the result (the
+    updated residual).
+"""
+
+from __future__ import annotations
+
+from typing import Dict
+
+import numpy as np
+
+from .rownorm import BF16, bf16_decode
+
+__all__ = ["bf16_ulp", "check_bf16", "check_f32", "check_fp8_codes", "signed_index"]
+
+
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """ulp of |v| in bfloat16 (the spacing of the binade |v| lies in)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    _, E = np.frexp(np.where(a > 0, a, 1.0))
+    e = np.maximum(E - 1, BF16.emin)
+    e = np.where(a > 0, e, BF16.emin)
+    return np.ldexp(1.0, e - (BF16.precision - 1))
+
+
+def check_bf16(gpu_bits: np.ndarray, exact: np.ndarray) -> Dict[str, float]:
+    """bf16 bits vs exact doubles: pass iff every |gpu - exact| <= ulp(exact)."""
+    g = bf16_decode(gpu_bits)
+    y = np.asarray(exact, dtype=np.float64)
+    err = np.abs(g - y)
+    ulp = bf16_ulp(y)
+    finite = np.isfinite(y)
+    ok = np.where(finite, err <= ulp, np.isnan(g) == np.isnan(y))
+    ratio = np.where(finite, err / ulp, 0.0)
+    return {"ok": bool(ok.all()), "max_ulp": float(ratio.max(initial=0.0)),
+            "n_bad": int((~ok).sum()), "n": int(ok.size)}
+
+
+def check_f32(gpu: np.ndarray, exact: np.ndarray, rtol: float = 1e-5) -> Dict[str, float]:
+    g = np.asarray(gpu, dtype=np.float64)
+    y = np.asarray(exact, dtype=np.float64)
+    err = np.abs(g - y)
+    tol = rtol * np.abs(y)
+    ok = (err <= tol) | (g == y)
+    rel = np.where(y != 0, err / np.where(y != 0, np.abs(y), 1.0), np.where(err == 0, 0.0, np.inf))
+    return {"ok": bool(ok.all()), "max_rel": float(rel.max(initial=0.0)),
+            "n_bad": int((~ok).sum()), "n": int(ok.size)}
+
+
+def signed_index(codes: np.ndarray) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    mag = c & 0x7F
+    return np.where(c & 0x80, -mag, mag)
+
+
+def check_fp8_codes(gpu: np.ndarray, ref: np.ndarray, max_steps: int = 1) -> Dict[str, float]:
+    d = np.abs(signed_index(gpu) - signed_index(ref))
+    return {"ok": bool((d <= max_steps).all()), "max_steps": int(d.max(initial=0)),
+            "frac_exact": float((d == 0).mean()) if d.size else 1.0, "n_bad": int((d > max_steps).sum()),
+            "n": int(d.size)}

@@ -1,0 +1,208 @@
+"""MI355X-native (gfx950) row normalization: fused residual add + RMSNorm,
+per-head QK-norm, and fp8 e4m3fn output with a per-row scale.
+
+Thin torch-facing binding over the C ABI in include/rmsnorm_rows.h: it checks
+tensors, allocates outputs with torch, and passes raw device pointers and the
+current HIP stream to the library.  Every step of the computation runs in the
+library's HIP kernels; nothing here computes, and nothing falls back to the CPU.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import NamedTuple, Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import LaunchConfig, RNError, check, lib, make_flags
+
+__all__ = [
+    "NormOutput",
+    "fused_add_rmsnorm",
+    "rmsnorm",
+    "qk_norm",
+    "query_config",
+    "query_qknorm_config",
+    "RNError",
+    "LaunchConfig",
+    "lib",
+]
+
+_NAMES = {torch.bfloat16: "bf16", torch.float32: "f32", torch.float8_e4m3fn: "fp8_e4m3fn"}
+_TORCH = {v: k for k, v in _NAMES.items()}
+
+
+class NormOutput(NamedTuple):
+    out: torch.Tensor
+    residual_out: Optional[torch.Tensor]
+    scale: Optional[torch.Tensor]  # fp8 output: float32 [rows]
+    amax: Optional[torch.Tensor]   # fp8 output when requested: float32 [rows]
+
+
+def _name(dtype: torch.dtype, what: str) -> str:
+    if dtype not in _NAMES:
+        raise TypeError(f"{what}: unsupported dtype {dtype}")
+    return _NAMES[dtype]
+
+
+def _dev_tensor(t: torch.Tensor, what: str, device: torch.device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{what} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def fused_add_rmsnorm(x: torch.Tensor, residual: Optional[torch.Tensor], weight: torch.Tensor,
+                      eps: float, *, weight_plus_one: bool = False,
+                      out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                      residual_out: Optional[torch.Tensor] = None, return_amax: bool = False,
+                      config: Optional[LaunchConfig] = None) -> NormOutput:
+    """``residual_out = x + residual``; ``out = RMSNorm(residual_out) * (w [+ 1])``.
+
+    ``x`` is [..., H] (bf16 or f32), ``residual`` the same shape (x dtype or
+    f32) or None, ``weight`` [H].  ``out_dtype`` is bf16, f32 or
+    ``torch.float8_e4m3fn`` (then ``scale`` holds one float32 per row and
+    ``out * scale`` dequantizes).  ``out=x`` and ``residual_out=residual``
+    are allowed (in place).  ``config`` forces a launch configuration.
+    """
+    device = x.device
+    if device.type != "cuda":
+        raise ValueError("x must be a device tensor")
+    _dev_tensor(x, "x", device)
+    H = x.shape[-1]
+    rows = x.numel() // H if H else 0
+    xd = _name(x.dtype, "x")
+    rd = None
+    if residual is not None:
+        _dev_tensor(residual, "residual", device)
+        if residual.shape != x.shape:
+            raise ValueError(f"residual shape {tuple(residual.shape)} != x shape {tuple(x.shape)}")
+        rd = _name(residual.dtype, "residual")
+    _dev_tensor(weight, "weight", device)
+    if weight.shape != (H,):
+        raise ValueError(f"weight shape {tuple(weight.shape)} != ({H},)")
+    wd = _name(weight.dtype, "weight")
+    od_t = out_dtype if out_dtype is not None else (out.dtype if out is not None else x.dtype)
+    od = _name(od_t, "out")
+    if out is None:
+        out = torch.empty(x.shape, dtype=od_t, device=device)
+    else:
+        _dev_tensor(out, "out", device)
+        if out.shape != x.shape or out.dtype != od_t:
+            raise ValueError("out has the wrong shape or dtype")
+    if residual is not None:
+        if residual_out is None:
+            residual_out = torch.empty_like(residual)
+        else:
+            _dev_tensor(residual_out, "residual_out", device)
+            if residual_out.shape != residual.shape or residual_out.dtype != residual.dtype:
+                raise ValueError("residual_out must match residual's shape and dtype")
+    elif residual_out is not None:
+        raise ValueError("residual_out given without residual")
+    scale = amax = None
+    if od == "fp8_e4m3fn":
+        scale = torch.empty(rows, dtype=torch.float32, device=device)
+        if return_amax:
+            amax = torch.empty(rows, dtype=torch.float32, device=device)
+    flags = make_flags(xd, rd, wd, od, weight_plus_one)
+    L = lib()
+    if config is not None:
+        st = L.rmsnorm_fwd_config(_p(x), _p(residual), _p(weight), _p(out), _p(residual_out), _p(scale),
+                                  _p(amax), rows, H, eps, flags, ctypes.byref(config), _stream(device))
+    else:
+        st = L.rmsnorm_fwd_ex(_p(x), _p(residual), _p(weight), _p(out), _p(residual_out), _p(scale),
+                              _p(amax), rows, H, eps, flags, _stream(device))
+    check(st)
+    return NormOutput(out, residual_out, scale, amax)
+
+
+def rmsnorm(x: torch.Tensor, weight: torch.Tensor, eps: float, **kw) -> NormOutput:
+    """RMSNorm over the last dimension, no residual (see ``fused_add_rmsnorm``)."""
+    return fused_add_rmsnorm(x, None, weight, eps, **kw)
+
+
+def _head_view(t: torch.Tensor, what: str, device: torch.device) -> Tuple[int, int, int, int]:
+    if t.device != device:
+        raise ValueError(f"{what} is on {t.device}, expected {device}")
+    if t.dim() != 3:
+        raise ValueError(f"{what} must be [tokens, heads, head_dim]")
+    T, nh, D = t.shape
+    if t.stride(2) != 1 or (nh > 1 and t.stride(1) != D):
+        raise ValueError(f"{what}: heads must be contiguous inside a token")
+    stride = t.stride(0) if T > 1 else nh * D
+    return T, nh, D, stride
+
+
+def _qk_flags(dtype: str, w_dtype: str, weight_plus_one: bool) -> int:
+    f = (_lib.DTYPE_CODES[dtype] << _lib.RN_FLAGS_X_SHIFT) | (_lib.DTYPE_CODES[w_dtype] << _lib.RN_FLAGS_W_SHIFT)
+    return f | (_lib.RN_FLAG_WEIGHT_PLUS_ONE if weight_plus_one else 0)
+
+
+def qk_norm(q: torch.Tensor, k: Optional[torch.Tensor], q_weight: torch.Tensor,
+            k_weight: Optional[torch.Tensor], eps: float, *, weight_plus_one: bool = False,
+            inplace: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Per-head RMSNorm of ``q`` [T, nq, D] and ``k`` [T, nk, D] over D (64, 128 or 256).
+
+    Views with a token stride (e.g. slices of a fused QKV buffer) are accepted.
+    ``inplace=True`` (the page's form) overwrites q and k; otherwise new
+    tensors with the same layout are returned.
+    """
+    device = q.device
+    if device.type != "cuda":
+        raise ValueError("q must be a device tensor")
+    T, nq, D, qs = _head_view(q, "q", device)
+    td = _name(q.dtype, "q")
+    nk, ks = 0, 0
+    if k is not None:
+        Tk, nk, Dk, ks = _head_view(k, "k", device)
+        if Tk != T or Dk != D or k.dtype != q.dtype:
+            raise ValueError("k must have q's tokens, head_dim and dtype")
+        if k_weight is None:
+            raise ValueError("k_weight is required with k")
+    _dev_tensor(q_weight, "q_weight", device)
+    if q_weight.shape != (D,):
+        raise ValueError("q_weight must be [head_dim]")
+    wd = _name(q_weight.dtype, "q_weight")
+    if k is not None:
+        _dev_tensor(k_weight, "k_weight", device)
+        if k_weight.shape != (D,) or k_weight.dtype != q_weight.dtype:
+            raise ValueError("k_weight must be [head_dim] with q_weight's dtype")
+    if inplace:
+        q_out, k_out = q, k
+    else:
+        q_out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=device)
+        k_out = None if k is None else torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=device)
+    flags = _qk_flags(td, wd, weight_plus_one)
+    st = lib().qknorm_fwd(_p(q), _p(k), _p(q_weight), _p(k_weight if k is not None else None),
+                          _p(q_out), _p(k_out), T, nq, nk, D, qs, ks, eps, flags, _stream(device))
+    check(st)
+    return q_out, k_out
+
+
+def query_config(rows: int, hidden: int, *, x_dtype: str = "bf16", w_dtype: str = "bf16",
+                 out_dtype: str = "bf16", weight_plus_one: bool = False, num_cus: int = 256) -> dict:
+    """The launch configuration the selector picks (host only; no GPU needed)."""
+    cfg = LaunchConfig()
+    flags = make_flags(x_dtype, None, w_dtype, out_dtype, weight_plus_one)
+    check(lib().rmsnorm_query_config(rows, hidden, flags, num_cus, ctypes.byref(cfg)))
+    return cfg.as_dict()
+
+
+def query_qknorm_config(tokens: int, num_q_heads: int, num_k_heads: int, head_dim: int, *,
+                        dtype: str = "bf16", w_dtype: str = "bf16", num_cus: int = 256) -> dict:
+    cfg = LaunchConfig()
+    flags = _qk_flags(dtype, w_dtype, False)
+    check(lib().qknorm_query_config(tokens, num_q_heads, num_k_heads, head_dim, flags, num_cus,
+                                    ctypes.byref(cfg)))
+    return cfg.as_dict()

@@ -1,0 +1,254 @@
+// C ABI entry points: argument checks, selector, kernel lookup, launch.
+//
+// Order inside every entry point: flags and sizes, then pointers and
+// alignment -- all on the host, before any HIP call -- and only then the
+// per-device compute-unit count (cached) and the asynchronous launch.
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "rn_internal.h"
+
+namespace rn {
+const char* last_error();
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_num_cus[kMaxDevices];  // 0 = not queried yet
+
+rn_status device_cus(int* num_cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(RN_ERR_HIP, "device index %d out of range", dev);
+  int n = g_num_cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || n < 1)
+      return fail(RN_ERR_HIP, "hipDeviceGetAttribute(compute units): %s", hipGetErrorString(e));
+    g_num_cus[dev].store(n, std::memory_order_relaxed);
+  }
+  *num_cus = n;
+  return RN_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+const void* pick_row_kernel(const RowKey& k) {
+  const void* (*const pickers[])(const RowKey&) = {
+      pick_row_kernel_bf16_bf16, pick_row_kernel_bf16_f32, pick_row_kernel_bf16_fp8,
+      pick_row_kernel_f32_bf16,  pick_row_kernel_f32_f32,  pick_row_kernel_f32_fp8};
+  for (auto p : pickers) {
+    const void* f = p(k);
+    if (f) return f;
+  }
+  return nullptr;
+}
+
+rn_status launch(const void* fn, int64_t grid, int block, void* args, void* stream) {
+  void* argv[] = {args};
+  hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(grid)), dim3(block),
+                                 args ? argv : nullptr, 0, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RN_ERR_HIP, "hipLaunchKernel: %s", hipGetErrorString(e));
+  return RN_OK;
+}
+
+rn_status rows_entry(const void* x, const void* residual, const void* weight, void* out,
+                     void* residual_out, float* out_scale, float* out_amax, int64_t rows,
+                     int64_t hidden, float eps, uint32_t flags, const rn_launch_config* explicit_cfg,
+                     void* stream) {
+  clear_error();
+  RowKey key;
+  rn_status st = check_row_shape(rows, hidden, flags, residual != nullptr, &key);
+  if (st != RN_OK) return st;
+  if (!(eps >= 0.0f) || eps == __builtin_inff()) return fail(RN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const bool fp8 = key.out == kFP8;
+  if (!fp8 && (out_scale != nullptr || out_amax != nullptr))
+    return fail(RN_ERR_INVALID_ARG, "out_scale / out_amax are only for fp8 output");
+  if (rows == 0) return RN_OK;
+  if (x == nullptr || weight == nullptr || out == nullptr)
+    return fail(RN_ERR_INVALID_ARG, "x, weight and out must not be NULL");
+  if ((residual == nullptr) != (residual_out == nullptr))
+    return fail(RN_ERR_INVALID_ARG, "residual and residual_out must both be given or both be NULL");
+  if (fp8 && out_scale == nullptr) return fail(RN_ERR_INVALID_ARG, "fp8 output needs out_scale");
+  if (residual_out != nullptr && residual_out == out)
+    return fail(RN_ERR_INVALID_ARG, "out and residual_out must be different buffers");
+  const void* ptrs16[] = {x, residual, weight, out, residual_out};
+  for (const void* p : ptrs16)
+    if (p != nullptr && !aligned(p, 16)) return fail(RN_ERR_MISALIGNED, "tensor pointer %p is not 16-byte aligned", p);
+  if ((out_scale && !aligned(out_scale, 4)) || (out_amax && !aligned(out_amax, 4)))
+    return fail(RN_ERR_MISALIGNED, "out_scale / out_amax must be 4-byte aligned");
+
+  rn_launch_config cfg;
+  if (explicit_cfg != nullptr) {
+    st = check_row_config(rows, hidden, key, explicit_cfg, &cfg);
+  } else {
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != RN_OK) return st;
+    st = select_row_config(rows, hidden, key, cus, &cfg);
+  }
+  if (st != RN_OK) return st;
+  key.nv = cfg.vecs_per_lane;
+  const void* fn = pick_row_kernel(key);
+  if (fn == nullptr) return fail(RN_ERR_UNSUPPORTED, "no kernel built for this dtype combination");
+
+  RowArgs a;
+  a.x = x;
+  a.res = residual;
+  a.w = weight;
+  a.out = out;
+  a.res_out = residual_out;
+  a.scale = out_scale;
+  a.amax = out_amax;
+  a.rows = rows;
+  a.hidden = static_cast<int32_t>(hidden);
+  a.nvec = static_cast<int32_t>(hidden / cfg.vec);
+  a.eps = eps;
+  return launch(fn, cfg.grid, cfg.block_threads, &a, stream);
+}
+
+}  // namespace
+}  // namespace rn
+
+using namespace rn;
+
+extern "C" {
+
+rn_status rmsnorm_fwd(const void* x, const void* residual, const void* weight, void* out,
+                      void* residual_out, float* out_scale, int64_t rows, int64_t hidden, float eps,
+                      uint32_t flags, void* stream) {
+  return rows_entry(x, residual, weight, out, residual_out, out_scale, nullptr, rows, hidden, eps,
+                    flags, nullptr, stream);
+}
+
+rn_status rmsnorm_fwd_ex(const void* x, const void* residual, const void* weight, void* out,
+                         void* residual_out, float* out_scale, float* out_amax, int64_t rows,
+                         int64_t hidden, float eps, uint32_t flags, void* stream) {
+  return rows_entry(x, residual, weight, out, residual_out, out_scale, out_amax, rows, hidden, eps,
+                    flags, nullptr, stream);
+}
+
+rn_status rmsnorm_fwd_config(const void* x, const void* residual, const void* weight, void* out,
+                             void* residual_out, float* out_scale, float* out_amax, int64_t rows,
+                             int64_t hidden, float eps, uint32_t flags,
+                             const rn_launch_config* cfg, void* stream) {
+  if (cfg == nullptr) {
+    clear_error();
+    return fail(RN_ERR_INVALID_ARG, "launch config is NULL");
+  }
+  return rows_entry(x, residual, weight, out, residual_out, out_scale, out_amax, rows, hidden, eps,
+                    flags, cfg, stream);
+}
+
+rn_status qknorm_fwd(const void* q, const void* k, const void* q_weight, const void* k_weight,
+                     void* q_out, void* k_out, int64_t tokens, int32_t num_q_heads,
+                     int32_t num_k_heads, int32_t head_dim, int64_t q_token_stride,
+                     int64_t k_token_stride, float eps, uint32_t flags, void* stream) {
+  clear_error();
+  HeadKey key;
+  rn_status st = check_head_shape(tokens, num_q_heads, num_k_heads, head_dim, flags, &key);
+  if (st != RN_OK) return st;
+  if (!(eps >= 0.0f) || eps == __builtin_inff()) return fail(RN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const int64_t qrow = (int64_t)num_q_heads * head_dim;
+  const int64_t krow = (int64_t)num_k_heads * head_dim;
+  if (q_token_stride == 0) q_token_stride = qrow;
+  if (k_token_stride == 0) k_token_stride = krow;
+  if (q_token_stride < qrow || q_token_stride < 0)
+    return fail(RN_ERR_INVALID_ARG, "q_token_stride (%lld) < num_q_heads * head_dim", (long long)q_token_stride);
+  if (num_k_heads > 0 && k_token_stride < krow)
+    return fail(RN_ERR_INVALID_ARG, "k_token_stride (%lld) < num_k_heads * head_dim", (long long)k_token_stride);
+  if (tokens == 0) return RN_OK;
+  if (q == nullptr || q_weight == nullptr || q_out == nullptr)
+    return fail(RN_ERR_INVALID_ARG, "q, q_weight and q_out must not be NULL");
+  const bool has_k = num_k_heads > 0;
+  if (has_k != (k != nullptr) || has_k != (k_weight != nullptr) || has_k != (k_out != nullptr))
+    return fail(RN_ERR_INVALID_ARG, "k, k_weight and k_out must be given iff num_k_heads > 0");
+  const void* ptrs16[] = {q, k, q_weight, k_weight, q_out, k_out};
+  for (const void* p : ptrs16)
+    if (p != nullptr && !aligned(p, 16)) return fail(RN_ERR_MISALIGNED, "tensor pointer %p is not 16-byte aligned", p);
+  const int eb = key.t == kBF16 ? 2 : 4;
+  if ((q_token_stride * eb) % 16 != 0 || (has_k && (k_token_stride * eb) % 16 != 0))
+    return fail(RN_ERR_MISALIGNED, "token strides must be multiples of 16 bytes");
+
+  int cus = 0;
+  st = device_cus(&cus);
+  if (st != RN_OK) return st;
+  rn_launch_config cfg;
+  st = select_head_config(tokens, num_q_heads, num_k_heads, key, cus, &cfg);
+  if (st != RN_OK) return st;
+  key.rpl = cfg.rows_per_lane;
+  const void* fn = pick_head_kernel(key);
+  if (fn == nullptr) return fail(RN_ERR_UNSUPPORTED, "no qknorm kernel built for this combination");
+
+  HeadArgs a;
+  a.q = q;
+  a.k = k;
+  a.qw = q_weight;
+  a.kw = k_weight;
+  a.q_out = q_out;
+  a.k_out = k_out;
+  a.q_stride = q_token_stride;
+  a.k_stride = k_token_stride;
+  a.num_q_heads = num_q_heads;
+  a.num_heads = num_q_heads + num_k_heads;
+  a.total_rows = static_cast<int32_t>(tokens * (num_q_heads + num_k_heads));
+  a.eps = eps;
+  return launch(fn, cfg.grid, cfg.block_threads, &a, stream);
+}
+
+rn_status rmsnorm_query_config(int64_t rows, int64_t hidden, uint32_t flags, int32_t num_cus,
+                               rn_launch_config* cfg) {
+  clear_error();
+  if (cfg == nullptr) return fail(RN_ERR_INVALID_ARG, "cfg is NULL");
+  RowKey key;
+  // the configuration does not depend on the residual, so its dtype bits are ignored here
+  rn_status st = check_row_shape(rows, hidden, flags, false, &key);
+  if (st != RN_OK) return st;
+  int cus = num_cus;
+  if (cus <= 0) {
+    st = device_cus(&cus);
+    if (st != RN_OK) return st;
+  }
+  return select_row_config(rows > 0 ? rows : 1, hidden, key, cus, cfg);
+}
+
+rn_status qknorm_query_config(int64_t tokens, int32_t num_q_heads, int32_t num_k_heads,
+                              int32_t head_dim, uint32_t flags, int32_t num_cus,
+                              rn_launch_config* cfg) {
+  clear_error();
+  if (cfg == nullptr) return fail(RN_ERR_INVALID_ARG, "cfg is NULL");
+  HeadKey key;
+  rn_status st = check_head_shape(tokens, num_q_heads, num_k_heads, head_dim, flags, &key);
+  if (st != RN_OK) return st;
+  int cus = num_cus;
+  if (cus <= 0) {
+    st = device_cus(&cus);
+    if (st != RN_OK) return st;
+  }
+  return select_head_config(tokens > 0 ? tokens : 1, num_q_heads, num_k_heads, key, cus, cfg);
+}
+
+rn_status rn_launch_empty(void* stream) {
+  clear_error();
+  return launch(empty_kernel_address(), 1, 64, nullptr, stream);
+}
+
+const char* rn_status_string(rn_status status) {
+  switch (status) {
+    case RN_OK: return "RN_OK: success";
+    case RN_ERR_INVALID_ARG: return "RN_ERR_INVALID_ARG: invalid argument";
+    case RN_ERR_UNSUPPORTED: return "RN_ERR_UNSUPPORTED: combination or size not built";
+    case RN_ERR_MISALIGNED: return "RN_ERR_MISALIGNED: pointer or stride not 16-byte aligned";
+    case RN_ERR_HIP: return "RN_ERR_HIP: HIP runtime error";
+    default: return "unknown rn_status";
+  }
+}
+
+const char* rn_last_error(void) { return last_error(); }
+
+int32_t rn_abi_version(void) { return RN_ABI_VERSION; }
+
+}  // extern "C"

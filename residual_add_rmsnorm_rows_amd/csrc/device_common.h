@@ -1,0 +1,200 @@
+// Device-side building blocks for the gfx950 (CDNA4, wave64) kernels:
+// element codecs, 16-byte lane-vector loads/stores, DPP reductions across
+// lanes, and the fp8 E4M3FN encoder.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rn_internal.h"
+
+namespace rn {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <int DT>
+struct DTypeInfo;
+template <>
+struct DTypeInfo<kBF16> { static constexpr int bytes = 2; };
+template <>
+struct DTypeInfo<kF32> { static constexpr int bytes = 4; };
+template <>
+struct DTypeInfo<kFP8> { static constexpr int bytes = 1; };
+
+// ---------------------------------------------------------------------------
+// Raw words: a lane vector of N elements of one dtype is N * bytes / 4 dwords.
+// ---------------------------------------------------------------------------
+
+template <int BYTES>
+__device__ __forceinline__ void load_words(const void* p, uint32_t (&w)[BYTES / 4]) {
+  static_assert(BYTES == 4 || BYTES == 8 || BYTES == 16 || BYTES == 32, "lane vector size");
+  if constexpr (BYTES == 32) {
+    const u32x4 a = reinterpret_cast<const u32x4*>(p)[0];
+    const u32x4 b = reinterpret_cast<const u32x4*>(p)[1];
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  } else if constexpr (BYTES == 16) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+  } else if constexpr (BYTES == 8) {
+    const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+    w[0] = a.x; w[1] = a.y;
+  } else {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+}
+
+// Stores of write-once outputs use the nontemporal hint: they are not re-read
+// by this kernel and would only evict useful lines from L2.
+template <int BYTES>
+__device__ __forceinline__ void store_words(void* p, const uint32_t (&w)[BYTES / 4]) {
+  static_assert(BYTES == 4 || BYTES == 8 || BYTES == 16 || BYTES == 32, "lane vector size");
+  if constexpr (BYTES == 32) {
+    u32x4 a = {w[0], w[1], w[2], w[3]};
+    u32x4 b = {w[4], w[5], w[6], w[7]};
+    __builtin_nontemporal_store(a, reinterpret_cast<u32x4*>(p));
+    __builtin_nontemporal_store(b, reinterpret_cast<u32x4*>(p) + 1);
+  } else if constexpr (BYTES == 16) {
+    u32x4 a = {w[0], w[1], w[2], w[3]};
+    __builtin_nontemporal_store(a, reinterpret_cast<u32x4*>(p));
+  } else if constexpr (BYTES == 8) {
+    u32x2 a = {w[0], w[1]};
+    __builtin_nontemporal_store(a, reinterpret_cast<u32x2*>(p));
+  } else {
+    __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t*>(p));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Element codecs (float32 in registers).
+// ---------------------------------------------------------------------------
+
+// bfloat16 is the upper half of a binary32: widening is a shift.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two floats -> two bfloat16 (round to nearest even) in one dword, element 0
+// in the low half: v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// float32 -> OCP fp8 E4M3FN code: round to nearest even, saturate to +-448.
+// E4M3FN: bias 7, 3 fraction bits, subnormal quantum 2^-9, largest finite
+// 1.75 * 2^8 = 448 (code 0x7E); 0x7F is NaN, so rounding past 448 clamps.
+__device__ __forceinline__ uint32_t e4m3fn_code(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = __builtin_fabsf(v);
+  uint32_t mag;
+  if (a < 0.015625f) {
+    // below 2^-6: a multiple of 2^-9 (v_rndne_f32 rounds to nearest even);
+    // a result of 8 is code 0x08, the smallest normal, as it should be.
+    mag = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
+  } else {
+    // keep 3 fraction bits with round to nearest even, then rebias the
+    // exponent from 127 to 7: ((e + 127) << 3 | m) - (120 << 3).
+    uint32_t u = __float_as_uint(a);
+    u += 0x7FFFFu + ((u >> 20) & 1u);
+    mag = (u >> 20) - (120u << 3);
+    mag = mag > 0x7Eu ? 0x7Eu : mag;
+  }
+  return sign | mag;
+}
+
+// Unpack a lane vector of VEC elements of dtype DT to floats.
+template <int DT, int VEC>
+__device__ __forceinline__ void unpack(const uint32_t (&w)[VEC * DTypeInfo<DT>::bytes / 4],
+                                       float (&f)[VEC]) {
+  if constexpr (DT == kBF16) {
+#pragma unroll
+    for (int i = 0; i < VEC / 2; ++i) {
+      f[2 * i] = bf16_lo(w[i]);
+      f[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+    static_assert(DT == kF32, "inputs are bf16 or f32");
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) f[i] = __uint_as_float(w[i]);
+  }
+}
+
+// Pack floats to a lane vector of dtype DT (bf16/f32 round to nearest even;
+// fp8 codes are produced by the caller with e4m3fn_code and packed here).
+template <int DT, int VEC>
+__device__ __forceinline__ void pack(const float (&f)[VEC],
+                                     uint32_t (&w)[(VEC * DTypeInfo<DT>::bytes + 3) / 4]) {
+  if constexpr (DT == kBF16) {
+#pragma unroll
+    for (int i = 0; i < VEC / 2; ++i) w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+  } else if constexpr (DT == kF32) {
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) w[i] = __float_as_uint(f[i]);
+  } else {
+    static_assert(DT == kFP8, "outputs are bf16, f32 or fp8");
+    static_assert(VEC % 4 == 0, "fp8 lane vectors are whole dwords");
+#pragma unroll
+    for (int i = 0; i < VEC / 4; ++i) {
+      w[i] = e4m3fn_code(f[4 * i]) | (e4m3fn_code(f[4 * i + 1]) << 8) |
+             (e4m3fn_code(f[4 * i + 2]) << 16) | (e4m3fn_code(f[4 * i + 3]) << 24);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane reductions (wave64).  DPP moves stay inside a 16-lane row:
+//   quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2),
+//   row_half_mirror (lane i of 8 <- 7 - i), row_mirror (lane i of 16 <- 15 - i).
+// After these four steps every lane of a row holds the row's total, bitwise
+// identical in all 16 lanes (each step adds the same two values in either
+// order).  Wider groups continue with ds_swizzle (lane ^ 16 inside 32) or
+// readlane of the four row totals (uniform result).
+// ---------------------------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, false));
+}
+
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kSwizzleXor16 = 0x401F;  // bitmask mode: and 0x1F, or 0, xor 0x10
+
+struct OpSum {
+  __device__ __forceinline__ static float apply(float a, float b) { return a + b; }
+};
+struct OpMax {
+  __device__ __forceinline__ static float apply(float a, float b) { return __builtin_fmaxf(a, b); }
+};
+
+// Reduce over aligned groups of G lanes (G = 8, 16, 32 or 64); every lane of
+// a group receives the group's result.
+template <int G, class Op>
+__device__ __forceinline__ float group_reduce(float v) {
+  static_assert(G == 8 || G == 16 || G == 32 || G == 64, "group size");
+  v = Op::apply(v, dpp_mov<kDppQuadXor1>(v));
+  v = Op::apply(v, dpp_mov<kDppQuadXor2>(v));
+  v = Op::apply(v, dpp_mov<kDppRowHalfMirror>(v));
+  if constexpr (G >= 16) v = Op::apply(v, dpp_mov<kDppRowMirror>(v));
+  if constexpr (G == 32) {
+    v = Op::apply(v, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
+                                                                           kSwizzleXor16)));
+  }
+  if constexpr (G == 64) {
+    const int b = __builtin_bit_cast(int, v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+    v = Op::apply(Op::apply(r0, r1), Op::apply(r2, r3));
+  }
+  return v;
+}
+
+}  // namespace rn

@@ -1,0 +1,119 @@
+// Internal declarations shared by the host-side selector, the C ABI and the
+// kernel translation units.  Plain C++ (no HIP headers) so that the selector
+// builds and runs on any host.
+#pragma once
+
+#include <stdint.h>
+
+#include "rmsnorm_rows.h"
+
+namespace rn {
+
+enum DType : int { kBF16 = 0, kF32 = 1, kFP8 = 2, kNone = 3 };
+
+inline int dtype_bytes(int dt) { return dt == kBF16 ? 2 : dt == kF32 ? 4 : dt == kFP8 ? 1 : 0; }
+
+// Kernel arguments of the rows kernel, passed by value as the only argument.
+struct RowArgs {
+  const void* x;
+  const void* res;       // nullptr: no residual add
+  const void* w;
+  void* out;
+  void* res_out;         // nullptr iff res is nullptr
+  float* scale;          // fp8 output only
+  float* amax;           // fp8 output only, may be nullptr
+  int64_t rows;
+  int32_t hidden;        // elements per row
+  int32_t nvec;          // lane vectors per row: hidden / vec
+  float eps;
+};
+
+// Kernel arguments of the per-head kernel.
+struct HeadArgs {
+  const void* q;
+  const void* k;
+  const void* qw;
+  const void* kw;
+  void* q_out;
+  void* k_out;
+  int64_t q_stride;      // elements between tokens
+  int64_t k_stride;
+  int32_t num_q_heads;
+  int32_t num_heads;     // num_q_heads + num_k_heads
+  int32_t total_rows;    // tokens * num_heads
+  float eps;
+};
+
+// Everything the launcher needs to pick a compiled kernel.
+struct RowKey {
+  int x, res, w, out;  // res == kNone: no residual
+  int bias;            // 0 or 1
+  int nv;              // vectors per lane: 1, 2, 4, 8
+};
+
+struct HeadKey {
+  int t, w;            // q/k dtype, weight dtype
+  int bias;
+  int head_dim;        // 64, 128, 256
+  int rpl;             // heads per lane group: 1, 2, 4
+};
+
+// Decoded and validated arguments of an rmsnorm call (host side).
+struct RowCall {
+  RowKey key;
+  rn_launch_config cfg;
+};
+
+struct HeadCall {
+  HeadKey key;
+  rn_launch_config cfg;
+};
+
+// --- selector / validation (select.cpp, host only) -------------------------
+
+// Thread-local message for rn_last_error(); returns `st` for convenience.
+rn_status fail(rn_status st, const char* fmt, ...);
+void clear_error();
+
+// Checks flags/sizes (not pointers) of an rmsnorm call and fills key.{x,res,w,out,bias}.
+rn_status check_row_shape(int64_t rows, int64_t hidden, uint32_t flags, bool has_residual,
+                          RowKey* key);
+// Selector: launch configuration for rows x hidden on num_cus compute units.
+rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int num_cus,
+                            rn_launch_config* cfg);
+// Checks an explicit configuration and fills the derived fields.
+rn_status check_row_config(int64_t rows, int64_t hidden, const RowKey& key,
+                           const rn_launch_config* in, rn_launch_config* out);
+
+rn_status check_head_shape(int64_t tokens, int32_t nq, int32_t nk, int32_t head_dim,
+                           uint32_t flags, HeadKey* key);
+rn_status select_head_config(int64_t tokens, int32_t nq, int32_t nk, const HeadKey& key,
+                             int num_cus, rn_launch_config* cfg);
+
+constexpr int kMaxWavesPerRow = 16;
+constexpr int kMaxVecsPerLane = 8;
+constexpr int kHeadBlockThreads = 256;
+
+// Largest workgroup a rows-kernel variant is compiled for: holding 8 vectors
+// per lane needs more than the 128 VGPRs a 1024-thread workgroup leaves each
+// lane, so that variant is built for at most 8 waves (256 VGPRs per lane).
+constexpr int max_threads_for_nv(int nv) { return nv >= 8 ? 512 : 1024; }
+
+}  // namespace rn
+
+// --- kernel pickers (defined in the kernel translation units) ----------------
+// Each returns the address of the compiled kernel for `key`, or nullptr when
+// that combination is not built.
+namespace rn {
+// rows_kernel.hip, compiled once per (x dtype, out dtype) pair
+const void* pick_row_kernel_bf16_bf16(const RowKey& key);
+const void* pick_row_kernel_bf16_f32(const RowKey& key);
+const void* pick_row_kernel_bf16_fp8(const RowKey& key);
+const void* pick_row_kernel_f32_bf16(const RowKey& key);
+const void* pick_row_kernel_f32_f32(const RowKey& key);
+const void* pick_row_kernel_f32_fp8(const RowKey& key);
+// heads_kernel.hip
+const void* pick_head_kernel(const HeadKey& key);
+// empty_kernel.hip
+const void* empty_kernel_address();
+}  // namespace rn

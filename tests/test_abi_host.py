@@ -1,0 +1,194 @@
+"""Host-side tests of the C-ABI library: it loads, exports what the header
+declares, rejects bad arguments before touching HIP, and the selector's
+launch configurations cover every row.  No GPU is needed: no call here
+reaches a kernel launch (every argument check fails first, or the call is a
+host-only query with an explicit compute-unit count).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from residual_add_rmsnorm_rows_amd import _lib as L
+import residual_add_rmsnorm_rows_amd as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rmsnorm_rows.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_what_binding_knows():
+    assert _declared_functions() == sorted(L.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.rn_abi_version() == L.ABI_VERSION
+    for st in range(5):
+        assert lib.rn_status_string(st).decode().startswith("RN_")
+    assert b"unknown" in lib.rn_status_string(99)
+
+
+FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced (every call below fails first)
+BF = L.make_flags("bf16", "bf16", "bf16", "bf16", False)
+
+
+def _fwd(lib, x=FAKE, res=FAKE, w=FAKE, out=FAKE + 0x1000, res_out=FAKE + 0x2000, scale=None, amax=None,
+         rows=4, hidden=1024, eps=1e-6, flags=BF):
+    return lib.rmsnorm_fwd_ex(x, res, w, out, res_out, scale, amax, rows, hidden, eps, flags, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=-1), L.RN_ERR_INVALID_ARG),
+    (dict(hidden=0), L.RN_ERR_INVALID_ARG),
+    (dict(flags=BF | (1 << 9)), L.RN_ERR_INVALID_ARG),
+    (dict(flags=3), L.RN_ERR_INVALID_ARG),
+    (dict(eps=-1.0), L.RN_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), L.RN_ERR_INVALID_ARG),
+    (dict(eps=float("inf")), L.RN_ERR_INVALID_ARG),
+    (dict(x=None), L.RN_ERR_INVALID_ARG),
+    (dict(w=None), L.RN_ERR_INVALID_ARG),
+    (dict(out=None), L.RN_ERR_INVALID_ARG),
+    (dict(res_out=None), L.RN_ERR_INVALID_ARG),
+    (dict(res=None), L.RN_ERR_INVALID_ARG),
+    (dict(res_out=FAKE + 0x1000), L.RN_ERR_INVALID_ARG),  # out == residual_out
+    (dict(scale=FAKE), L.RN_ERR_INVALID_ARG),  # scale without fp8
+    (dict(flags=L.make_flags("bf16", "bf16", "bf16", "fp8_e4m3fn", False)), L.RN_ERR_INVALID_ARG),  # fp8, no scale
+    (dict(hidden=1001), L.RN_ERR_UNSUPPORTED),
+    (dict(hidden=32768 + 8), L.RN_ERR_UNSUPPORTED),
+    (dict(flags=L.make_flags("f32", "bf16", "f32", "f32", False), hidden=1024), L.RN_ERR_UNSUPPORTED),
+    (dict(flags=L.make_flags("fp8_e4m3fn", "bf16", "bf16", "bf16", False)), L.RN_ERR_UNSUPPORTED),
+    (dict(x=FAKE + 8), L.RN_ERR_MISALIGNED),
+    (dict(res_out=FAKE + 0x2004), L.RN_ERR_MISALIGNED),
+    (dict(flags=L.make_flags("bf16", "bf16", "bf16", "fp8_e4m3fn", False), scale=FAKE + 2), L.RN_ERR_MISALIGNED),
+])
+def test_rmsnorm_rejects_before_any_hip_call(lib, kw, status):
+    assert _fwd(lib, **kw) == status
+    assert lib.rn_last_error().decode() != ""
+
+
+def test_rows_zero_is_a_noop(lib):
+    assert _fwd(lib, rows=0, x=None, res=None, w=None, out=None, res_out=None) == L.RN_OK
+    assert lib.rn_last_error() == b""
+
+
+def test_qknorm_rejects_before_any_hip_call(lib):
+    f = 0
+    q = FAKE
+
+    def call(**kw):
+        a = dict(q=q, k=None, qw=q, kw=None, qo=q, ko=None, T=4, nq=2, nk=0, D=128, qs=0, ks=0, eps=1e-6, f=f)
+        a.update(kw)
+        return lib.qknorm_fwd(a["q"], a["k"], a["qw"], a["kw"], a["qo"], a["ko"], a["T"], a["nq"], a["nk"],
+                              a["D"], a["qs"], a["ks"], a["eps"], a["f"], None)
+
+    assert call(D=96) == L.RN_ERR_UNSUPPORTED
+    assert call(nq=0) == L.RN_ERR_INVALID_ARG
+    assert call(T=-1) == L.RN_ERR_INVALID_ARG
+    assert call(f=1 << 6) == L.RN_ERR_INVALID_ARG       # out-dtype bits are not used by qknorm
+    assert call(f=2) == L.RN_ERR_UNSUPPORTED            # fp8 tensors
+    assert call(qs=100) == L.RN_ERR_INVALID_ARG         # stride below heads * head_dim
+    assert call(nk=2) == L.RN_ERR_INVALID_ARG           # k missing
+    assert call(q=FAKE + 4) == L.RN_ERR_MISALIGNED
+    assert call(qs=256 + 4) == L.RN_ERR_MISALIGNED      # stride of 8 bytes past 16-byte alignment
+    assert call(T=1 << 30, nq=4) == L.RN_ERR_UNSUPPORTED
+    assert call(T=0, q=None, qw=None, qo=None) == L.RN_OK
+
+
+def _cfg(rows, hidden, x="bf16", out="bf16", cus=256):
+    return R.query_config(rows, hidden, x_dtype=x, out_dtype=out, num_cus=cus)
+
+
+@pytest.mark.parametrize("x", ["bf16", "f32"])
+def test_selector_covers_every_row(x):
+    vec = 8 if x == "bf16" else 4
+    hmax = 32768 if x == "bf16" else 16384
+    for hidden in list(range(vec, 4096 + 1, vec * 7)) + [7168, 8192, 12288, 16384, hmax]:
+        if hidden > hmax:
+            continue
+        for rows in (1, 8, 255, 256, 257, 4096, 16384):
+            c = _cfg(rows, hidden, x=x)
+            W, NV = c["waves_per_row"], c["vecs_per_lane"]
+            assert c["vec"] == vec
+            assert 1 <= W <= 16 and NV in (1, 2, 4, 8)
+            assert 64 * W * NV * vec >= hidden, (rows, hidden, c)
+            assert c["block_threads"] == 64 * W
+            assert c["block_threads"] <= (512 if NV == 8 else 1024)
+            assert c["grid"] == rows
+
+
+def test_selector_shapes_of_the_workloads():
+    # decode: one wave per row while a lane holds the row (no LDS, no barrier)
+    assert _cfg(8, 1024)["waves_per_row"] == 1
+    assert _cfg(256, 4096)["waves_per_row"] == 1
+    # prefill: no idle lanes for 8192 and 7168
+    c3 = _cfg(16384, 8192)
+    assert 64 * c3["waves_per_row"] * c3["vecs_per_lane"] * 8 == 8192
+    c5 = _cfg(8192, 7168, out="fp8_e4m3fn")
+    assert 64 * c5["waves_per_row"] * c5["vecs_per_lane"] * 8 == 7168
+
+
+def test_head_mapping_covers_each_row_once():
+    """Replays the per-head kernel's row mapping on the CPU for the selector's grids."""
+    for dtype, D in (("bf16", 64), ("bf16", 128), ("bf16", 256), ("f32", 64), ("f32", 128), ("f32", 256)):
+        for tokens, nq, nk in ((4096, 32, 0), (7, 3, 1), (1, 1, 0), (33, 32, 8), (1000, 5, 3)):
+            c = R.query_qknorm_config(tokens, nq, nk, D, dtype=dtype)
+            vec = 8 if dtype == "bf16" else 4
+            G = D // vec
+            gpw = 64 // G
+            rpl = c["rows_per_lane"]
+            total = tokens * (nq + nk)
+            seen = {}
+            waves = c["grid"] * c["block_threads"] // 64
+            for wave in range(waves):
+                first = wave * gpw * rpl
+                for j in range(rpl):
+                    for grp in range(gpw):
+                        row = first + j * gpw + grp
+                        if row < total:
+                            seen[row] = seen.get(row, 0) + 1
+            assert len(seen) == total and set(seen.values()) == {1}, (dtype, D, tokens, nq, nk)
+            # no workgroup lies wholly past the end
+            assert (c["grid"] - 1) * (c["block_threads"] // 64) * gpw * rpl < total
+
+
+def test_query_config_validates(lib):
+    cfg = L.LaunchConfig()
+    assert lib.rmsnorm_query_config(10, 1001, 0, 256, ctypes.byref(cfg)) == L.RN_ERR_UNSUPPORTED
+    assert lib.rmsnorm_query_config(10, 1024, 0, 256, None) == L.RN_ERR_INVALID_ARG
+    assert lib.qknorm_query_config(10, 2, 0, 100, 0, 256, ctypes.byref(cfg)) == L.RN_ERR_UNSUPPORTED
+
+
+def test_explicit_config_is_checked(lib):
+    cfg = L.LaunchConfig()
+    cfg.kernel, cfg.waves_per_row, cfg.vecs_per_lane, cfg.grid = 0, 1, 1, 4
+    # 64 lanes x 1 vector x 8 < 1024 elements: rejected before any HIP call
+    st = lib.rmsnorm_fwd_config(FAKE, FAKE, FAKE, FAKE + 0x1000, FAKE + 0x2000, None, None, 4, 1024, 1e-6, BF,
+                                ctypes.byref(cfg), None)
+    assert st == L.RN_ERR_INVALID_ARG
+    cfg.waves_per_row, cfg.vecs_per_lane = 16, 8  # 1024 threads with 8 vectors per lane: not built
+    st = lib.rmsnorm_fwd_config(FAKE, FAKE, FAKE, FAKE + 0x1000, FAKE + 0x2000, None, None, 4, 1024, 1e-6, BF,
+                                ctypes.byref(cfg), None)
+    assert st == L.RN_ERR_INVALID_ARG
+    cfg.waves_per_row, cfg.vecs_per_lane, cfg.grid = 2, 1, 5  # grid above rows
+    st = lib.rmsnorm_fwd_config(FAKE, FAKE, FAKE, FAKE + 0x1000, FAKE + 0x2000, None, None, 4, 1024, 1e-6, BF,
+                                ctypes.byref(cfg), None)
+    assert st == L.RN_ERR_INVALID_ARG

@@ -1,0 +1,292 @@
+"""GPU parity: the HIP library (called through the C ABI) against the CPU oracle.
+
+Inputs come from the seeded generator in ``workloads``; both sides see the
+same bits.  Tolerances are those of ``oracle.compare``: bf16 outputs within
+one bf16 ulp, f32 within 1e-5 relative, fp8 codes within one step, the
+updated residual bit-exact, fp8 scales within 1e-5 relative with the
+``amax / 448`` formula bit-exact on the GPU's own amax.
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import residual_add_rmsnorm_rows_amd as R
+import workloads as WL
+from oracle import compare as C
+from oracle import rownorm as O
+from residual_add_rmsnorm_rows_amd import _lib as L
+from tests.gpu_util import TORCH_DTYPES, judge_rows, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def run_rownorm(wl, inputs, config=None, inplace=False):
+    x = to_dev(inputs["x"], wl.x_dtype)
+    res = None if inputs["residual"] is None else to_dev(inputs["residual"], wl.res_dtype)
+    w = to_dev(inputs["weight"], wl.w_dtype)
+    kw = {}
+    if inplace:
+        if TORCH_DTYPES[wl.out_dtype] == x.dtype:
+            kw["out"] = x
+        if res is not None:
+            kw["residual_out"] = res
+    r = R.fused_add_rmsnorm(x, res, w, wl.eps, weight_plus_one=wl.weight_plus_one,
+                            out_dtype=TORCH_DTYPES[wl.out_dtype], return_amax=wl.out_dtype == "fp8_e4m3fn",
+                            config=config, **kw)
+    torch.cuda.synchronize()
+    return r
+
+
+def judge(wl, inputs, r, rows=None):
+    sel = slice(None) if rows is None else rows
+    sub = {"x": inputs["x"][sel], "residual": None if inputs["residual"] is None else inputs["residual"][sel],
+           "weight": inputs["weight"]}
+    out = to_host(r.out)[sel]
+    res_out = None if r.residual_out is None else to_host(r.residual_out)[sel]
+    scale = None if r.scale is None else r.scale.cpu().numpy()[sel]
+    amax = None if r.amax is None else r.amax.cpu().numpy()[sel]
+    return judge_rows(sub, wl.x_dtype, wl.res_dtype, wl.w_dtype, wl.out_dtype, wl.eps, wl.weight_plus_one,
+                      out, res_out, scale, amax)
+
+
+ROW_WORKLOADS = ["decode_8x1024", "decode_256x4096", "prefill_16384x8192", "prefill_fp8_8192x7168"]
+
+
+@pytest.mark.parametrize("name", ROW_WORKLOADS)
+def test_workload_parity_small(name):
+    """Each fused add+RMSNorm workload at its hidden size, with few enough rows
+    for the oracle to check every element (ragged row count, several tiles)."""
+    wl = WL.WORKLOADS[name]
+    wl = wl.with_rows(min(wl.rows, 300))
+    _announce(f"{name} rows={wl.rows} hidden={wl.hidden}")
+    inputs = WL.generate_rownorm(wl, seed=0)
+    rep = judge(wl, inputs, run_rownorm(wl, inputs))
+    print(rep)
+    assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("name", ["prefill_16384x8192", "prefill_fp8_8192x7168", "decode_256x4096"])
+def test_workload_parity_full_size_sampled(name):
+    """Full-size workload in the benchmark's launch configuration (the
+    selector's); the oracle checks sampled rows, including the first and last."""
+    wl = WL.WORKLOADS[name]
+    _announce(f"{name} full size rows={wl.rows} hidden={wl.hidden} cfg={R.query_config(wl.rows, wl.hidden, x_dtype=wl.x_dtype, out_dtype=wl.out_dtype)}")
+    inputs = WL.generate_rownorm(wl, seed=0)
+    r = run_rownorm(wl, inputs)
+    rng = np.random.default_rng(123)
+    rows = np.unique(np.concatenate([np.arange(4), np.arange(wl.rows - 4, wl.rows),
+                                     rng.integers(0, wl.rows, 56)]))
+    rep = judge(wl, inputs, r, rows)
+    print(rep)
+    assert rep["ok"], rep
+
+
+def test_qknorm_workload_full():
+    wl = WL.WORKLOADS["qknorm_4096x32x128"]
+    _announce(f"{wl.name} tokens={wl.tokens} heads={wl.num_q_heads} D={wl.head_dim} "
+              f"cfg={R.query_qknorm_config(wl.tokens, wl.num_q_heads, 0, wl.head_dim)}")
+    inp = WL.generate_qknorm(wl, seed=0)
+    q = to_dev(inp["q"].reshape(wl.tokens, -1), wl.dtype).view(wl.tokens, wl.num_q_heads, wl.head_dim)
+    qw = to_dev(inp["q_weight"], wl.w_dtype)
+    q_out, _ = R.qk_norm(q, None, qw, None, wl.eps, weight_plus_one=wl.weight_plus_one, inplace=False)
+    torch.cuda.synchronize()
+    qy, _ = O.qknorm(O.decode(inp["q"], wl.dtype), None, O.decode(inp["q_weight"], wl.w_dtype), None, wl.eps,
+                     1.0 if wl.weight_plus_one else 0.0)
+    rep = C.check_bf16(to_host(q_out), qy)
+    print(rep)
+    assert rep["ok"], rep
+    # in place (the page's form) gives the same bits
+    R.qk_norm(q, None, qw, None, wl.eps, inplace=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(q), to_host(q_out))
+
+
+DTYPE_COMBOS = [
+    (x, res, w, out, b)
+    for x in ("bf16", "f32")
+    for res in ((None, "bf16", "f32") if x == "bf16" else (None, "f32"))
+    for w in ("bf16", "f32")
+    for out in ("bf16", "f32", "fp8_e4m3fn")
+    for b in (False, True)
+]
+
+
+@pytest.mark.parametrize("x,res,w,out,b", DTYPE_COMBOS)
+@pytest.mark.parametrize("rows", [37, 300])
+def test_every_dtype_combination(x, res, w, out, b, rows):
+    H = 1000
+    wl = WL.RowNormWorkload(name="combo", kind="test", rows=rows, hidden=H, x_dtype=x, res_dtype=res, w_dtype=w,
+                            out_dtype=out, x_dist=WL.Dist(0, 1, 0.01, 20.0), res_dist=WL.Dist(0, 2),
+                            w_dist=WL.Dist(0.0 if b else 1.0, 0.1), weight_plus_one=b, eps=1e-5)
+    _announce(f"combo x={x} res={res} w={w} out={out} plus_one={b} rows={rows} H={H}")
+    inputs = WL.generate_rownorm(wl, seed=7)
+    rep = judge(wl, inputs, run_rownorm(wl, inputs))
+    assert rep["ok"], rep
+
+
+def _variants(hidden, vec):
+    nvec = hidden // vec
+    for W in range(1, 17):
+        for NV in (1, 2, 4, 8):
+            if 64 * W > (512 if NV == 8 else 1024):
+                continue
+            if 64 * W * NV >= nvec and 64 * W * (NV // 2 if NV > 1 else 0) < nvec + 64 * W:
+                yield W, NV
+
+
+@pytest.mark.parametrize("hidden,x,out", [(8192, "bf16", "bf16"), (7168, "bf16", "fp8_e4m3fn"),
+                                          (1000, "bf16", "bf16"), (1000, "f32", "f32"), (64, "bf16", "bf16"),
+                                          (8, "bf16", "fp8_e4m3fn"), (3072, "f32", "bf16")])
+def test_every_launch_variant(hidden, x, out):
+    """Every (waves per row, vectors per lane) variant that covers the row, with
+    a workgroup per row and with fewer workgroups than rows (row striding)."""
+    res = "f32"
+    wl = WL.RowNormWorkload(name="variant", kind="test", rows=67, hidden=hidden, x_dtype=x, res_dtype=res,
+                            w_dtype="bf16", out_dtype=out, x_dist=WL.Dist(0, 1), res_dist=WL.Dist(0, 4),
+                            w_dist=WL.Dist(1, 0.1), weight_plus_one=False, eps=1e-6)
+    inputs = WL.generate_rownorm(wl, seed=3)
+    vec = 8 if x == "bf16" else 4
+    n = 0
+    for W, NV in _variants(hidden, vec):
+        for grid in (wl.rows, 5):
+            cfg = L.LaunchConfig()
+            cfg.kernel, cfg.waves_per_row, cfg.vecs_per_lane, cfg.grid = L.RN_KERNEL_ROWS, W, NV, grid
+            _announce(f"variant H={hidden} x={x} out={out} W={W} NV={NV} grid={grid}")
+            rep = judge(wl, inputs, run_rownorm(wl, inputs, config=cfg))
+            assert rep["ok"], (W, NV, grid, rep)
+            n += 1
+    assert n > 0
+
+
+def test_edge_cases():
+    base = WL.WORKLOADS["decode_8x1024"]
+    # rows == 0: no launch, empty outputs
+    _announce("rows=0")
+    x = torch.empty((0, 1024), dtype=torch.bfloat16, device="cuda")
+    r = R.fused_add_rmsnorm(x, x.clone(), torch.ones(1024, dtype=torch.bfloat16, device="cuda"), 1e-6)
+    assert r.out.shape == (0, 1024)
+    # one row; largest hidden; smallest hidden
+    for rows, H in ((1, 1024), (3, 32768), (5, 8), (2, 16384)):
+        _announce(f"rows={rows} H={H}")
+        wl = base.with_rows(rows).with_hidden(H)
+        inputs = WL.generate_rownorm(wl, seed=11)
+        rep = judge(wl, inputs, run_rownorm(wl, inputs))
+        assert rep["ok"], (rows, H, rep)
+    # all-zero rows: y = 0 exactly; fp8 scale 0, codes 0
+    _announce("zero rows")
+    for out in ("bf16", "fp8_e4m3fn"):
+        wl = WL.WORKLOADS["prefill_fp8_8192x7168"].with_rows(4)
+        wl = WL.RowNormWorkload(**{**wl.__dict__, "out_dtype": out})
+        inputs = WL.generate_rownorm(wl, seed=0)
+        inputs["x"][1:3] = 0
+        inputs["residual"][1:3] = 0
+        r = run_rownorm(wl, inputs)
+        o = to_host(r.out)
+        assert np.all(o[1:3] == 0)
+        if out == "fp8_e4m3fn":
+            assert np.all(r.scale.cpu().numpy()[1:3] == 0)
+        rep = judge(wl, inputs, r)
+        assert rep["ok"], rep
+    # eps = 0 on non-zero rows
+    _announce("eps=0")
+    wl = WL.RowNormWorkload(**{**base.__dict__, "eps": 0.0})
+    inputs = WL.generate_rownorm(wl, seed=2)
+    rep = judge(wl, inputs, run_rownorm(wl, inputs))
+    assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("name", ["decode_256x4096", "prefill_16384x8192"])
+def test_in_place(name):
+    wl = WL.WORKLOADS[name].with_rows(64)
+    _announce(f"in place {name}")
+    inputs = WL.generate_rownorm(wl, seed=5)
+    r = run_rownorm(wl, inputs, inplace=True)
+    rep = judge(wl, inputs, r)
+    assert rep["ok"], rep
+
+
+QK_CASES = [
+    # dtype, w dtype, head_dim, tokens, nq, nk, plus_one, strided
+    ("bf16", "bf16", 128, 4096, 32, 0, False, False),
+    ("bf16", "bf16", 128, 333, 32, 8, False, True),
+    ("bf16", "bf16", 64, 77, 16, 4, True, False),
+    ("bf16", "bf16", 256, 51, 8, 2, False, True),
+    ("bf16", "f32", 128, 19, 5, 3, True, False),
+    ("f32", "f32", 64, 41, 7, 1, False, False),
+    ("f32", "bf16", 128, 29, 4, 4, True, True),
+    ("f32", "f32", 256, 13, 3, 2, False, False),
+    ("bf16", "bf16", 128, 1, 1, 0, False, False),
+]
+
+
+@pytest.mark.parametrize("dt,wdt,D,T,nq,nk,b,strided", QK_CASES)
+def test_qknorm_parity(dt, wdt, D, T, nq, nk, b, strided):
+    _announce(f"qknorm dt={dt} w={wdt} D={D} T={T} nq={nq} nk={nk} plus_one={b} strided={strided}")
+    qwl = WL.QKNormWorkload(name="qk", tokens=T, num_q_heads=nq, num_k_heads=nk, head_dim=D, dtype=dt, w_dtype=wdt,
+                            x_dist=WL.Dist(0, 2), w_dist=WL.Dist(0.0 if b else 1.0, 0.1), weight_plus_one=b,
+                            eps=1e-6)
+    inp = WL.generate_qknorm(qwl, seed=9)
+    qh = to_dev(inp["q"].reshape(T, -1), dt)
+    kh = None if nk == 0 else to_dev(inp["k"].reshape(T, -1), dt)
+    if strided:
+        # Q and K as views of one fused [T, (nq + 2 nk) * D] QKV buffer
+        qkv = torch.zeros((T, (nq + 2 * nk) * D), dtype=qh.dtype, device="cuda")
+        qkv[:, : nq * D] = qh
+        if nk:
+            qkv[:, nq * D: (nq + nk) * D] = kh
+        q = qkv[:, : nq * D].view(T, nq, D)
+        k = None if nk == 0 else qkv[:, nq * D: (nq + nk) * D].view(T, nk, D)
+    else:
+        q = qh.view(T, nq, D)
+        k = None if nk == 0 else kh.view(T, nk, D)
+    qw = to_dev(inp["q_weight"], wdt)
+    kw = None if nk == 0 else to_dev(inp["k_weight"], wdt)
+    before = None if not strided else to_host(qkv[:, (nq + nk) * D:]).copy()
+    R.qk_norm(q, k, qw, kw, qwl.eps, weight_plus_one=b, inplace=True)
+    torch.cuda.synchronize()
+    qy, ky = O.qknorm(O.decode(inp["q"], dt), None if nk == 0 else O.decode(inp["k"], dt),
+                      O.decode(inp["q_weight"], wdt), None if nk == 0 else O.decode(inp["k_weight"], wdt),
+                      qwl.eps, 1.0 if b else 0.0)
+    chk = C.check_bf16 if dt == "bf16" else C.check_f32
+    rq = chk(to_host(q.reshape(T, -1) if not strided else q.contiguous()).reshape(qy.shape), qy)
+    assert rq["ok"], rq
+    if nk:
+        rk = chk(to_host(k.contiguous()).reshape(ky.shape), ky)
+        assert rk["ok"], rk
+    if strided:  # the V part of the fused buffer is untouched
+        assert np.array_equal(to_host(qkv[:, (nq + nk) * D:]), before)
+
+
+def test_qknorm_equals_rmsnorm_on_reshaped_rows():
+    """GPU vs GPU: per-head norm of [T, H, D] == row norm of [T*H, D] (same bits)."""
+    _announce("qknorm vs rmsnorm reshape")
+    wl = WL.WORKLOADS["qknorm_4096x32x128"].with_tokens(512)
+    inp = WL.generate_qknorm(wl, seed=1)
+    q = to_dev(inp["q"].reshape(wl.tokens, -1), "bf16").view(wl.tokens, wl.num_q_heads, wl.head_dim)
+    w = to_dev(inp["q_weight"], "bf16")
+    a, _ = R.qk_norm(q, None, w, None, wl.eps, inplace=False)
+    b = R.rmsnorm(q.reshape(-1, wl.head_dim), w, wl.eps).out
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(a).reshape(-1), to_host(b).reshape(-1))
+
+
+def test_deterministic():
+    wl = WL.WORKLOADS["prefill_fp8_8192x7168"].with_rows(512)
+    _announce("determinism")
+    inputs = WL.generate_rownorm(wl, seed=4)
+    r1 = run_rownorm(wl, inputs)
+    r2 = run_rownorm(wl, inputs)
+    assert np.array_equal(to_host(r1.out), to_host(r2.out))
+    assert np.array_equal(r1.scale.cpu().numpy(), r2.scale.cpu().numpy())
+
+
+def test_empty_kernel_launch():
+    L.check(L.lib().rn_launch_empty(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
