@@ -287,12 +287,14 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of 1 GiB (torch copy_), the reference for scaling "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only; the row kernels shard over rows with no exchange, "
-              "so a multi-GPU figure is the one-GPU figure times the GPU count and is not measured here. "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py: this benchmark runs on one GPU only (--gpus 1); multi-GPU runs are not part "
+              "of it.", file=sys.stderr)
         return 2
     if args.steps < 1 or args.warmup < 0:
         print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
@@ -344,6 +346,16 @@ def main() -> int:
     }
     del call
     torch.cuda.empty_cache()
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration"] = {"bytes_read": n, "bytes_written": n, "launches": 3}
+        del src, dst
+        torch.cuda.empty_cache()
     if not args.no_secondary:
         sec = {}
         for name in ("decode_8x1024", "decode_256x4096"):

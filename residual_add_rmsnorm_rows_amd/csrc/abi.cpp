@@ -105,7 +105,6 @@ rn_status rows_entry(const void* x, const void* residual, const void* weight, vo
   a.amax = out_amax;
   a.rows = rows;
   a.hidden = static_cast<int32_t>(hidden);
-  a.nvec = static_cast<int32_t>(hidden / cfg.vec);
   a.eps = eps;
   return launch(fn, cfg.grid, cfg.block_threads, &a, stream);
 }

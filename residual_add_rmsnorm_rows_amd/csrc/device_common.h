@@ -69,6 +69,70 @@ __device__ __forceinline__ void store_words(void* p, const uint32_t (&w)[BYTES /
 }
 
 // ---------------------------------------------------------------------------
+// Buffer addressing.  A buffer resource (four scalar registers) holds a base
+// address and a size in bytes; raw buffer loads and stores take a 32-bit lane
+// offset from that base, and the hardware range check turns an access at or
+// past the size into a load of zeros or a dropped store.  A row's tail
+// therefore needs no branch: lanes whose chunk lies past the end of the row
+// load zeros (neutral for the sum of squares and the max) and store nothing.
+// The fourth descriptor dword is the gfx9-family buffer format word (32-bit
+// data format, no swizzle, stride 0: raw byte addressing).
+// ---------------------------------------------------------------------------
+
+constexpr int kBufferFormatWord = 0x00020000;
+constexpr int kCachePolicyNontemporal = 2;  // "nt" on gfx94x/gfx950 (the former slc bit)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           kBufferFormatWord);
+}
+
+template <int BYTES>
+__device__ __forceinline__ void buffer_load_words(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                  uint32_t (&w)[BYTES / 4]) {
+  static_assert(BYTES == 4 || BYTES == 8 || BYTES == 16 || BYTES == 32, "lane vector size");
+  const int o = static_cast<int>(off);
+  if constexpr (BYTES == 32) {
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0);
+    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, o + 16, 0, 0);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  } else if constexpr (BYTES == 16) {
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+  } else if constexpr (BYTES == 8) {
+    const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, 0);
+    w[0] = a.x; w[1] = a.y;
+  } else {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0);
+  }
+}
+
+// Write-once outputs carry the nontemporal hint: this kernel never re-reads
+// them, and on MI355X the hint measured faster than plain stores for these
+// streams (when each store instruction writes one contiguous run).
+template <int BYTES>
+__device__ __forceinline__ void buffer_store_words(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                   const uint32_t (&w)[BYTES / 4]) {
+  static_assert(BYTES == 4 || BYTES == 8 || BYTES == 16 || BYTES == 32, "lane vector size");
+  const int o = static_cast<int>(off);
+  if constexpr (BYTES == 32) {
+    const u32x4 a = {w[0], w[1], w[2], w[3]};
+    const u32x4 b = {w[4], w[5], w[6], w[7]};
+    __builtin_amdgcn_raw_buffer_store_b128(a, r, o, 0, kCachePolicyNontemporal);
+    __builtin_amdgcn_raw_buffer_store_b128(b, r, o + 16, 0, kCachePolicyNontemporal);
+  } else if constexpr (BYTES == 16) {
+    const u32x4 a = {w[0], w[1], w[2], w[3]};
+    __builtin_amdgcn_raw_buffer_store_b128(a, r, o, 0, kCachePolicyNontemporal);
+  } else if constexpr (BYTES == 8) {
+    const u32x2 a = {w[0], w[1]};
+    __builtin_amdgcn_raw_buffer_store_b64(a, r, o, 0, kCachePolicyNontemporal);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(w[0], r, o, 0, kCachePolicyNontemporal);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Element codecs (float32 in registers).
 // ---------------------------------------------------------------------------
 

@@ -24,7 +24,6 @@ struct RowArgs {
   float* amax;           // fp8 output only, may be nullptr
   int64_t rows;
   int32_t hidden;        // elements per row
-  int32_t nvec;          // lane vectors per row: hidden / vec
   float eps;
 };
 

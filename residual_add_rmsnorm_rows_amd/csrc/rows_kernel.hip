@@ -9,12 +9,21 @@
 //   fp8: p = (w + b) * h, amax = max|p| * inv, y = p * inv,
 //        code = e4m3fn(y * (448 / amax)), scale = amax / 448
 //
-// Layout of one row across the workgroup: the row is H / VEC lane vectors of
-// 16 bytes of x (VEC = 8 bf16 or 4 f32).  Vector v = (s * W + wave) * 64 + lane
-// belongs to lane `lane` of wave `wave` at step s < NV, so every load and
-// store instruction of a wave touches 64 consecutive vectors (1 KiB of x).
-// All loads of a row are issued before any arithmetic, the row then lives in
-// registers: each input byte is read once and each output byte written once.
+// Layout of one row across the workgroup: each lane holds NV steps of VEC
+// elements, VEC = 16 bytes of x (8 bf16 or 4 f32).  Step s of lane `lane` in
+// wave `wave` is split into SUB chunks of U = VEC / SUB contiguous elements;
+// chunk c covers row elements [u * U, u * U + U) with
+//     u = ((s * W + wave) * SUB + c) * 64 + lane,
+// so every load and store instruction of a wave touches one contiguous run of
+// 64 * U elements of each tensor.  SUB is 1 when every tensor has the width of
+// x; with bf16 x and a 32-bit residual, weight or output it is 2, which keeps
+// the 32-bit tensors at 16 bytes per lane per instruction (one whole 1 KiB run)
+// instead of two interleaved half-runs, whose nontemporal stores would reach
+// HBM as partial lines.  All loads of a row are issued before any arithmetic
+// and the row then lives in registers: each input byte is read once and each
+// output byte written once.  Every tensor row is addressed through a buffer
+// resource sized to the row, so chunks past the row end (a ragged hidden size)
+// read zeros and write nothing, without a branch.
 //
 // Reduction: per-lane partial sum -> DPP inside each 16-lane row -> readlane
 // of the four row totals (uniform) -> with W > 1, one float per wave through
@@ -42,6 +51,8 @@ namespace {
 
 constexpr int storage_bytes(int dt) { return dt == kBF16 ? 2 : dt == kFP8 ? 1 : 4; }
 
+constexpr int max_of(int a, int b) { return a > b ? a : b; }
+
 template <int XD, int RD, int WD, int OD, int BIAS, int NV>
 __global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowArgs a) {
   constexpr int XB = storage_bytes(XD);
@@ -51,9 +62,14 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowA
   constexpr int RB = storage_bytes(RD);
   constexpr int WB = storage_bytes(WD);
   constexpr int OB = storage_bytes(OD);
-  constexpr int RW = VEC * RB / 4;        // dwords of residual per lane vector
-  constexpr int WW = VEC * WB / 4;        // dwords of weight per lane vector
-  constexpr int OW = (VEC * OB + 3) / 4;  // dwords of output per lane vector
+  constexpr int WIDEST = max_of(max_of(XB, HAS_RES ? RB : 1), max_of(WB, OB));
+  constexpr int SUB = WIDEST / XB;        // chunks per step (1 or 2)
+  constexpr int U = VEC / SUB;            // elements per chunk
+  constexpr int XW = U * XB / 4;          // dwords of x per chunk
+  constexpr int RW = U * RB / 4;          // dwords of residual per chunk
+  constexpr int WW = U * WB / 4;          // dwords of weight per chunk
+  constexpr int OW = (U * OB + 3) / 4;    // dwords of output per chunk
+  static_assert(SUB == 1 || SUB == 2, "chunking");
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -63,73 +79,75 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowA
 
   const char* __restrict__ xp = static_cast<const char*>(a.x);
   const char* __restrict__ rp = static_cast<const char*>(a.res);
-  const char* __restrict__ wp = static_cast<const char*>(a.w);
   char* __restrict__ op = static_cast<char*>(a.out);
   char* __restrict__ rop = static_cast<char*>(a.res_out);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, static_cast<uint32_t>(a.hidden) * WB);
+
+  // Byte offset (in units of one element) of chunk (s, c) of this lane from
+  // the row start: (((s * W + wave) * SUB + c) * 64 + lane) * U.  Chunks past
+  // the row end fall outside the row's buffer resource.
+  auto elem_of = [&](int s, int c) -> uint32_t {
+    return static_cast<uint32_t>((((s * nw + wave) * SUB + c) * 64 + lane) * U);
+  };
 
   for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
     const int64_t row_elem = row * a.hidden;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(xp + row_elem * XB, static_cast<uint32_t>(a.hidden) * XB);
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(rp + row_elem * RB, static_cast<uint32_t>(a.hidden) * RB);
+    const __amdgpu_buffer_rsrc_t orr = make_rsrc(op + row_elem * OB, static_cast<uint32_t>(a.hidden) * OB);
+    const __amdgpu_buffer_rsrc_t ror = make_rsrc(rop + row_elem * RB, static_cast<uint32_t>(a.hidden) * RB);
 
     // 1. Issue every load of this lane's share of the row.
-    uint32_t xw[NV][4];
-    uint32_t rw[NV][HAS_RES ? RW : 1];
-    uint32_t ww[NV][WW];
-    bool ok[NV];
+    uint32_t xw[NV][SUB][XW];
+    uint32_t rw[NV][SUB][HAS_RES ? RW : 1];
+    uint32_t ww[NV][SUB][WW];
 #pragma unroll
     for (int s = 0; s < NV; ++s) {
-      const int v = (s * nw + wave) * 64 + lane;
-      ok[s] = v < a.nvec;
-      if (ok[s]) {
-        const int64_t e = row_elem + static_cast<int64_t>(v) * VEC;
-        load_words<16>(xp + e * XB, xw[s]);
-        if constexpr (HAS_RES) load_words<RW * 4>(rp + e * RB, rw[s]);
-        load_words<WW * 4>(wp + static_cast<int64_t>(v) * VEC * WB, ww[s]);
-      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xw[s][i] = 0;
-#pragma unroll
-        for (int i = 0; i < (HAS_RES ? RW : 1); ++i) rw[s][i] = 0;
-#pragma unroll
-        for (int i = 0; i < WW; ++i) ww[s][i] = 0;
+      for (int c = 0; c < SUB; ++c) {
+        const uint32_t e = elem_of(s, c);
+        buffer_load_words<XW * 4>(xr, e * XB, xw[s][c]);
+        if constexpr (HAS_RES) buffer_load_words<RW * 4>(rr, e * RB, rw[s][c]);
+        buffer_load_words<WW * 4>(wr, e * WB, ww[s][c]);
       }
     }
 
     // 2. Residual add (rounded once to the residual dtype and written back),
     //    local sum of squares of the rounded value; fp8 also takes the
     //    weighted products and their local max magnitude.
-    float h[NV][VEC];
+    float h[NV][SUB][U];
     float ss = 0.f;
     float mx = 0.f;
 #pragma unroll
     for (int s = 0; s < NV; ++s) {
-      float xf[VEC];
-      unpack<XD, VEC>(xw[s], xf);
-      if constexpr (HAS_RES) {
-        float rf[VEC], sum[VEC];
-        unpack<RD, VEC>(rw[s], rf);
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) sum[i] = xf[i] + rf[i];
-        uint32_t hw[RW];
-        pack<RD, VEC>(sum, hw);
-        unpack<RD, VEC>(hw, h[s]);
-        if (ok[s]) {
-          const int64_t e = row_elem + static_cast<int64_t>((s * nw + wave) * 64 + lane) * VEC;
-          store_words<RW * 4>(rop + e * RB, hw);
+      for (int c = 0; c < SUB; ++c) {
+        float xf[U];
+        unpack<XD, U>(xw[s][c], xf);
+        if constexpr (HAS_RES) {
+          float rf[U], sum[U];
+          unpack<RD, U>(rw[s][c], rf);
+#pragma unroll
+          for (int i = 0; i < U; ++i) sum[i] = xf[i] + rf[i];
+          uint32_t hw[RW];
+          pack<RD, U>(sum, hw);
+          unpack<RD, U>(hw, h[s][c]);
+          buffer_store_words<RW * 4>(ror, elem_of(s, c) * RB, hw);
+        } else {
+#pragma unroll
+          for (int i = 0; i < U; ++i) h[s][c][i] = xf[i];
         }
-      } else {
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) h[s][i] = xf[i];
-      }
+        for (int i = 0; i < U; ++i) ss += h[s][c][i] * h[s][c][i];
+        if constexpr (FP8) {
+          float wf[U];
+          unpack<WD, U>(ww[s][c], wf);
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) ss += h[s][i] * h[s][i];
-      if constexpr (FP8) {
-        float wf[VEC];
-        unpack<WD, VEC>(ww[s], wf);
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          if constexpr (BIAS) wf[i] += 1.0f;
-          h[s][i] = wf[i] * h[s][i];
-          mx = __builtin_fmaxf(mx, __builtin_fabsf(h[s][i]));
+          for (int i = 0; i < U; ++i) {
+            if constexpr (BIAS) wf[i] += 1.0f;
+            h[s][c][i] = wf[i] * h[s][c][i];
+            mx = __builtin_fmaxf(mx, __builtin_fabsf(h[s][c][i]));
+          }
         }
       }
     }
@@ -161,24 +179,24 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowA
     }
 #pragma unroll
     for (int s = 0; s < NV; ++s) {
-      float y[VEC];
-      if constexpr (FP8) {
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) y[i] = (h[s][i] * inv) * qmul;
-      } else {
-        float wf[VEC];
-        unpack<WD, VEC>(ww[s], wf);
+      for (int c = 0; c < SUB; ++c) {
+        float y[U];
+        if constexpr (FP8) {
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          if constexpr (BIAS) wf[i] += 1.0f;
-          y[i] = wf[i] * (h[s][i] * inv);
+          for (int i = 0; i < U; ++i) y[i] = (h[s][c][i] * inv) * qmul;
+        } else {
+          float wf[U];
+          unpack<WD, U>(ww[s][c], wf);
+#pragma unroll
+          for (int i = 0; i < U; ++i) {
+            if constexpr (BIAS) wf[i] += 1.0f;
+            y[i] = wf[i] * (h[s][c][i] * inv);
+          }
         }
-      }
-      uint32_t ow[OW];
-      pack<OD, VEC>(y, ow);
-      if (ok[s]) {
-        const int64_t e = row_elem + static_cast<int64_t>((s * nw + wave) * 64 + lane) * VEC;
-        store_words<OW * 4>(op + e * OB, ow);
+        uint32_t ow[OW];
+        pack<OD, U>(y, ow);
+        buffer_store_words<OW * 4>(orr, elem_of(s, c) * OB, ow);
       }
     }
     if constexpr (FP8) {

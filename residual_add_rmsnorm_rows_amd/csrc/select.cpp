@@ -8,9 +8,11 @@
 // decode variant with one warp per block when there are fewer warps than SMs;
 // this is the MI355X version of that idea, tuned by measurement):
 //   * vec = 16 bytes of x per lane (8 bf16 or 4 f32): global_load_dwordx4;
-//   * decode shape (rows <= compute units): one wave64 per row, no LDS and no
-//     barrier, as long as a lane holds at most 8 vectors; longer rows get the
-//     fewest waves that fit;
+//   * decode shape (rows <= compute units): the data is small and the call is
+//     latency bound, so a row is spread over as many waves as give each lane a
+//     single vector (up to 16 waves; longer rows take 2, 4 or 8 vectors per
+//     lane).  Measured on MI355X for 256 x 4096 bf16: 8 waves x 1 vector per
+//     lane take 2.7 us per call against 4.5 us for one wave x 8 vectors;
 //   * prefill shape: W waves share a row so that each lane holds
 //     `prefill_vecs_per_lane` vectors (2), with W in 1..16; the variant with
 //     the fewest idle lanes wins among equal choices;
@@ -130,10 +132,15 @@ rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int
   const int64_t nvec = hidden / vec;
   int waves = 0, nv = 0;
   if (rows <= num_cus) {
-    // decode: the fewest waves per row that hold the row in registers
-    for (int w = 1; w <= kMaxWavesPerRow && !nv; ++w) {
-      const int f = fit_nv(w, nvec);
-      if (f) { waves = w; nv = f; }
+    // decode: the fewest vectors per lane, then the fewest waves giving that
+    const int choices[4] = {1, 2, 4, 8};
+    for (int f : choices) {
+      const int64_t w = (nvec + 64 * f - 1) / (64 * f);
+      if (rows_variant_ok(static_cast<int>(w < 1 ? 1 : w), f, nvec)) {
+        waves = static_cast<int>(w < 1 ? 1 : w);
+        nv = f;
+        break;
+      }
     }
   } else {
     // prefill: about kPrefillVecsPerLane vectors per lane; among the waves

@@ -136,9 +136,10 @@ def test_selector_covers_every_row(x):
 
 
 def test_selector_shapes_of_the_workloads():
-    # decode: one wave per row while a lane holds the row (no LDS, no barrier)
-    assert _cfg(8, 1024)["waves_per_row"] == 1
-    assert _cfg(256, 4096)["waves_per_row"] == 1
+    # decode: latency bound, one vector per lane spread over as many waves as needed
+    c1, c2 = _cfg(8, 1024), _cfg(256, 4096)
+    assert (c1["waves_per_row"], c1["vecs_per_lane"]) == (2, 1)
+    assert (c2["waves_per_row"], c2["vecs_per_lane"]) == (8, 1)
     # prefill: no idle lanes for 8192 and 7168
     c3 = _cfg(16384, 8192)
     assert 64 * c3["waves_per_row"] * c3["vecs_per_lane"] * 8 == 8192
