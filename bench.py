@@ -315,8 +315,8 @@ def main() -> int:
     wl = WL.WORKLOADS[MAIN]
     log(f"generating {MAIN}")
     call = RowCall(wl, WL.generate_rownorm(wl, seed=0))
-    cfg = R.query_config(wl.rows, wl.hidden, x_dtype=wl.x_dtype, w_dtype=wl.w_dtype, out_dtype=wl.out_dtype,
-                         weight_plus_one=wl.weight_plus_one, num_cus=0)
+    cfg = R.query_config(wl.rows, wl.hidden, x_dtype=wl.x_dtype, res_dtype=wl.res_dtype, w_dtype=wl.w_dtype,
+                         out_dtype=wl.out_dtype, weight_plus_one=wl.weight_plus_one, num_cus=0)
     log(f"timing {MAIN}: warmup {args.warmup}, steps {args.steps}, config {cfg}")
     stream = torch.cuda.current_stream().cuda_stream
     for _ in range(args.warmup):
@@ -340,7 +340,8 @@ def main() -> int:
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{MAIN}: {wl.description}", "rows": wl.rows, "hidden": wl.hidden,
                    "x": wl.x_dtype, "residual": wl.res_dtype, "weight": wl.w_dtype, "out": wl.out_dtype,
-                   "eps": wl.eps, "launch": cfg, "algorithmic_bytes_per_step": nbytes},
+                   "eps": wl.eps, "launch": cfg, "algorithmic_bytes_per_step": nbytes,
+                   "source_sha256": source_digest()},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic},
     }

@@ -170,10 +170,22 @@ rn_status qknorm_fwd(const void* q, const void* k, const void* q_weight, const v
                      int32_t num_k_heads, int32_t head_dim, int64_t q_token_stride,
                      int64_t k_token_stride, float eps, uint32_t flags, void* stream);
 
+/* As qknorm_fwd, with an explicit launch configuration (for tuning and for
+ * testing every variant): cfg->kernel must be RN_KERNEL_HEADS, rows_per_lane
+ * 1, 2 or 4, block_threads 64, 128 or 256; the grid is derived from those and
+ * cfg's other fields are ignored. */
+rn_status qknorm_fwd_config(const void* q, const void* k, const void* q_weight, const void* k_weight,
+                            void* q_out, void* k_out, int64_t tokens, int32_t num_q_heads,
+                            int32_t num_k_heads, int32_t head_dim, int64_t q_token_stride,
+                            int64_t k_token_stride, float eps, uint32_t flags,
+                            const rn_launch_config* cfg, void* stream);
+
 /* Host-only: the launch configuration rmsnorm_fwd would use for these sizes on
- * a device with num_cus compute units (num_cus <= 0: query the current device). */
-rn_status rmsnorm_query_config(int64_t rows, int64_t hidden, uint32_t flags, int32_t num_cus,
-                               rn_launch_config* cfg);
+ * a device with num_cus compute units (num_cus <= 0: query the current device);
+ * has_residual says whether the call passes a residual (its dtype bits are then
+ * read from flags). */
+rn_status rmsnorm_query_config(int64_t rows, int64_t hidden, uint32_t flags, int32_t has_residual,
+                               int32_t num_cus, rn_launch_config* cfg);
 
 /* Host-only: the launch configuration qknorm_fwd would use. */
 rn_status qknorm_query_config(int64_t tokens, int32_t num_q_heads, int32_t num_k_heads,

@@ -151,12 +151,14 @@ def _qk_flags(dtype: str, w_dtype: str, weight_plus_one: bool) -> int:
 
 def qk_norm(q: torch.Tensor, k: Optional[torch.Tensor], q_weight: torch.Tensor,
             k_weight: Optional[torch.Tensor], eps: float, *, weight_plus_one: bool = False,
-            inplace: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+            inplace: bool = True, config: Optional[LaunchConfig] = None
+            ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Per-head RMSNorm of ``q`` [T, nq, D] and ``k`` [T, nk, D] over D (64, 128 or 256).
 
     Views with a token stride (e.g. slices of a fused QKV buffer) are accepted.
     ``inplace=True`` (the page's form) overwrites q and k; otherwise new
-    tensors with the same layout are returned.
+    tensors with the same layout are returned.  ``config`` forces a launch
+    configuration (rows_per_lane, block_threads).
     """
     device = q.device
     if device.type != "cuda":
@@ -184,18 +186,25 @@ def qk_norm(q: torch.Tensor, k: Optional[torch.Tensor], q_weight: torch.Tensor,
         q_out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=device)
         k_out = None if k is None else torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=device)
     flags = _qk_flags(td, wd, weight_plus_one)
-    st = lib().qknorm_fwd(_p(q), _p(k), _p(q_weight), _p(k_weight if k is not None else None),
-                          _p(q_out), _p(k_out), T, nq, nk, D, qs, ks, eps, flags, _stream(device))
+    args = (_p(q), _p(k), _p(q_weight), _p(k_weight if k is not None else None), _p(q_out), _p(k_out),
+            T, nq, nk, D, qs, ks, eps, flags)
+    if config is not None:
+        st = lib().qknorm_fwd_config(*args, ctypes.byref(config), _stream(device))
+    else:
+        st = lib().qknorm_fwd(*args, _stream(device))
     check(st)
     return q_out, k_out
 
 
-def query_config(rows: int, hidden: int, *, x_dtype: str = "bf16", w_dtype: str = "bf16",
-                 out_dtype: str = "bf16", weight_plus_one: bool = False, num_cus: int = 256) -> dict:
-    """The launch configuration the selector picks (host only; no GPU needed)."""
+def query_config(rows: int, hidden: int, *, x_dtype: str = "bf16", res_dtype: Optional[str] = None,
+                 w_dtype: str = "bf16", out_dtype: str = "bf16", weight_plus_one: bool = False,
+                 num_cus: int = 256) -> dict:
+    """The launch configuration the selector picks (host only with an explicit
+    ``num_cus``; ``num_cus=0`` queries the current device)."""
     cfg = LaunchConfig()
-    flags = make_flags(x_dtype, None, w_dtype, out_dtype, weight_plus_one)
-    check(lib().rmsnorm_query_config(rows, hidden, flags, num_cus, ctypes.byref(cfg)))
+    flags = make_flags(x_dtype, res_dtype, w_dtype, out_dtype, weight_plus_one)
+    check(lib().rmsnorm_query_config(rows, hidden, flags, int(res_dtype is not None), num_cus,
+                                     ctypes.byref(cfg)))
     return cfg.as_dict()
 
 

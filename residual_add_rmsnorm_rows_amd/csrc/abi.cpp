@@ -109,6 +109,67 @@ rn_status rows_entry(const void* x, const void* residual, const void* weight, vo
   return launch(fn, cfg.grid, cfg.block_threads, &a, stream);
 }
 
+rn_status heads_entry(const void* q, const void* k, const void* q_weight, const void* k_weight,
+                      void* q_out, void* k_out, int64_t tokens, int32_t num_q_heads,
+                      int32_t num_k_heads, int32_t head_dim, int64_t q_token_stride,
+                      int64_t k_token_stride, float eps, uint32_t flags,
+                      const rn_launch_config* explicit_cfg, void* stream) {
+  clear_error();
+  HeadKey key;
+  rn_status st = check_head_shape(tokens, num_q_heads, num_k_heads, head_dim, flags, &key);
+  if (st != RN_OK) return st;
+  if (!(eps >= 0.0f) || eps == __builtin_inff()) return fail(RN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const int64_t qrow = (int64_t)num_q_heads * head_dim;
+  const int64_t krow = (int64_t)num_k_heads * head_dim;
+  if (q_token_stride == 0) q_token_stride = qrow;
+  if (k_token_stride == 0) k_token_stride = krow;
+  if (q_token_stride < qrow || q_token_stride < 0)
+    return fail(RN_ERR_INVALID_ARG, "q_token_stride (%lld) < num_q_heads * head_dim", (long long)q_token_stride);
+  if (num_k_heads > 0 && k_token_stride < krow)
+    return fail(RN_ERR_INVALID_ARG, "k_token_stride (%lld) < num_k_heads * head_dim", (long long)k_token_stride);
+  if (tokens == 0) return RN_OK;
+  if (q == nullptr || q_weight == nullptr || q_out == nullptr)
+    return fail(RN_ERR_INVALID_ARG, "q, q_weight and q_out must not be NULL");
+  const bool has_k = num_k_heads > 0;
+  if (has_k != (k != nullptr) || has_k != (k_weight != nullptr) || has_k != (k_out != nullptr))
+    return fail(RN_ERR_INVALID_ARG, "k, k_weight and k_out must be given iff num_k_heads > 0");
+  const void* ptrs16[] = {q, k, q_weight, k_weight, q_out, k_out};
+  for (const void* p : ptrs16)
+    if (p != nullptr && !aligned(p, 16)) return fail(RN_ERR_MISALIGNED, "tensor pointer %p is not 16-byte aligned", p);
+  const int eb = key.t == kBF16 ? 2 : 4;
+  if ((q_token_stride * eb) % 16 != 0 || (has_k && (k_token_stride * eb) % 16 != 0))
+    return fail(RN_ERR_MISALIGNED, "token strides must be multiples of 16 bytes");
+
+  rn_launch_config cfg;
+  if (explicit_cfg != nullptr) {
+    st = check_head_config(tokens, num_q_heads, num_k_heads, key, explicit_cfg, &cfg);
+  } else {
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != RN_OK) return st;
+    st = select_head_config(tokens, num_q_heads, num_k_heads, key, cus, &cfg);
+  }
+  if (st != RN_OK) return st;
+  key.rpl = cfg.rows_per_lane;
+  const void* fn = pick_head_kernel(key);
+  if (fn == nullptr) return fail(RN_ERR_UNSUPPORTED, "no qknorm kernel built for this combination");
+
+  HeadArgs a;
+  a.q = q;
+  a.k = k;
+  a.qw = q_weight;
+  a.kw = k_weight;
+  a.q_out = q_out;
+  a.k_out = k_out;
+  a.q_stride = q_token_stride;
+  a.k_stride = k_token_stride;
+  a.num_q_heads = num_q_heads;
+  a.num_heads = num_q_heads + num_k_heads;
+  a.total_rows = static_cast<int32_t>(tokens * (num_q_heads + num_k_heads));
+  a.eps = eps;
+  return launch(fn, cfg.grid, cfg.block_threads, &a, stream);
+}
+
 }  // namespace
 }  // namespace rn
 
@@ -146,65 +207,29 @@ rn_status qknorm_fwd(const void* q, const void* k, const void* q_weight, const v
                      void* q_out, void* k_out, int64_t tokens, int32_t num_q_heads,
                      int32_t num_k_heads, int32_t head_dim, int64_t q_token_stride,
                      int64_t k_token_stride, float eps, uint32_t flags, void* stream) {
-  clear_error();
-  HeadKey key;
-  rn_status st = check_head_shape(tokens, num_q_heads, num_k_heads, head_dim, flags, &key);
-  if (st != RN_OK) return st;
-  if (!(eps >= 0.0f) || eps == __builtin_inff()) return fail(RN_ERR_INVALID_ARG, "eps must be finite and >= 0");
-  const int64_t qrow = (int64_t)num_q_heads * head_dim;
-  const int64_t krow = (int64_t)num_k_heads * head_dim;
-  if (q_token_stride == 0) q_token_stride = qrow;
-  if (k_token_stride == 0) k_token_stride = krow;
-  if (q_token_stride < qrow || q_token_stride < 0)
-    return fail(RN_ERR_INVALID_ARG, "q_token_stride (%lld) < num_q_heads * head_dim", (long long)q_token_stride);
-  if (num_k_heads > 0 && k_token_stride < krow)
-    return fail(RN_ERR_INVALID_ARG, "k_token_stride (%lld) < num_k_heads * head_dim", (long long)k_token_stride);
-  if (tokens == 0) return RN_OK;
-  if (q == nullptr || q_weight == nullptr || q_out == nullptr)
-    return fail(RN_ERR_INVALID_ARG, "q, q_weight and q_out must not be NULL");
-  const bool has_k = num_k_heads > 0;
-  if (has_k != (k != nullptr) || has_k != (k_weight != nullptr) || has_k != (k_out != nullptr))
-    return fail(RN_ERR_INVALID_ARG, "k, k_weight and k_out must be given iff num_k_heads > 0");
-  const void* ptrs16[] = {q, k, q_weight, k_weight, q_out, k_out};
-  for (const void* p : ptrs16)
-    if (p != nullptr && !aligned(p, 16)) return fail(RN_ERR_MISALIGNED, "tensor pointer %p is not 16-byte aligned", p);
-  const int eb = key.t == kBF16 ? 2 : 4;
-  if ((q_token_stride * eb) % 16 != 0 || (has_k && (k_token_stride * eb) % 16 != 0))
-    return fail(RN_ERR_MISALIGNED, "token strides must be multiples of 16 bytes");
-
-  int cus = 0;
-  st = device_cus(&cus);
-  if (st != RN_OK) return st;
-  rn_launch_config cfg;
-  st = select_head_config(tokens, num_q_heads, num_k_heads, key, cus, &cfg);
-  if (st != RN_OK) return st;
-  key.rpl = cfg.rows_per_lane;
-  const void* fn = pick_head_kernel(key);
-  if (fn == nullptr) return fail(RN_ERR_UNSUPPORTED, "no qknorm kernel built for this combination");
-
-  HeadArgs a;
-  a.q = q;
-  a.k = k;
-  a.qw = q_weight;
-  a.kw = k_weight;
-  a.q_out = q_out;
-  a.k_out = k_out;
-  a.q_stride = q_token_stride;
-  a.k_stride = k_token_stride;
-  a.num_q_heads = num_q_heads;
-  a.num_heads = num_q_heads + num_k_heads;
-  a.total_rows = static_cast<int32_t>(tokens * (num_q_heads + num_k_heads));
-  a.eps = eps;
-  return launch(fn, cfg.grid, cfg.block_threads, &a, stream);
+  return heads_entry(q, k, q_weight, k_weight, q_out, k_out, tokens, num_q_heads, num_k_heads, head_dim,
+                     q_token_stride, k_token_stride, eps, flags, nullptr, stream);
 }
 
-rn_status rmsnorm_query_config(int64_t rows, int64_t hidden, uint32_t flags, int32_t num_cus,
-                               rn_launch_config* cfg) {
+rn_status qknorm_fwd_config(const void* q, const void* k, const void* q_weight, const void* k_weight,
+                            void* q_out, void* k_out, int64_t tokens, int32_t num_q_heads,
+                            int32_t num_k_heads, int32_t head_dim, int64_t q_token_stride,
+                            int64_t k_token_stride, float eps, uint32_t flags,
+                            const rn_launch_config* cfg, void* stream) {
+  if (cfg == nullptr) {
+    clear_error();
+    return fail(RN_ERR_INVALID_ARG, "launch config is NULL");
+  }
+  return heads_entry(q, k, q_weight, k_weight, q_out, k_out, tokens, num_q_heads, num_k_heads, head_dim,
+                     q_token_stride, k_token_stride, eps, flags, cfg, stream);
+}
+
+rn_status rmsnorm_query_config(int64_t rows, int64_t hidden, uint32_t flags, int32_t has_residual,
+                               int32_t num_cus, rn_launch_config* cfg) {
   clear_error();
   if (cfg == nullptr) return fail(RN_ERR_INVALID_ARG, "cfg is NULL");
   RowKey key;
-  // the configuration does not depend on the residual, so its dtype bits are ignored here
-  rn_status st = check_row_shape(rows, hidden, flags, false, &key);
+  rn_status st = check_row_shape(rows, hidden, flags, has_residual != 0, &key);
   if (st != RN_OK) return st;
   int cus = num_cus;
   if (cus <= 0) {

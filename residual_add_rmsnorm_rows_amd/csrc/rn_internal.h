@@ -88,6 +88,10 @@ rn_status check_head_shape(int64_t tokens, int32_t nq, int32_t nk, int32_t head_
                            uint32_t flags, HeadKey* key);
 rn_status select_head_config(int64_t tokens, int32_t nq, int32_t nk, const HeadKey& key,
                              int num_cus, rn_launch_config* cfg);
+// Checks an explicit per-head configuration (rows_per_lane, block_threads) and
+// derives the grid.
+rn_status check_head_config(int64_t tokens, int32_t nq, int32_t nk, const HeadKey& key,
+                            const rn_launch_config* in, rn_launch_config* out);
 
 constexpr int kMaxWavesPerRow = 16;
 constexpr int kMaxVecsPerLane = 8;

@@ -13,9 +13,13 @@
 //     single vector (up to 16 waves; longer rows take 2, 4 or 8 vectors per
 //     lane).  Measured on MI355X for 256 x 4096 bf16: 8 waves x 1 vector per
 //     lane take 2.7 us per call against 4.5 us for one wave x 8 vectors;
-//   * prefill shape: W waves share a row so that each lane holds
-//     `prefill_vecs_per_lane` vectors (2), with W in 1..16; the variant with
-//     the fewest idle lanes wins among equal choices;
+//   * prefill shape: for the dtype classes and hidden sizes that were
+//     measured on MI355X (2048..16384 wide rows), the fastest variant of an
+//     interleaved sweep is taken from a table (kTuned below); otherwise the
+//     exact fit with the fewest vectors per lane.  (With a residual and a
+//     16/32-bit output, one extra partly idle wave often measured 0.5-2%
+//     faster than the exact fit; with fp8 output or no residual the same
+//     extra wave measured up to 25% slower, so the exact fit is the default);
 //   * grid = rows (a workgroup per row; MI355X's dispatcher refills CUs as
 //     workgroups finish, so no persistent loop is needed).
 #include <math.h>
@@ -114,60 +118,78 @@ static bool rows_variant_ok(int waves, int nv, int64_t nvec) {
   return (int64_t)64 * waves * nv >= nvec;
 }
 
-// Smallest built vecs-per-lane that covers nvec with `waves` waves (0: none).
-static int fit_nv(int waves, int64_t nvec) {
-  const int choices[4] = {1, 2, 4, 8};
-  for (int nv : choices)
-    if (rows_variant_ok(waves, nv, nvec)) return nv;
-  return 0;
-}
-
-static const int kPrefillVecsPerLane = 2;
 static const int64_t kMaxGrid = 0x7FFFFFFF;
+
+// Fastest (waves, vectors per lane) measured on MI355X for prefill-sized row
+// counts (1.2 GB of traffic per call) with a bf16 weight: each entry won an
+// interleaved sweep of every variant covering at most twice the row, three
+// repetitions each.  Key: x dtype, residual dtype (kNone: no residual),
+// whether the output is fp8, hidden size.
+struct Tuned {
+  int x, res;
+  bool fp8;
+  int hidden;
+  int waves, nv;
+};
+static const Tuned kTuned[] = {
+    // bf16 x, f32 residual stream, bf16/f32 out
+    {kBF16, kF32, false, 2048, 6, 1},    {kBF16, kF32, false, 4096, 9, 1},
+    {kBF16, kF32, false, 5120, 11, 1},   {kBF16, kF32, false, 7168, 12, 2},
+    {kBF16, kF32, false, 8192, 6, 4},    {kBF16, kF32, false, 12288, 16, 2},
+    {kBF16, kF32, false, 16384, 16, 2},
+    // bf16 x, bf16 residual, bf16/f32 out
+    {kBF16, kBF16, false, 2048, 5, 1},   {kBF16, kBF16, false, 4096, 9, 1},
+    {kBF16, kBF16, false, 5120, 9, 2},   {kBF16, kBF16, false, 7168, 9, 2},
+    {kBF16, kBF16, false, 8192, 9, 2},   {kBF16, kBF16, false, 12288, 16, 2},
+    {kBF16, kBF16, false, 16384, 12, 4},
+    // bf16 x, bf16 residual, fp8 out
+    {kBF16, kBF16, true, 2048, 4, 1},    {kBF16, kBF16, true, 4096, 8, 1},
+    {kBF16, kBF16, true, 5120, 5, 2},    {kBF16, kBF16, true, 7168, 7, 2},
+    {kBF16, kBF16, true, 8192, 16, 1},   {kBF16, kBF16, true, 12288, 12, 2},
+    {kBF16, kBF16, true, 16384, 16, 2},
+    // bf16 x, f32 residual stream, fp8 out
+    {kBF16, kF32, true, 2048, 5, 1},     {kBF16, kF32, true, 4096, 9, 1},
+    {kBF16, kF32, true, 5120, 10, 1},    {kBF16, kF32, true, 7168, 16, 1},
+    {kBF16, kF32, true, 8192, 16, 1},    {kBF16, kF32, true, 12288, 16, 2},
+    {kBF16, kF32, true, 16384, 16, 2},
+    // bf16 x, no residual, bf16/f32 out
+    {kBF16, kNone, false, 2048, 4, 1},   {kBF16, kNone, false, 4096, 8, 1},
+    {kBF16, kNone, false, 5120, 6, 2},   {kBF16, kNone, false, 7168, 5, 4},
+    {kBF16, kNone, false, 8192, 8, 2},   {kBF16, kNone, false, 12288, 4, 8},
+    {kBF16, kNone, false, 16384, 8, 4},
+    // f32 x, f32 residual, f32/bf16 out
+    {kF32, kF32, false, 2048, 7, 2},     {kF32, kF32, false, 4096, 16, 1},
+    {kF32, kF32, false, 5120, 15, 2},    {kF32, kF32, false, 7168, 6, 8},
+    {kF32, kF32, false, 8192, 15, 4},    {kF32, kF32, false, 12288, 16, 4},
+    {kF32, kF32, false, 16384, 16, 4},
+};
 
 rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int num_cus,
                             rn_launch_config* cfg) {
   if (num_cus < 1) return fail(RN_ERR_INVALID_ARG, "num_cus must be >= 1");
   const int vec = 16 / (key.x == kBF16 ? 2 : 4);
   const int64_t nvec = hidden / vec;
+  const int choices[4] = {1, 2, 4, 8};
   int waves = 0, nv = 0;
-  if (rows <= num_cus) {
-    // decode: the fewest vectors per lane, then the fewest waves giving that
-    const int choices[4] = {1, 2, 4, 8};
-    for (int f : choices) {
-      const int64_t w = (nvec + 64 * f - 1) / (64 * f);
-      if (rows_variant_ok(static_cast<int>(w < 1 ? 1 : w), f, nvec)) {
-        waves = static_cast<int>(w < 1 ? 1 : w);
-        nv = f;
+  if (rows > num_cus) {
+    for (const Tuned& t : kTuned) {
+      if (t.x == key.x && t.res == key.res && t.fp8 == (key.out == kFP8) && t.hidden == hidden &&
+          rows_variant_ok(t.waves, t.nv, nvec)) {
+        waves = t.waves;
+        nv = t.nv;
         break;
       }
     }
-  } else {
-    // prefill: about kPrefillVecsPerLane vectors per lane; among the waves
-    // counts around that target, take the one with the fewest idle lanes.
-    int64_t target = (nvec + 64 * kPrefillVecsPerLane - 1) / (64 * kPrefillVecsPerLane);
-    if (target < 1) target = 1;
-    if (target > kMaxWavesPerRow) target = kMaxWavesPerRow;
-    int64_t best_idle = -1;
-    for (int w = 1; w <= kMaxWavesPerRow; ++w) {
-      if (w < target / 2 || w > 2 * target) continue;
-      const int f = fit_nv(w, nvec);
-      if (!f) continue;
-      const int64_t idle = (int64_t)64 * w * f - nvec;
-      // fewer idle lanes first, then closest to the target waves count
-      const int64_t dist = w > target ? w - target : target - w;
-      const int64_t score = idle * 64 + dist;
-      if (best_idle < 0 || score < best_idle) {
-        best_idle = score;
-        waves = w;
-        nv = f;
-      }
-    }
-    if (!nv) {
-      for (int w = 1; w <= kMaxWavesPerRow && !nv; ++w) {
-        const int f = fit_nv(w, nvec);
-        if (f) { waves = w; nv = f; }
-      }
+  }
+  // decode (rows <= CUs, latency bound) and untabulated prefill shapes: the
+  // fewest vectors per lane, then the fewest waves that cover the row
+  for (int f : choices) {
+    if (nv) break;
+    int64_t w = (nvec + 64 * f - 1) / (64 * f);
+    if (w < 1) w = 1;
+    if (w <= kMaxWavesPerRow && rows_variant_ok(static_cast<int>(w), f, nvec)) {
+      waves = static_cast<int>(w);
+      nv = f;
     }
   }
   if (!nv) return fail(RN_ERR_UNSUPPORTED, "no rows-kernel variant holds %lld lane vectors", (long long)nvec);
@@ -214,6 +236,23 @@ rn_status check_head_shape(int64_t tokens, int32_t nq, int32_t nk, int32_t head_
   return RN_OK;
 }
 
+static void fill_head_cfg(int64_t rows, int vec, int lanes, int rpl, int block,
+                          rn_launch_config* cfg) {
+  const int per_wave = 64 / lanes;
+  const int64_t waves = (rows + (int64_t)per_wave * rpl - 1) / ((int64_t)per_wave * rpl);
+  const int waves_per_block = block / 64;
+  memset(cfg, 0, sizeof(*cfg));
+  cfg->kernel = RN_KERNEL_HEADS;
+  cfg->vec = vec;
+  cfg->waves_per_row = 1;
+  cfg->vecs_per_lane = 1;
+  cfg->lanes_per_row = lanes;
+  cfg->rows_per_lane = rpl;
+  cfg->block_threads = block;
+  cfg->grid = (waves + waves_per_block - 1) / waves_per_block;
+  if (cfg->grid < 1) cfg->grid = 1;
+}
+
 rn_status select_head_config(int64_t tokens, int32_t nq, int32_t nk, const HeadKey& key,
                              int num_cus, rn_launch_config* cfg) {
   if (num_cus < 1) return fail(RN_ERR_INVALID_ARG, "num_cus must be >= 1");
@@ -227,17 +266,21 @@ rn_status select_head_config(int64_t tokens, int32_t nq, int32_t nk, const HeadK
   int rpl = 2;
   const int64_t waves2 = (rows + per_wave * 2 - 1) / (per_wave * 2);
   if (waves2 < (int64_t)num_cus * waves_per_block * 2) rpl = 1;
-  const int64_t waves = (rows + (int64_t)per_wave * rpl - 1) / ((int64_t)per_wave * rpl);
-  memset(cfg, 0, sizeof(*cfg));
-  cfg->kernel = RN_KERNEL_HEADS;
-  cfg->vec = vec;
-  cfg->waves_per_row = 1;
-  cfg->vecs_per_lane = 1;
-  cfg->lanes_per_row = lanes;
-  cfg->rows_per_lane = rpl;
-  cfg->block_threads = kHeadBlockThreads;
-  cfg->grid = (waves + waves_per_block - 1) / waves_per_block;
-  if (cfg->grid < 1) cfg->grid = 1;
+  fill_head_cfg(rows, vec, lanes, rpl, kHeadBlockThreads, cfg);
+  return RN_OK;
+}
+
+rn_status check_head_config(int64_t tokens, int32_t nq, int32_t nk, const HeadKey& key,
+                            const rn_launch_config* in, rn_launch_config* out) {
+  if (in == nullptr) return fail(RN_ERR_INVALID_ARG, "launch config is NULL");
+  if (in->kernel != RN_KERNEL_HEADS) return fail(RN_ERR_INVALID_ARG, "config kernel must be RN_KERNEL_HEADS");
+  if (in->rows_per_lane != 1 && in->rows_per_lane != 2 && in->rows_per_lane != 4)
+    return fail(RN_ERR_INVALID_ARG, "config rows_per_lane must be 1, 2 or 4");
+  if (in->block_threads != 64 && in->block_threads != 128 && in->block_threads != 256)
+    return fail(RN_ERR_INVALID_ARG, "config block_threads must be 64, 128 or 256");
+  const int vec = 16 / (key.t == kBF16 ? 2 : 4);
+  const int64_t rows = tokens * ((int64_t)nq + nk);
+  fill_head_cfg(rows > 0 ? rows : 1, vec, key.head_dim / vec, in->rows_per_lane, in->block_threads, out);
   return RN_OK;
 }
 

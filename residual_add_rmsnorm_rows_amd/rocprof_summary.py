@@ -1,0 +1,138 @@
+"""Summarize rocprofv3 CSV output into short text files.
+
+Two summaries:
+
+``stats``   per-kernel dispatch counts and durations from a
+            ``--kernel-trace --stats`` run (``*_kernel_stats.csv``);
+``traffic`` HBM bytes per launch of one kernel from two ``--pmc`` runs
+            (``FETCH_SIZE``, then ``WRITE_SIZE``; ``*_counter_collection.csv``).
+            Each counter is scaled by what it reads for a plain device copy of
+            known size in the same run (the benchmark's ``--copy-calibration``:
+            three 1 GiB copies by the HIP runtime's copy kernel), so the result
+            is in bytes whatever unit or subset of channels the counter covers.
+
+Usage:
+  python -m residual_add_rmsnorm_rows_amd.rocprof_summary stats CSV --command CMD --out FILE
+  python -m residual_add_rmsnorm_rows_amd.rocprof_summary traffic --fetch CSV --write CSV \\
+      --kernel SUBSTR --bench-out FILE --command CMD --out FILE
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import json
+import statistics
+import sys
+from typing import Dict, List
+
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 1 << 30
+
+
+def _rows(path: str) -> List[Dict[str, str]]:
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def stats(csv_path: str, command: str, notes=()) -> str:
+    rows = _rows(csv_path)
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [
+        "# rocprofv3 --kernel-trace --stats summary",
+        f"# command: {command}",
+        *[f"# {n}" for n in notes],
+        "# columns: calls  avg_us  min_us  max_us  total_ms  kernel",
+    ]
+    for r in rows:
+        lines.append(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.3f} {float(r['MinNs']) / 1e3:10.3f} "
+                     f"{float(r['MaxNs']) / 1e3:10.3f} {float(r['TotalDurationNs']) / 1e6:10.3f}  {r['Name']}")
+    return "\n".join(lines) + "\n"
+
+
+def _counter(rows, counter: str, match) -> List[float]:
+    return [float(r["Counter_Value"]) for r in rows if r["Counter_Name"] == counter and match(r)]
+
+
+def _copy_rows(rows):
+    copies = [r for r in rows if r["Kernel_Name"] == COPY_KERNEL]
+    if not copies:
+        raise SystemExit("no copy-calibration dispatches in the counter file")
+    big = max(int(r["Grid_Size"]) for r in copies)
+    return lambda r: r["Kernel_Name"] == COPY_KERNEL and int(r["Grid_Size"]) == big
+
+
+def _last_json(path: str) -> dict:
+    with open(path) as f:
+        lines = [l for l in f if l.startswith("{")]
+    if not lines:
+        raise SystemExit(f"no JSON line in {path}")
+    return json.loads(lines[-1])
+
+
+def traffic(fetch_csv: str, write_csv: str, kernel: str, bench_out: str, command: str) -> str:
+    fr, wr = _rows(fetch_csv), _rows(write_csv)
+    names = sorted({r["Kernel_Name"] for r in fr + wr if kernel in r["Kernel_Name"]})
+    if len(names) != 1:
+        raise SystemExit(f"kernel substring {kernel!r} matches {names}")
+    main = lambda r: r["Kernel_Name"] == names[0]  # noqa: E731
+    fetch_k = _counter(fr, "FETCH_SIZE", main)
+    write_k = _counter(wr, "WRITE_SIZE", main)
+    cf = _counter(fr, "FETCH_SIZE", _copy_rows(fr))
+    cw = _counter(wr, "WRITE_SIZE", _copy_rows(wr))
+    fetch_factor = COPY_BYTES / (statistics.mean(cf) * 1024)
+    write_factor = COPY_BYTES / (statistics.mean(cw) * 1024)
+    fetch_b = statistics.mean(fetch_k) * 1024 * fetch_factor
+    write_b = statistics.mean(write_k) * 1024 * write_factor
+    bench = _last_json(bench_out)
+    alg = bench["config"]["algorithmic_bytes_per_step"]
+    lines = [
+        "# HBM traffic per launch from rocprofv3 counters (FETCH_SIZE and WRITE_SIZE runs),",
+        "# each scaled by the same counter's reading for a 1 GiB device copy in the same run.",
+        f"# command (FETCH_SIZE; the WRITE_SIZE run differs only in the counter): {command}",
+        f"kernel: {names[0]}",
+        f"workload: {bench['config']['workload']}",
+        f"source_sha256: {bench['config']['source_sha256']}",
+        f"dispatches_fetch: {len(fetch_k)}",
+        f"dispatches_write: {len(write_k)}",
+        f"fetch_size_kib_per_dispatch: {statistics.mean(fetch_k):.1f}",
+        f"write_size_kib_per_dispatch: {statistics.mean(write_k):.1f}",
+        f"copy_fetch_size_kib_per_GiB: {statistics.mean(cf):.1f}",
+        f"copy_write_size_kib_per_GiB: {statistics.mean(cw):.1f}",
+        f"fetch_scale: {fetch_factor:.4f}",
+        f"write_scale: {write_factor:.4f}",
+        f"fetch_bytes_per_launch: {fetch_b:.0f}",
+        f"write_bytes_per_launch: {write_b:.0f}",
+        f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
+        f"algorithmic_bytes_per_launch: {alg}",
+        f"traffic_over_algorithmic: {(fetch_b + write_b) / alg:.4f}",
+    ]
+    return "\n".join(lines) + "\n"
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--command", required=True)
+    s.add_argument("--out", required=True)
+    s.add_argument("--note", action="append", default=[])
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--bench-out", required=True)
+    t.add_argument("--command", required=True)
+    t.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    text = stats(a.csv, a.command, a.note) if a.what == "stats" else traffic(a.fetch, a.write, a.kernel, a.bench_out,
+                                                                        a.command)
+    with open(a.out, "w") as f:
+        f.write(text)
+    print(text)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

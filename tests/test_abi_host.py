@@ -117,6 +117,10 @@ def _cfg(rows, hidden, x="bf16", out="bf16", cus=256):
     return R.query_config(rows, hidden, x_dtype=x, out_dtype=out, num_cus=cus)
 
 
+def _cfg_res(rows, hidden, res, x="bf16", out="bf16", cus=256):
+    return R.query_config(rows, hidden, x_dtype=x, res_dtype=res, out_dtype=out, num_cus=cus)
+
+
 @pytest.mark.parametrize("x", ["bf16", "f32"])
 def test_selector_covers_every_row(x):
     vec = 8 if x == "bf16" else 4
@@ -140,11 +144,16 @@ def test_selector_shapes_of_the_workloads():
     c1, c2 = _cfg(8, 1024), _cfg(256, 4096)
     assert (c1["waves_per_row"], c1["vecs_per_lane"]) == (2, 1)
     assert (c2["waves_per_row"], c2["vecs_per_lane"]) == (8, 1)
-    # prefill: no idle lanes for 8192 and 7168
-    c3 = _cfg(16384, 8192)
-    assert 64 * c3["waves_per_row"] * c3["vecs_per_lane"] * 8 == 8192
-    c5 = _cfg(8192, 7168, out="fp8_e4m3fn")
-    assert 64 * c5["waves_per_row"] * c5["vecs_per_lane"] * 8 == 7168
+    # prefill: the measured table (bf16 x with an f32 or bf16 residual stream)
+    c3 = _cfg_res(16384, 8192, "f32")
+    assert (c3["waves_per_row"], c3["vecs_per_lane"]) == (6, 4)
+    c5 = _cfg_res(8192, 7168, "bf16", out="fp8_e4m3fn")
+    assert (c5["waves_per_row"], c5["vecs_per_lane"]) == (7, 2)
+    # outside the table: the exact fit with the fewest vectors per lane
+    c = _cfg_res(4096, 3072, "bf16")
+    assert (c["waves_per_row"], c["vecs_per_lane"]) == (6, 1)
+    c = _cfg_res(4096, 10240, "bf16")
+    assert (c["waves_per_row"], c["vecs_per_lane"]) == (10, 2)
 
 
 def test_head_mapping_covers_each_row_once():
@@ -171,10 +180,29 @@ def test_head_mapping_covers_each_row_once():
             assert (c["grid"] - 1) * (c["block_threads"] // 64) * gpw * rpl < total
 
 
+def test_explicit_qknorm_config_is_checked(lib):
+    cfg = L.LaunchConfig()
+
+    def call(rpl, block, kernel=L.RN_KERNEL_HEADS):
+        cfg.kernel, cfg.rows_per_lane, cfg.block_threads = kernel, rpl, block
+        return lib.qknorm_fwd_config(FAKE, None, FAKE, None, FAKE, None, 4, 2, 0, 128, 0, 0, 1e-6, 0,
+                                     ctypes.byref(cfg), None)
+
+    assert call(3, 256) == L.RN_ERR_INVALID_ARG
+    assert call(2, 512) == L.RN_ERR_INVALID_ARG
+    assert call(2, 256, kernel=L.RN_KERNEL_ROWS) == L.RN_ERR_INVALID_ARG
+    assert lib.qknorm_fwd_config(FAKE, None, FAKE, None, FAKE, None, 4, 2, 0, 128, 0, 0, 1e-6, 0, None,
+                                 None) == L.RN_ERR_INVALID_ARG
+
+
 def test_query_config_validates(lib):
     cfg = L.LaunchConfig()
-    assert lib.rmsnorm_query_config(10, 1001, 0, 256, ctypes.byref(cfg)) == L.RN_ERR_UNSUPPORTED
-    assert lib.rmsnorm_query_config(10, 1024, 0, 256, None) == L.RN_ERR_INVALID_ARG
+    assert lib.rmsnorm_query_config(10, 1001, 0, 1, 256, ctypes.byref(cfg)) == L.RN_ERR_UNSUPPORTED
+    assert lib.rmsnorm_query_config(10, 1024, 0, 1, 256, None) == L.RN_ERR_INVALID_ARG
+    # a bf16 residual with f32 x is not built: rejected only when a residual is present
+    f = L.make_flags("f32", "bf16", "f32", "f32", False)
+    assert lib.rmsnorm_query_config(10, 1024, f, 1, 256, ctypes.byref(cfg)) == L.RN_ERR_UNSUPPORTED
+    assert lib.rmsnorm_query_config(10, 1024, f, 0, 256, ctypes.byref(cfg)) == L.RN_OK
     assert lib.qknorm_query_config(10, 2, 0, 100, 0, 256, ctypes.byref(cfg)) == L.RN_ERR_UNSUPPORTED
 
 

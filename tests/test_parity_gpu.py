@@ -77,7 +77,7 @@ def test_workload_parity_full_size_sampled(name):
     """Full-size workload in the benchmark's launch configuration (the
     selector's); the oracle checks sampled rows, including the first and last."""
     wl = WL.WORKLOADS[name]
-    _announce(f"{name} full size rows={wl.rows} hidden={wl.hidden} cfg={R.query_config(wl.rows, wl.hidden, x_dtype=wl.x_dtype, out_dtype=wl.out_dtype)}")
+    _announce(f"{name} full size rows={wl.rows} hidden={wl.hidden} cfg={R.query_config(wl.rows, wl.hidden, x_dtype=wl.x_dtype, res_dtype=wl.res_dtype, out_dtype=wl.out_dtype)}")
     inputs = WL.generate_rownorm(wl, seed=0)
     r = run_rownorm(wl, inputs)
     rng = np.random.default_rng(123)
@@ -262,6 +262,32 @@ def test_qknorm_parity(dt, wdt, D, T, nq, nk, b, strided):
         assert rk["ok"], rk
     if strided:  # the V part of the fused buffer is untouched
         assert np.array_equal(to_host(qkv[:, (nq + nk) * D:]), before)
+
+
+@pytest.mark.parametrize("dt,D,T,nq,nk", [("bf16", 128, 77, 32, 8), ("bf16", 64, 50, 9, 3), ("bf16", 256, 21, 5, 2),
+                                          ("f32", 128, 33, 6, 2), ("f32", 256, 9, 3, 1)])
+def test_every_qknorm_launch_variant(dt, D, T, nq, nk):
+    """Every (heads per lane group, workgroup size) variant of the per-head kernel."""
+    qwl = WL.QKNormWorkload(name="qkv", tokens=T, num_q_heads=nq, num_k_heads=nk, head_dim=D, dtype=dt,
+                            w_dtype=dt, x_dist=WL.Dist(0, 1), w_dist=WL.Dist(1, 0.1), weight_plus_one=False,
+                            eps=1e-6)
+    inp = WL.generate_qknorm(qwl, seed=21)
+    q = to_dev(inp["q"].reshape(T, -1), dt).view(T, nq, D)
+    k = to_dev(inp["k"].reshape(T, -1), dt).view(T, nk, D)
+    qw, kw = to_dev(inp["q_weight"], dt), to_dev(inp["k_weight"], dt)
+    qy, ky = O.qknorm(O.decode(inp["q"], dt), O.decode(inp["k"], dt), O.decode(inp["q_weight"], dt),
+                      O.decode(inp["k_weight"], dt), qwl.eps, 0.0)
+    chk = C.check_bf16 if dt == "bf16" else C.check_f32
+    for rpl in (1, 2, 4):
+        for block in (64, 128, 256):
+            _announce(f"qknorm variant dt={dt} D={D} T={T} nq={nq} nk={nk} rpl={rpl} block={block}")
+            cfg = L.LaunchConfig()
+            cfg.kernel, cfg.rows_per_lane, cfg.block_threads = L.RN_KERNEL_HEADS, rpl, block
+            qo, ko = R.qk_norm(q, k, qw, kw, qwl.eps, inplace=False, config=cfg)
+            torch.cuda.synchronize()
+            rq = chk(to_host(qo).reshape(qy.shape), qy)
+            rk = chk(to_host(ko).reshape(ky.shape), ky)
+            assert rq["ok"] and rk["ok"], (rpl, block, rq, rk)
 
 
 def test_qknorm_equals_rmsnorm_on_reshaped_rows():
