@@ -15,9 +15,11 @@ The same line carries:
   * ``cpu_baseline``: the CPU oracle (numpy, float64) timed on a bounded
     sample of the same workload on this host;
   * ``secondary``: the other workloads -- decode calls (us/call against an
-    empty kernel launched the same way), per-head QK-norm and the fp8-output
-    prefill (GB/s, with rotating buffer sets larger than the 256 MB
-    Infinity Cache so that every call streams from HBM).
+    empty kernel launched the same way), per-head QK-norm, the fp8-output
+    prefill with per-row scales, and the same prefill with block-scaled
+    outputs (fp8 per-128 scales, MXFP8, MXFP4) (GB/s, with rotating buffer
+    sets larger than the 256 MB Infinity Cache so that every call streams
+    from HBM).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
 """
@@ -80,18 +82,19 @@ def read_traffic(workload: str):
         return None
 
 
-def rownorm_bytes(wl, rows=None) -> int:
-    """Algorithmic bytes: x, residual read once; out, residual_out written once; weight once; fp8 scale."""
-    import workloads as WL  # noqa: F401
+SCALE_BYTES = {"row": lambda h: 4, "group128": lambda h: 4 * (h // 128), "mx32": lambda h: h // 32}
 
+
+def rownorm_bytes(wl, rows=None, scale_scheme: str = "row") -> int:
+    """Algorithmic bytes: x, residual read once; out, residual_out written once; weight once; scales."""
     r = wl.rows if rows is None else rows
-    size = {"bf16": 2, "f32": 4, "fp8_e4m3fn": 1}
+    size = {"bf16": 2, "f32": 4, "fp8_e4m3fn": 1, "fp4_e2m1": 0.5}
     per_row = wl.hidden * (size[wl.x_dtype] + size[wl.out_dtype])
     if wl.res_dtype is not None:
         per_row += 2 * wl.hidden * size[wl.res_dtype]
-    if wl.out_dtype == "fp8_e4m3fn":
-        per_row += 4
-    return r * per_row + wl.hidden * size[wl.w_dtype]
+    if wl.out_dtype in ("fp8_e4m3fn", "fp4_e2m1"):
+        per_row += SCALE_BYTES[scale_scheme](wl.hidden)
+    return int(r * per_row + wl.hidden * size[wl.w_dtype])
 
 
 def qknorm_bytes(wl) -> int:
@@ -103,12 +106,15 @@ def qknorm_bytes(wl) -> int:
 class RowCall:
     """Device buffers of one fused add+RMSNorm workload and a raw C-ABI call over them."""
 
-    def __init__(self, wl, inputs, sets: int = 1):
+    def __init__(self, wl, inputs, sets: int = 1, scale_scheme: str = "row"):
         import torch
         from residual_add_rmsnorm_rows_amd import _lib as L
         from tests.gpu_util import TORCH_DTYPES, to_dev
 
         self.wl = wl
+        quant = wl.out_dtype in ("fp8_e4m3fn", "fp4_e2m1")
+        out_cols = wl.hidden // 2 if wl.out_dtype == "fp4_e2m1" else wl.hidden
+        scale_bytes = SCALE_BYTES[scale_scheme](wl.hidden)
         self.L = L.lib()
         x = to_dev(inputs["x"], wl.x_dtype)
         res = None if inputs["residual"] is None else to_dev(inputs["residual"], wl.res_dtype)
@@ -117,11 +123,12 @@ class RowCall:
         for i in range(sets):
             xs = x if i == 0 else x.clone()
             rs = None if res is None else (res if i == 0 else res.clone())
-            out = torch.empty(x.shape, dtype=TORCH_DTYPES[wl.out_dtype], device="cuda")
+            out = torch.empty((wl.rows, out_cols), dtype=TORCH_DTYPES[wl.out_dtype], device="cuda")
             ro = None if rs is None else torch.empty_like(rs)
-            sc = torch.empty(wl.rows, dtype=torch.float32, device="cuda") if wl.out_dtype == "fp8_e4m3fn" else None
+            sc = torch.empty((wl.rows, scale_bytes), dtype=torch.uint8, device="cuda") if quant else None
             self.sets.append((xs, rs, out, ro, sc))
-        self.flags = L.make_flags(wl.x_dtype, wl.res_dtype, wl.w_dtype, wl.out_dtype, wl.weight_plus_one)
+        self.flags = L.make_flags(wl.x_dtype, wl.res_dtype, wl.w_dtype, wl.out_dtype, wl.weight_plus_one,
+                                  scale_scheme)
         self.i = 0
 
     def __call__(self, stream: int) -> None:
@@ -203,14 +210,20 @@ def decode_metrics(name: str) -> dict:
     }
 
 
-def stream_metrics(name: str, steps: int, warmup: int, sets: int) -> dict:
+def stream_metrics(name: str, steps: int, warmup: int, sets: int, out_dtype=None,
+                   scale_scheme: str = "row") -> dict:
+    from dataclasses import replace
+
     import workloads as WL
 
     wl = WL.WORKLOADS[name]
-    call = RowCall(wl, WL.generate_rownorm(wl, seed=0), sets=sets)
+    if out_dtype is not None:
+        wl = replace(wl, out_dtype=out_dtype)
+    call = RowCall(wl, WL.generate_rownorm(wl, seed=0), sets=sets, scale_scheme=scale_scheme)
     ms = time_stream_loop(call, steps, warmup)
-    b = rownorm_bytes(wl)
-    return {"workload": wl.description, "us_per_call": round(ms * 1000, 3), "algorithmic_bytes": b,
+    b = rownorm_bytes(wl, scale_scheme=scale_scheme)
+    return {"workload": wl.description, "out": wl.out_dtype, "scale_scheme": scale_scheme,
+            "us_per_call": round(ms * 1000, 3), "algorithmic_bytes": b,
             "GBps": round(b / (ms * 1e-3) / 1e9, 1), "frac_of_peak": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "buffer_sets": sets}
 
@@ -366,6 +379,13 @@ def main() -> int:
         sec["qknorm_4096x32x128"] = qknorm_metrics(args.steps * 4, args.warmup)
         log("prefill_fp8_8192x7168")
         sec["prefill_fp8_8192x7168"] = stream_metrics("prefill_fp8_8192x7168", args.steps, args.warmup, sets=3)
+        log("block-scaled outputs on the 8192 x 7168 prefill")
+        sec["prefill_8192x7168_fp8_group128"] = stream_metrics("prefill_fp8_8192x7168", args.steps, args.warmup,
+                                                               sets=3, scale_scheme="group128")
+        sec["prefill_8192x7168_mxfp8"] = stream_metrics("prefill_fp8_8192x7168", args.steps, args.warmup, sets=3,
+                                                        scale_scheme="mx32")
+        sec["prefill_8192x7168_mxfp4"] = stream_metrics("prefill_fp8_8192x7168", args.steps, args.warmup, sets=3,
+                                                        out_dtype="fp4_e2m1", scale_scheme="mx32")
         result["secondary"] = sec
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

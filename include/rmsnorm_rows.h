@@ -70,10 +70,28 @@ typedef enum rn_status {
 /* Element types. */
 #define RN_DTYPE_BF16 0u       /* bfloat16 */
 #define RN_DTYPE_F32 1u        /* IEEE binary32 */
-#define RN_DTYPE_FP8_E4M3FN 2u /* OCP fp8 E4M3FN, outputs only, with a float32 scale per row */
+#define RN_DTYPE_FP8_E4M3FN 2u /* OCP fp8 E4M3FN, outputs only, with scales (see RN_SCALE_*) */
+#define RN_DTYPE_FP4_E2M1 3u   /* OCP MX fp4 E2M1, outputs only, two codes per byte (element 2k
+                                  in the low nibble), with MX scales */
+
+/* Scale granularity of a quantized output (flags bits 9-10), after the
+ * block-scaled schemes of the "Blackwell support" section (MXFP8, MXFP4, FP8
+ * block-wise scaling), with the formats of the OCP FP8 and MX specifications:
+ *   RN_SCALE_ROW       fp8: one float32 scale amax/448 per row, amax = max|y| of the row
+ *   RN_SCALE_GROUP128  fp8: one float32 scale amax/448 per 128 consecutive elements
+ *                      (hidden % 128 == 0); an all-zero group has scale 0
+ *   RN_SCALE_MX32      fp8 or fp4: one E8M0 byte per 32 consecutive elements (hidden % 32
+ *                      == 0) holding e + 127 with e = clamp(floor(log2 amax) - emax, -127,
+ *                      127), emax = 8 (fp8) or 2 (fp4); codes encode y * 2^-e with
+ *                      saturation; an all-zero block has e = -127
+ * Codes round to nearest, ties to even, and saturate at the format's largest value. */
+#define RN_SCALE_ROW 0u
+#define RN_SCALE_GROUP128 1u
+#define RN_SCALE_MX32 2u
 
 /* flags: bits 0-1 dtype of x, bits 2-3 dtype of residual and residual_out,
- * bits 4-5 dtype of weight, bits 6-7 dtype of out, bit 8 weight form (1 + w).
+ * bits 4-5 dtype of weight, bits 6-7 dtype of out, bit 8 weight form (1 + w),
+ * bits 9-10 scale granularity of a quantized out (RN_SCALE_*).
  * qknorm_fwd uses bits 0-1 for q/k (in and out), bits 4-5 for the weights and
  * bit 8; its other bits must be zero. */
 #define RN_FLAGS_X_SHIFT 0
@@ -81,7 +99,8 @@ typedef enum rn_status {
 #define RN_FLAGS_W_SHIFT 4
 #define RN_FLAGS_OUT_SHIFT 6
 #define RN_FLAG_WEIGHT_PLUS_ONE (1u << 8)
-#define RN_FLAGS_KNOWN_MASK 0x1FFu
+#define RN_FLAGS_SCALE_SHIFT 9
+#define RN_FLAGS_KNOWN_MASK 0x7FFu
 #define RN_MAKE_FLAGS(x_dt, res_dt, w_dt, out_dt, plus_one)                                   \
   (((uint32_t)(x_dt) << RN_FLAGS_X_SHIFT) | ((uint32_t)(res_dt) << RN_FLAGS_RES_SHIFT) |     \
    ((uint32_t)(w_dt) << RN_FLAGS_W_SHIFT) | ((uint32_t)(out_dt) << RN_FLAGS_OUT_SHIFT) |     \
@@ -110,15 +129,19 @@ typedef struct rn_launch_config {
  *   x            [rows, hidden] of dtype flags.x                       (read)
  *   residual     [rows, hidden] of dtype flags.res, or NULL for no residual add (read)
  *   weight       [hidden] of dtype flags.w                             (read)
- *   out          [rows, hidden] of dtype flags.out; for fp8, one byte per element (write)
+ *   out          [rows, hidden] of dtype flags.out: fp8 one byte per element, fp4 half a
+ *                byte (hidden / 2 bytes per row)                      (write)
  *   residual_out [rows, hidden] of dtype flags.res; must be NULL iff residual is NULL (write)
- *   out_scale    [rows] float32, fp8 output only (else must be NULL)   (write)
+ *   out_scale    quantized output only (else NULL): float32 [rows] (RN_SCALE_ROW),
+ *                float32 [rows, hidden/128] (RN_SCALE_GROUP128) or uint8 E8M0
+ *                [rows, hidden/32] (RN_SCALE_MX32)                     (write)
  *   rows         >= 0;  hidden >= 1, a multiple of the lane vector (8 for bf16 x,
  *                4 for f32 x) and at most 32768 (bf16 x) / 16384 (f32 x): the
  *                whole row is held in registers, 4096 lane vectors at most
  *   eps          finite, >= 0, used as given (a float32)
- *   flags        RN_MAKE_FLAGS(...); x is bf16 or f32; the residual dtype is the
- *                x dtype or f32; weight bf16 or f32; out bf16, f32 or fp8.
+ *   flags        RN_MAKE_FLAGS(...) | (scale << RN_FLAGS_SCALE_SHIFT); x is bf16 or f32;
+ *                the residual dtype is the x dtype or f32; weight bf16 or f32; out bf16,
+ *                f32, fp8 (any scale granularity) or fp4 (RN_SCALE_MX32 only).
  *
  * Residual reading (not on the pages): h = x + residual is rounded once to the
  * residual dtype, written to residual_out, and normalized; out == RMSNorm(h).
@@ -129,14 +152,14 @@ typedef struct rn_launch_config {
  * any other overlap is undefined, and out == residual_out is rejected.
  */
 rn_status rmsnorm_fwd(const void* x, const void* residual, const void* weight, void* out,
-                      void* residual_out, float* out_scale, int64_t rows, int64_t hidden, float eps,
+                      void* residual_out, void* out_scale, int64_t rows, int64_t hidden, float eps,
                       uint32_t flags, void* stream);
 
-/* As rmsnorm_fwd; for fp8 output, out_amax (may be NULL) also receives each
- * row's float32 amax, from which out_scale was computed.  out_amax must be NULL
- * for other outputs. */
+/* As rmsnorm_fwd; for a quantized output, out_amax (may be NULL) also receives
+ * the float32 amax from which each scale was computed (one per row, group or
+ * block, laid out like the scales).  out_amax must be NULL for other outputs. */
 rn_status rmsnorm_fwd_ex(const void* x, const void* residual, const void* weight, void* out,
-                         void* residual_out, float* out_scale, float* out_amax, int64_t rows,
+                         void* residual_out, void* out_scale, float* out_amax, int64_t rows,
                          int64_t hidden, float eps, uint32_t flags, void* stream);
 
 /* As rmsnorm_fwd_ex, with an explicit launch configuration instead of the
@@ -145,7 +168,7 @@ rn_status rmsnorm_fwd_ex(const void* x, const void* residual, const void* weight
  * 64 * waves_per_row * vecs_per_lane * vec >= hidden, 1 <= grid <= rows;
  * block_threads, lanes_per_row and rows_per_lane are derived and ignored. */
 rn_status rmsnorm_fwd_config(const void* x, const void* residual, const void* weight, void* out,
-                             void* residual_out, float* out_scale, float* out_amax, int64_t rows,
+                             void* residual_out, void* out_scale, float* out_amax, int64_t rows,
                              int64_t hidden, float eps, uint32_t flags,
                              const rn_launch_config* cfg, void* stream);
 

@@ -22,7 +22,7 @@ import numpy as np
 
 from .rownorm import BF16, bf16_decode
 
-__all__ = ["bf16_ulp", "check_bf16", "check_f32", "check_fp8_codes", "signed_index"]
+__all__ = ["bf16_ulp", "check_bf16", "check_f32", "check_fp8_codes", "check_fp4_codes", "signed_index"]
 
 
 def bf16_ulp(v: np.ndarray) -> np.ndarray:
@@ -66,6 +66,18 @@ def signed_index(codes: np.ndarray) -> np.ndarray:
 
 def check_fp8_codes(gpu: np.ndarray, ref: np.ndarray, max_steps: int = 1) -> Dict[str, float]:
     d = np.abs(signed_index(gpu) - signed_index(ref))
+    return {"ok": bool((d <= max_steps).all()), "max_steps": int(d.max(initial=0)),
+            "frac_exact": float((d == 0).mean()) if d.size else 1.0, "n_bad": int((d > max_steps).sum()),
+            "n": int(d.size)}
+
+
+def check_fp4_codes(gpu: np.ndarray, ref: np.ndarray, max_steps: int = 1) -> Dict[str, float]:
+    """4-bit E2M1 codes (unpacked, 0..15): steps on the signed magnitude index."""
+    def idx(c):
+        c = np.asarray(c, dtype=np.int64)
+        mag = c & 0x7
+        return np.where(c & 0x8, -mag, mag)
+    d = np.abs(idx(gpu) - idx(ref))
     return {"ok": bool((d <= max_steps).all()), "max_steps": int(d.max(initial=0)),
             "frac_exact": float((d == 0).mean()) if d.size else 1.0, "n_bad": int((d > max_steps).sum()),
             "n": int(d.size)}

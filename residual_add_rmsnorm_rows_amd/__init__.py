@@ -29,15 +29,17 @@ __all__ = [
     "lib",
 ]
 
-_NAMES = {torch.bfloat16: "bf16", torch.float32: "f32", torch.float8_e4m3fn: "fp8_e4m3fn"}
+_NAMES = {torch.bfloat16: "bf16", torch.float32: "f32", torch.float8_e4m3fn: "fp8_e4m3fn",
+          torch.float4_e2m1fn_x2: "fp4_e2m1"}
+_GROUP = {"row": None, "group128": 128, "mx32": 32}
 _TORCH = {v: k for k, v in _NAMES.items()}
 
 
 class NormOutput(NamedTuple):
     out: torch.Tensor
     residual_out: Optional[torch.Tensor]
-    scale: Optional[torch.Tensor]  # fp8 output: float32 [rows]
-    amax: Optional[torch.Tensor]   # fp8 output when requested: float32 [rows]
+    scale: Optional[torch.Tensor]  # quantized output: float32 [rows] / [rows, H/128], or E8M0 [rows, H/32]
+    amax: Optional[torch.Tensor]   # quantized output when requested: float32, one per scale
 
 
 def _name(dtype: torch.dtype, what: str) -> str:
@@ -67,14 +69,17 @@ def fused_add_rmsnorm(x: torch.Tensor, residual: Optional[torch.Tensor], weight:
                       eps: float, *, weight_plus_one: bool = False,
                       out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
                       residual_out: Optional[torch.Tensor] = None, return_amax: bool = False,
-                      config: Optional[LaunchConfig] = None) -> NormOutput:
+                      scale_scheme: str = "row", config: Optional[LaunchConfig] = None) -> NormOutput:
     """``residual_out = x + residual``; ``out = RMSNorm(residual_out) * (w [+ 1])``.
 
     ``x`` is [..., H] (bf16 or f32), ``residual`` the same shape (x dtype or
-    f32) or None, ``weight`` [H].  ``out_dtype`` is bf16, f32 or
-    ``torch.float8_e4m3fn`` (then ``scale`` holds one float32 per row and
-    ``out * scale`` dequantizes).  ``out=x`` and ``residual_out=residual``
-    are allowed (in place).  ``config`` forces a launch configuration.
+    f32) or None, ``weight`` [H].  ``out_dtype`` is bf16, f32,
+    ``torch.float8_e4m3fn`` or ``torch.float4_e2m1fn_x2`` (two codes per byte,
+    [..., H/2]).  Quantized outputs carry scales per ``scale_scheme``:
+    ``"row"`` (fp8; float32 [rows]), ``"group128"`` (fp8; float32
+    [rows, H/128]) or ``"mx32"`` (fp8 or fp4; E8M0 ``torch.float8_e8m0fnu``
+    [rows, H/32]).  ``out=x`` and ``residual_out=residual`` are allowed (in
+    place).  ``config`` forces a launch configuration.
     """
     device = x.device
     if device.type != "cuda":
@@ -95,12 +100,17 @@ def fused_add_rmsnorm(x: torch.Tensor, residual: Optional[torch.Tensor], weight:
     wd = _name(weight.dtype, "weight")
     od_t = out_dtype if out_dtype is not None else (out.dtype if out is not None else x.dtype)
     od = _name(od_t, "out")
+    out_shape = x.shape if od != "fp4_e2m1" else (*x.shape[:-1], H // 2)
+    if od == "fp4_e2m1" and H % 2:
+        raise ValueError("fp4 output needs an even hidden size")
     if out is None:
-        out = torch.empty(x.shape, dtype=od_t, device=device)
+        out = torch.empty(out_shape, dtype=od_t, device=device)
     else:
         _dev_tensor(out, "out", device)
-        if out.shape != x.shape or out.dtype != od_t:
+        if tuple(out.shape) != tuple(out_shape) or out.dtype != od_t:
             raise ValueError("out has the wrong shape or dtype")
+    if scale_scheme not in _GROUP:
+        raise ValueError(f"scale_scheme must be one of {sorted(_GROUP)}")
     if residual is not None:
         if residual_out is None:
             residual_out = torch.empty_like(residual)
@@ -111,11 +121,14 @@ def fused_add_rmsnorm(x: torch.Tensor, residual: Optional[torch.Tensor], weight:
     elif residual_out is not None:
         raise ValueError("residual_out given without residual")
     scale = amax = None
-    if od == "fp8_e4m3fn":
-        scale = torch.empty(rows, dtype=torch.float32, device=device)
+    if od in ("fp8_e4m3fn", "fp4_e2m1"):
+        g = _GROUP[scale_scheme]
+        nscale = (rows,) if g is None else (rows, H // g if H % g == 0 else 0)
+        sdt = torch.float8_e8m0fnu if scale_scheme == "mx32" else torch.float32
+        scale = torch.empty(nscale, dtype=sdt, device=device)
         if return_amax:
-            amax = torch.empty(rows, dtype=torch.float32, device=device)
-    flags = make_flags(xd, rd, wd, od, weight_plus_one)
+            amax = torch.empty(nscale, dtype=torch.float32, device=device)
+    flags = make_flags(xd, rd, wd, od, weight_plus_one, scale_scheme)
     L = lib()
     if config is not None:
         st = L.rmsnorm_fwd_config(_p(x), _p(residual), _p(weight), _p(out), _p(residual_out), _p(scale),
@@ -198,11 +211,11 @@ def qk_norm(q: torch.Tensor, k: Optional[torch.Tensor], q_weight: torch.Tensor,
 
 def query_config(rows: int, hidden: int, *, x_dtype: str = "bf16", res_dtype: Optional[str] = None,
                  w_dtype: str = "bf16", out_dtype: str = "bf16", weight_plus_one: bool = False,
-                 num_cus: int = 256) -> dict:
+                 scale_scheme: str = "row", num_cus: int = 256) -> dict:
     """The launch configuration the selector picks (host only with an explicit
     ``num_cus``; ``num_cus=0`` queries the current device)."""
     cfg = LaunchConfig()
-    flags = make_flags(x_dtype, res_dtype, w_dtype, out_dtype, weight_plus_one)
+    flags = make_flags(x_dtype, res_dtype, w_dtype, out_dtype, weight_plus_one, scale_scheme)
     check(lib().rmsnorm_query_config(rows, hidden, flags, int(res_dtype is not None), num_cus,
                                      ctypes.byref(cfg)))
     return cfg.as_dict()

@@ -24,16 +24,20 @@ RN_ERR_HIP = 4
 RN_DTYPE_BF16 = 0
 RN_DTYPE_F32 = 1
 RN_DTYPE_FP8_E4M3FN = 2
+RN_DTYPE_FP4_E2M1 = 3  # outputs only
 RN_FLAGS_X_SHIFT = 0
 RN_FLAGS_RES_SHIFT = 2
 RN_FLAGS_W_SHIFT = 4
 RN_FLAGS_OUT_SHIFT = 6
 RN_FLAG_WEIGHT_PLUS_ONE = 1 << 8
+RN_FLAGS_SCALE_SHIFT = 9
+SCALE_SCHEMES = {"row": 0, "group128": 1, "mx32": 2}
 
 RN_KERNEL_ROWS = 0
 RN_KERNEL_HEADS = 1
 
-DTYPE_CODES = {"bf16": RN_DTYPE_BF16, "f32": RN_DTYPE_F32, "fp8_e4m3fn": RN_DTYPE_FP8_E4M3FN}
+DTYPE_CODES = {"bf16": RN_DTYPE_BF16, "f32": RN_DTYPE_F32, "fp8_e4m3fn": RN_DTYPE_FP8_E4M3FN,
+               "fp4_e2m1": RN_DTYPE_FP4_E2M1}
 
 # Every symbol include/rmsnorm_rows.h declares.
 EXPORTED_SYMBOLS = (
@@ -44,8 +48,10 @@ EXPORTED_SYMBOLS = (
 ABI_VERSION = 1
 
 
-def make_flags(x: str, res: str | None, w: str, out: str, weight_plus_one: bool) -> int:
+def make_flags(x: str, res: str | None, w: str, out: str, weight_plus_one: bool,
+               scale_scheme: str = "row") -> int:
     f = DTYPE_CODES[x] << RN_FLAGS_X_SHIFT
+    f |= SCALE_SCHEMES[scale_scheme] << RN_FLAGS_SCALE_SHIFT
     f |= DTYPE_CODES[res or "bf16"] << RN_FLAGS_RES_SHIFT
     f |= DTYPE_CODES[w] << RN_FLAGS_W_SHIFT
     f |= DTYPE_CODES[out] << RN_FLAGS_OUT_SHIFT

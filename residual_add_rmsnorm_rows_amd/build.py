@@ -41,22 +41,21 @@ HOST_FLAGS = [
     "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include", f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
-ROW_VARIANTS = [  # (x dtype, out dtype, name)
-    ("kBF16", "kBF16", "bf16_bf16"),
-    ("kBF16", "kF32", "bf16_f32"),
-    ("kBF16", "kFP8", "bf16_fp8"),
-    ("kF32", "kBF16", "f32_bf16"),
-    ("kF32", "kF32", "f32_f32"),
-    ("kF32", "kFP8", "f32_fp8"),
+ROW_VARIANTS = [  # (x dtype, out dtype, scale scheme, name)
+    (x, out, qs, f"{xn}_{on}" + (f"_{qn}" if qn else ""))
+    for x, xn in (("kBF16", "bf16"), ("kF32", "f32"))
+    for out, on, qs, qn in (("kBF16", "bf16", "kQRow", ""), ("kF32", "f32", "kQRow", ""),
+                            ("kFP8", "fp8", "kQRow", "row"), ("kFP8", "fp8", "kQGroup128", "g128"),
+                            ("kFP8", "fp8", "kQMx32", "mx"), ("kFP4", "fp4", "kQMx32", "mx"))
 ]
 
 
 def _jobs():
     jobs = []
-    for x, out, name in ROW_VARIANTS:
+    for x, out, qs, name in ROW_VARIANTS:
         obj = os.path.join(BUILD_DIR, f"rows_{name}.o")
-        cmd = [HIPCC, *HIP_FLAGS, f"-DRN_TU_X={x}", f"-DRN_TU_OUT={out}", f"-DRN_TU_NAME={name}",
-               "-c", os.path.join(CSRC, "rows_kernel.hip"), "-o", obj]
+        cmd = [HIPCC, *HIP_FLAGS, f"-DRN_TU_X={x}", f"-DRN_TU_OUT={out}", f"-DRN_TU_QS={qs}",
+               f"-DRN_TU_NAME={name}", "-c", os.path.join(CSRC, "rows_kernel.hip"), "-o", obj]
         jobs.append((obj, cmd))
     for name in ("heads_kernel", "empty_kernel"):
         obj = os.path.join(BUILD_DIR, f"{name}.o")

@@ -38,8 +38,10 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 const void* pick_row_kernel(const RowKey& k) {
   const void* (*const pickers[])(const RowKey&) = {
-      pick_row_kernel_bf16_bf16, pick_row_kernel_bf16_f32, pick_row_kernel_bf16_fp8,
-      pick_row_kernel_f32_bf16,  pick_row_kernel_f32_f32,  pick_row_kernel_f32_fp8};
+      pick_row_kernel_bf16_bf16,    pick_row_kernel_bf16_f32,     pick_row_kernel_bf16_fp8_row,
+      pick_row_kernel_bf16_fp8_g128, pick_row_kernel_bf16_fp8_mx, pick_row_kernel_bf16_fp4_mx,
+      pick_row_kernel_f32_bf16,     pick_row_kernel_f32_f32,      pick_row_kernel_f32_fp8_row,
+      pick_row_kernel_f32_fp8_g128, pick_row_kernel_f32_fp8_mx,   pick_row_kernel_f32_fp4_mx};
   for (auto p : pickers) {
     const void* f = p(k);
     if (f) return f;
@@ -56,7 +58,7 @@ rn_status launch(const void* fn, int64_t grid, int block, void* args, void* stre
 }
 
 rn_status rows_entry(const void* x, const void* residual, const void* weight, void* out,
-                     void* residual_out, float* out_scale, float* out_amax, int64_t rows,
+                     void* residual_out, void* out_scale, float* out_amax, int64_t rows,
                      int64_t hidden, float eps, uint32_t flags, const rn_launch_config* explicit_cfg,
                      void* stream) {
   clear_error();
@@ -64,22 +66,22 @@ rn_status rows_entry(const void* x, const void* residual, const void* weight, vo
   rn_status st = check_row_shape(rows, hidden, flags, residual != nullptr, &key);
   if (st != RN_OK) return st;
   if (!(eps >= 0.0f) || eps == __builtin_inff()) return fail(RN_ERR_INVALID_ARG, "eps must be finite and >= 0");
-  const bool fp8 = key.out == kFP8;
-  if (!fp8 && (out_scale != nullptr || out_amax != nullptr))
-    return fail(RN_ERR_INVALID_ARG, "out_scale / out_amax are only for fp8 output");
+  const bool quant = key.out == kFP8 || key.out == kFP4;
+  if (!quant && (out_scale != nullptr || out_amax != nullptr))
+    return fail(RN_ERR_INVALID_ARG, "out_scale / out_amax are only for fp8 / fp4 output");
   if (rows == 0) return RN_OK;
   if (x == nullptr || weight == nullptr || out == nullptr)
     return fail(RN_ERR_INVALID_ARG, "x, weight and out must not be NULL");
   if ((residual == nullptr) != (residual_out == nullptr))
     return fail(RN_ERR_INVALID_ARG, "residual and residual_out must both be given or both be NULL");
-  if (fp8 && out_scale == nullptr) return fail(RN_ERR_INVALID_ARG, "fp8 output needs out_scale");
+  if (quant && out_scale == nullptr) return fail(RN_ERR_INVALID_ARG, "quantized output needs out_scale");
   if (residual_out != nullptr && residual_out == out)
     return fail(RN_ERR_INVALID_ARG, "out and residual_out must be different buffers");
   const void* ptrs16[] = {x, residual, weight, out, residual_out};
   for (const void* p : ptrs16)
     if (p != nullptr && !aligned(p, 16)) return fail(RN_ERR_MISALIGNED, "tensor pointer %p is not 16-byte aligned", p);
-  if ((out_scale && !aligned(out_scale, 4)) || (out_amax && !aligned(out_amax, 4)))
-    return fail(RN_ERR_MISALIGNED, "out_scale / out_amax must be 4-byte aligned");
+  if ((out_scale && key.qs != kQMx32 && !aligned(out_scale, 4)) || (out_amax && !aligned(out_amax, 4)))
+    return fail(RN_ERR_MISALIGNED, "float32 scales / out_amax must be 4-byte aligned");
 
   rn_launch_config cfg;
   if (explicit_cfg != nullptr) {
@@ -178,21 +180,21 @@ using namespace rn;
 extern "C" {
 
 rn_status rmsnorm_fwd(const void* x, const void* residual, const void* weight, void* out,
-                      void* residual_out, float* out_scale, int64_t rows, int64_t hidden, float eps,
+                      void* residual_out, void* out_scale, int64_t rows, int64_t hidden, float eps,
                       uint32_t flags, void* stream) {
   return rows_entry(x, residual, weight, out, residual_out, out_scale, nullptr, rows, hidden, eps,
                     flags, nullptr, stream);
 }
 
 rn_status rmsnorm_fwd_ex(const void* x, const void* residual, const void* weight, void* out,
-                         void* residual_out, float* out_scale, float* out_amax, int64_t rows,
+                         void* residual_out, void* out_scale, float* out_amax, int64_t rows,
                          int64_t hidden, float eps, uint32_t flags, void* stream) {
   return rows_entry(x, residual, weight, out, residual_out, out_scale, out_amax, rows, hidden, eps,
                     flags, nullptr, stream);
 }
 
 rn_status rmsnorm_fwd_config(const void* x, const void* residual, const void* weight, void* out,
-                             void* residual_out, float* out_scale, float* out_amax, int64_t rows,
+                             void* residual_out, void* out_scale, float* out_amax, int64_t rows,
                              int64_t hidden, float eps, uint32_t flags,
                              const rn_launch_config* cfg, void* stream) {
   if (cfg == nullptr) {

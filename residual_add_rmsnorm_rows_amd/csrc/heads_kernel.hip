@@ -13,7 +13,9 @@
 // 64 / G * RPL consecutive rows [first, first + 64 / G * RPL), so each load
 // instruction reads 64 consecutive vectors when the heads are contiguous.
 // Rows past the end are masked (the page's kernel needs an exact grid).
-// Weights: every lane loads its slice of the Q and K weights once.
+// Weights: every lane loads its slice of the Q and K weights once.  Heads are
+// loaded without the nontemporal hint: on MI355X this kernel measured 6.07
+// TB/s with plain loads and 5.25 TB/s with the hint (4096 x 32 x 128 bf16).
 
 #include "device_common.h"
 

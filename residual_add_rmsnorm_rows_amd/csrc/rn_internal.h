@@ -9,9 +9,16 @@
 
 namespace rn {
 
-enum DType : int { kBF16 = 0, kF32 = 1, kFP8 = 2, kNone = 3 };
+// kFP4 is OCP fp4 e2m1 (outputs only, two codes per byte); kNone marks an
+// absent residual.
+enum DType : int { kBF16 = 0, kF32 = 1, kFP8 = 2, kNone = 3, kFP4 = 4 };
 
-inline int dtype_bytes(int dt) { return dt == kBF16 ? 2 : dt == kF32 ? 4 : dt == kFP8 ? 1 : 0; }
+// Scale granularity of a quantized (fp8 / fp4) output.
+enum QScheme : int {
+  kQRow = 0,       // one float32 scale amax / 448 per row (fp8)
+  kQGroup128 = 1,  // one float32 scale amax / 448 per 128 consecutive elements (fp8)
+  kQMx32 = 2,      // OCP MX: one E8M0 scale per 32 consecutive elements (fp8 e4m3 or fp4 e2m1)
+};
 
 // Kernel arguments of the rows kernel, passed by value as the only argument.
 struct RowArgs {
@@ -20,8 +27,8 @@ struct RowArgs {
   const void* w;
   void* out;
   void* res_out;         // nullptr iff res is nullptr
-  float* scale;          // fp8 output only
-  float* amax;           // fp8 output only, may be nullptr
+  void* scale;           // quantized output only: float32 per row / per group, or E8M0 per block
+  float* amax;           // quantized output only, may be nullptr: float32 amax per scale
   int64_t rows;
   int32_t hidden;        // elements per row
   float eps;
@@ -46,6 +53,7 @@ struct HeadArgs {
 // Everything the launcher needs to pick a compiled kernel.
 struct RowKey {
   int x, res, w, out;  // res == kNone: no residual
+  int qs;              // QScheme (kQRow unless the output is quantized)
   int bias;            // 0 or 1
   int nv;              // vectors per lane: 1, 2, 4, 8
 };
@@ -108,13 +116,19 @@ constexpr int max_threads_for_nv(int nv) { return nv >= 8 ? 512 : 1024; }
 // Each returns the address of the compiled kernel for `key`, or nullptr when
 // that combination is not built.
 namespace rn {
-// rows_kernel.hip, compiled once per (x dtype, out dtype) pair
+// rows_kernel.hip, compiled once per (x dtype, out dtype, scale scheme)
 const void* pick_row_kernel_bf16_bf16(const RowKey& key);
 const void* pick_row_kernel_bf16_f32(const RowKey& key);
-const void* pick_row_kernel_bf16_fp8(const RowKey& key);
+const void* pick_row_kernel_bf16_fp8_row(const RowKey& key);
+const void* pick_row_kernel_bf16_fp8_g128(const RowKey& key);
+const void* pick_row_kernel_bf16_fp8_mx(const RowKey& key);
+const void* pick_row_kernel_bf16_fp4_mx(const RowKey& key);
 const void* pick_row_kernel_f32_bf16(const RowKey& key);
 const void* pick_row_kernel_f32_f32(const RowKey& key);
-const void* pick_row_kernel_f32_fp8(const RowKey& key);
+const void* pick_row_kernel_f32_fp8_row(const RowKey& key);
+const void* pick_row_kernel_f32_fp8_g128(const RowKey& key);
+const void* pick_row_kernel_f32_fp8_mx(const RowKey& key);
+const void* pick_row_kernel_f32_fp4_mx(const RowKey& key);
 // heads_kernel.hip
 const void* pick_head_kernel(const HeadKey& key);
 // empty_kernel.hip

@@ -31,8 +31,17 @@
 // of a workgroup, so the next row's writes cannot race the current reads).
 // With W == 1 there is no LDS traffic and no barrier (the decode shape).
 //
-// This file is compiled once per (x dtype, out dtype) pair, selected by
-// RN_TU_X / RN_TU_OUT / RN_TU_NAME, so the variants build in parallel.
+// Quantized outputs (fp8 e4m3fn, fp4 e2m1) carry scales at one of three
+// granularities ("Blackwell support" names MXFP8/MXFP4 and FP8 block-wise
+// scaling; the formats follow the OCP FP8 and MX specifications):
+//   per row      scale = amax / 448, codes = e4m3fn(y * 448 / amax);
+//   per 128      the same per group of 128 consecutive elements;
+//   MX per 32    E8M0 scale 2^e with e = floor(log2 amax) - emax (8 for e4m3,
+//                2 for e2m1), codes = encode(y * 2^-e), saturating.
+//
+// This file is compiled once per (x dtype, out dtype, scale scheme), selected
+// by RN_TU_X / RN_TU_OUT / RN_TU_QS / RN_TU_NAME, so the variants build in
+// parallel.
 
 #include "device_common.h"
 
@@ -43,33 +52,46 @@
 #error "RN_TU_OUT (out dtype) must be defined"
 #endif
 
+#ifndef RN_TU_QS
+#define RN_TU_QS kQRow
+#endif
+
 #define RN_CAT2(a, b) a##b
 #define RN_CAT(a, b) RN_CAT2(a, b)
 
 namespace rn {
 namespace {
 
-constexpr int storage_bytes(int dt) { return dt == kBF16 ? 2 : dt == kFP8 ? 1 : 4; }
+constexpr int storage_bits(int dt) {
+  return dt == kBF16 ? 16 : dt == kF32 ? 32 : dt == kFP8 ? 8 : dt == kFP4 ? 4 : 32;
+}
 
 constexpr int max_of(int a, int b) { return a > b ? a : b; }
 
-template <int XD, int RD, int WD, int OD, int BIAS, int NV>
+template <int XD, int RD, int WD, int OD, int QS, int BIAS, int NV>
 __global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowArgs a) {
-  constexpr int XB = storage_bytes(XD);
+  constexpr int XB = storage_bits(XD) / 8;
   constexpr int VEC = 16 / XB;
   constexpr bool HAS_RES = RD != kNone;
-  constexpr bool FP8 = OD == kFP8;
-  constexpr int RB = storage_bytes(RD);
-  constexpr int WB = storage_bytes(WD);
-  constexpr int OB = storage_bytes(OD);
-  constexpr int WIDEST = max_of(max_of(XB, HAS_RES ? RB : 1), max_of(WB, OB));
-  constexpr int SUB = WIDEST / XB;        // chunks per step (1 or 2)
-  constexpr int U = VEC / SUB;            // elements per chunk
-  constexpr int XW = U * XB / 4;          // dwords of x per chunk
-  constexpr int RW = U * RB / 4;          // dwords of residual per chunk
-  constexpr int WW = U * WB / 4;          // dwords of weight per chunk
-  constexpr int OW = (U * OB + 3) / 4;    // dwords of output per chunk
+  constexpr bool QUANT = OD == kFP8 || OD == kFP4;
+  constexpr int RB = storage_bits(RD) / 8;
+  constexpr int WB = storage_bits(WD) / 8;
+  constexpr int OBITS = storage_bits(OD);
+  constexpr int WIDEST = max_of(max_of(XB, HAS_RES ? RB : 1), max_of(WB, max_of(OBITS / 8, 1)));
+  constexpr int SUB = WIDEST / XB;          // chunks per step (1 or 2)
+  constexpr int U = VEC / SUB;              // elements per chunk
+  constexpr int XW = U * XB / 4;            // dwords of x per chunk
+  constexpr int RW = U * RB / 4;            // dwords of residual per chunk
+  constexpr int WW = U * WB / 4;            // dwords of weight per chunk
+  constexpr int OCB = U * OBITS / 8;        // output bytes per chunk
+  constexpr int OW = words_for<OD, U>();    // dwords holding one output chunk
+  constexpr int QG = QS == kQGroup128 ? 128 : QS == kQMx32 ? 32 : 0;  // elements per scale
+  constexpr int GL = QG ? QG / U : 1;       // lanes per scale group
+  constexpr int EMAX = OD == kFP8 ? 8 : 2;  // MX: exponent of the element format's top binade
   static_assert(SUB == 1 || SUB == 2, "chunking");
+  static_assert(!QUANT || QS == kQRow || (QG % U == 0 && (64 * U) % QG == 0), "scale groups");
+  static_assert(QS == kQRow || QUANT, "scale groups only for quantized outputs");
+  static_assert(OD != kFP4 || QS == kQMx32, "fp4 output is MX-scaled");
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -82,10 +104,12 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowA
   char* __restrict__ op = static_cast<char*>(a.out);
   char* __restrict__ rop = static_cast<char*>(a.res_out);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, static_cast<uint32_t>(a.hidden) * WB);
+  const uint32_t groups = QG ? static_cast<uint32_t>(a.hidden) / QG : 1;  // scales per row
+  constexpr int SCALE_BYTES = QS == kQMx32 ? 1 : 4;
 
-  // Byte offset (in units of one element) of chunk (s, c) of this lane from
-  // the row start: (((s * W + wave) * SUB + c) * 64 + lane) * U.  Chunks past
-  // the row end fall outside the row's buffer resource.
+  // Element offset of chunk (s, c) of this lane from the row start:
+  // (((s * W + wave) * SUB + c) * 64 + lane) * U.  Chunks past the row end
+  // fall outside the row's buffer resources.
   auto elem_of = [&](int s, int c) -> uint32_t {
     return static_cast<uint32_t>((((s * nw + wave) * SUB + c) * 64 + lane) * U);
   };
@@ -94,7 +118,8 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowA
     const int64_t row_elem = row * a.hidden;
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(xp + row_elem * XB, static_cast<uint32_t>(a.hidden) * XB);
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(rp + row_elem * RB, static_cast<uint32_t>(a.hidden) * RB);
-    const __amdgpu_buffer_rsrc_t orr = make_rsrc(op + row_elem * OB, static_cast<uint32_t>(a.hidden) * OB);
+    const __amdgpu_buffer_rsrc_t orr =
+        make_rsrc(op + row_elem * OBITS / 8, static_cast<uint32_t>(a.hidden) * OBITS / 8);
     const __amdgpu_buffer_rsrc_t ror = make_rsrc(rop + row_elem * RB, static_cast<uint32_t>(a.hidden) * RB);
 
     // 1. Issue every load of this lane's share of the row.
@@ -106,15 +131,16 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowA
 #pragma unroll
       for (int c = 0; c < SUB; ++c) {
         const uint32_t e = elem_of(s, c);
-        buffer_load_words<XW * 4>(xr, e * XB, xw[s][c]);
-        if constexpr (HAS_RES) buffer_load_words<RW * 4>(rr, e * RB, rw[s][c]);
-        buffer_load_words<WW * 4>(wr, e * WB, ww[s][c]);
+        buffer_load_words<XW * 4, true>(xr, e * XB, xw[s][c]);
+        if constexpr (HAS_RES) buffer_load_words<RW * 4, true>(rr, e * RB, rw[s][c]);
+        buffer_load_words<WW * 4, false>(wr, e * WB, ww[s][c]);
       }
     }
 
     // 2. Residual add (rounded once to the residual dtype and written back),
-    //    local sum of squares of the rounded value; fp8 also takes the
-    //    weighted products and their local max magnitude.
+    //    local sum of squares of the rounded value; quantized outputs also
+    //    take the weighted products p = (w + b) * h (and, with one scale per
+    //    row, their local max magnitude).
     float h[NV][SUB][U];
     float ss = 0.f;
     float mx = 0.f;
@@ -139,22 +165,23 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowA
         }
 #pragma unroll
         for (int i = 0; i < U; ++i) ss += h[s][c][i] * h[s][c][i];
-        if constexpr (FP8) {
+        if constexpr (QUANT) {
           float wf[U];
           unpack<WD, U>(ww[s][c], wf);
 #pragma unroll
           for (int i = 0; i < U; ++i) {
             if constexpr (BIAS) wf[i] += 1.0f;
             h[s][c][i] = wf[i] * h[s][c][i];
-            mx = __builtin_fmaxf(mx, __builtin_fabsf(h[s][c][i]));
+            if constexpr (QS == kQRow) mx = __builtin_fmaxf(mx, __builtin_fabsf(h[s][c][i]));
           }
         }
       }
     }
 
     // 3. Row reduction: DPP + readlane inside the wave, LDS across waves.
+    constexpr bool ROW_MAX = QUANT && QS == kQRow;
     ss = group_reduce<64, OpSum>(ss);
-    if constexpr (FP8) mx = group_reduce<64, OpMax>(mx);
+    if constexpr (ROW_MAX) mx = group_reduce<64, OpMax>(mx);
     if (nw > 1) {
       if (lane == 0) {
         red[parity][wave][0] = ss;
@@ -165,26 +192,57 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowA
       mx = 0.f;
       for (int i = 0; i < nw; ++i) {
         ss += red[parity][i][0];
-        if constexpr (FP8) mx = __builtin_fmaxf(mx, red[parity][i][1]);
+        if constexpr (ROW_MAX) mx = __builtin_fmaxf(mx, red[parity][i][1]);
       }
       parity ^= 1;
     }
     const float inv = rsqrtf(ss / static_cast<float>(a.hidden) + a.eps);
 
-    // 4. Scale and store.
+    // 4. Scale and store.  Scale groups (per 128 or per 32 elements) are GL
+    //    neighbouring lanes of one chunk: their max is a DPP group reduction,
+    //    and the group's first lane stores its scale (and amax).
     float amax = 0.f, qmul = 0.f;
-    if constexpr (FP8) {
+    if constexpr (ROW_MAX) {
       amax = mx * inv;  // == max |p * inv|: multiplying by inv > 0 is monotone
       qmul = amax > 0.f ? 448.0f / amax : 0.f;
+    }
+    __amdgpu_buffer_rsrc_t sr, ar;
+    if constexpr (QUANT && QS != kQRow) {
+      char* sbase = static_cast<char*>(a.scale) + row * groups * SCALE_BYTES;
+      sr = make_rsrc(sbase, groups * SCALE_BYTES);
+      ar = make_rsrc(a.amax != nullptr ? reinterpret_cast<char*>(a.amax) + row * groups * 4 : sbase,
+                     a.amax != nullptr ? groups * 4 : 0);
     }
 #pragma unroll
     for (int s = 0; s < NV; ++s) {
 #pragma unroll
       for (int c = 0; c < SUB; ++c) {
         float y[U];
-        if constexpr (FP8) {
+        if constexpr (QUANT && QS == kQRow) {
 #pragma unroll
           for (int i = 0; i < U; ++i) y[i] = (h[s][c][i] * inv) * qmul;
+        } else if constexpr (QUANT) {
+          float m = 0.f;
+#pragma unroll
+          for (int i = 0; i < U; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(h[s][c][i]));
+          const float gamax = group_reduce<GL, OpMax>(m) * inv;
+          const uint32_t gidx = elem_of(s, c) / QG;
+          const bool leader = (lane % GL) == 0;
+          if constexpr (QS == kQGroup128) {
+            const float gq = gamax > 0.f ? 448.0f / gamax : 0.f;
+#pragma unroll
+            for (int i = 0; i < U; ++i) y[i] = (h[s][c][i] * inv) * gq;
+            if (leader) buffer_store_f32(sr, gidx * 4, gamax / 448.0f);
+          } else {
+            // MX: shared exponent floor(log2 amax) - EMAX, clamped to E8M0's
+            // range; an all-zero block takes the smallest scale, 2^-127.
+            int se = gamax > 0.f ? __builtin_amdgcn_frexp_expf(gamax) - 1 - EMAX : -127;
+            se = se < -127 ? -127 : (se > 127 ? 127 : se);
+#pragma unroll
+            for (int i = 0; i < U; ++i) y[i] = __builtin_amdgcn_ldexpf(h[s][c][i] * inv, -se);
+            if (leader) buffer_store_u8(sr, gidx, static_cast<uint32_t>(se + 127));
+          }
+          if (leader && a.amax != nullptr) buffer_store_f32(ar, gidx * 4, gamax);
         } else {
           float wf[U];
           unpack<WD, U>(ww[s][c], wf);
@@ -196,47 +254,50 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowA
         }
         uint32_t ow[OW];
         pack<OD, U>(y, ow);
-        buffer_store_words<OW * 4>(orr, elem_of(s, c) * OB, ow);
+        buffer_store_words<OCB>(orr, elem_of(s, c) * OBITS / 8, ow);
       }
     }
-    if constexpr (FP8) {
+    if constexpr (ROW_MAX) {
       if (threadIdx.x == 0) {
-        a.scale[row] = amax / 448.0f;  // IEEE float32 division
+        static_cast<float*>(a.scale)[row] = amax / 448.0f;  // IEEE float32 division
         if (a.amax != nullptr) a.amax[row] = amax;
       }
     }
   }
 }
 
-template <int XD, int RD, int WD, int OD, int BIAS>
+template <int XD, int RD, int WD, int OD, int QS, int BIAS>
 const void* pick_nv(int nv) {
   switch (nv) {
-    case 1: return reinterpret_cast<const void*>(&rows_kernel<XD, RD, WD, OD, BIAS, 1>);
-    case 2: return reinterpret_cast<const void*>(&rows_kernel<XD, RD, WD, OD, BIAS, 2>);
-    case 4: return reinterpret_cast<const void*>(&rows_kernel<XD, RD, WD, OD, BIAS, 4>);
-    case 8: return reinterpret_cast<const void*>(&rows_kernel<XD, RD, WD, OD, BIAS, 8>);
+    case 1: return reinterpret_cast<const void*>(&rows_kernel<XD, RD, WD, OD, QS, BIAS, 1>);
+    case 2: return reinterpret_cast<const void*>(&rows_kernel<XD, RD, WD, OD, QS, BIAS, 2>);
+    case 4: return reinterpret_cast<const void*>(&rows_kernel<XD, RD, WD, OD, QS, BIAS, 4>);
+    case 8: return reinterpret_cast<const void*>(&rows_kernel<XD, RD, WD, OD, QS, BIAS, 8>);
     default: return nullptr;
   }
 }
 
-template <int XD, int RD, int OD>
+template <int XD, int RD, int OD, int QS>
 const void* pick_weight(const RowKey& k) {
-  if (k.w == kBF16) return k.bias ? pick_nv<XD, RD, kBF16, OD, 1>(k.nv) : pick_nv<XD, RD, kBF16, OD, 0>(k.nv);
-  if (k.w == kF32) return k.bias ? pick_nv<XD, RD, kF32, OD, 1>(k.nv) : pick_nv<XD, RD, kF32, OD, 0>(k.nv);
+  if (k.w == kBF16)
+    return k.bias ? pick_nv<XD, RD, kBF16, OD, QS, 1>(k.nv) : pick_nv<XD, RD, kBF16, OD, QS, 0>(k.nv);
+  if (k.w == kF32)
+    return k.bias ? pick_nv<XD, RD, kF32, OD, QS, 1>(k.nv) : pick_nv<XD, RD, kF32, OD, QS, 0>(k.nv);
   return nullptr;
 }
 
 }  // namespace
 
-// Built combinations for this (x, out) pair: residual none, f32, or the x
-// dtype; weight bf16 or f32; both weight forms; 1, 2, 4 or 8 vectors per lane.
+// Built combinations for this (x, out, scale scheme): residual none, f32, or
+// the x dtype; weight bf16 or f32; both weight forms; 1, 2, 4 or 8 vectors
+// per lane.
 const void* RN_CAT(pick_row_kernel_, RN_TU_NAME)(const RowKey& k) {
-  if (k.x != RN_TU_X || k.out != RN_TU_OUT) return nullptr;
+  if (k.x != RN_TU_X || k.out != RN_TU_OUT || k.qs != RN_TU_QS) return nullptr;
   switch (k.res) {
-    case kNone: return pick_weight<RN_TU_X, kNone, RN_TU_OUT>(k);
-    case kF32: return pick_weight<RN_TU_X, kF32, RN_TU_OUT>(k);
+    case kNone: return pick_weight<RN_TU_X, kNone, RN_TU_OUT, RN_TU_QS>(k);
+    case kF32: return pick_weight<RN_TU_X, kF32, RN_TU_OUT, RN_TU_QS>(k);
     case kBF16:
-      if constexpr (RN_TU_X == kBF16) return pick_weight<kBF16, kBF16, RN_TU_OUT>(k);
+      if constexpr (RN_TU_X == kBF16) return pick_weight<kBF16, kBF16, RN_TU_OUT, RN_TU_QS>(k);
       return nullptr;
     default: return nullptr;
   }

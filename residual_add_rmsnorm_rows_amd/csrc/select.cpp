@@ -52,6 +52,7 @@ static const char* dt_name(int dt) {
     case kBF16: return "bf16";
     case kF32: return "f32";
     case kFP8: return "fp8_e4m3fn";
+    case kFP4: return "fp4_e2m1";
     default: return "invalid";
   }
 }
@@ -65,11 +66,19 @@ rn_status check_row_shape(int64_t rows, int64_t hidden, uint32_t flags, bool has
   const int x = (flags >> RN_FLAGS_X_SHIFT) & 3;
   const int r = (flags >> RN_FLAGS_RES_SHIFT) & 3;
   const int w = (flags >> RN_FLAGS_W_SHIFT) & 3;
-  const int o = (flags >> RN_FLAGS_OUT_SHIFT) & 3;
-  if (x == 3 || w == 3 || o == 3 || (has_residual && r == 3))
-    return fail(RN_ERR_INVALID_ARG, "dtype code 3 is not a dtype (flags 0x%x)", flags);
+  const int o_code = (flags >> RN_FLAGS_OUT_SHIFT) & 3;
+  const int qs = (flags >> RN_FLAGS_SCALE_SHIFT) & 3;
+  if (x == 3 || w == 3 || (has_residual && r == 3))
+    return fail(RN_ERR_INVALID_ARG, "dtype code 3 is not an input dtype (flags 0x%x)", flags);
+  if (qs == 3) return fail(RN_ERR_INVALID_ARG, "scale granularity 3 does not exist (flags 0x%x)", flags);
   if (x == kFP8) return fail(RN_ERR_UNSUPPORTED, "x must be bf16 or f32");
   if (w == kFP8) return fail(RN_ERR_UNSUPPORTED, "weight must be bf16 or f32");
+  const int o = o_code == 3 ? kFP4 : o_code;
+  const bool quant = o == kFP8 || o == kFP4;
+  if (!quant && qs != kQRow)
+    return fail(RN_ERR_INVALID_ARG, "a scale granularity needs an fp8 or fp4 output");
+  if (o == kFP4 && qs != kQMx32)
+    return fail(RN_ERR_UNSUPPORTED, "fp4 e2m1 output is built with MX scales (RN_SCALE_MX32) only");
   int res = kNone;
   if (has_residual) {
     if (r == kFP8) return fail(RN_ERR_UNSUPPORTED, "residual must be bf16 or f32");
@@ -82,6 +91,11 @@ rn_status check_row_shape(int64_t rows, int64_t hidden, uint32_t flags, bool has
   if (hidden % vec != 0)
     return fail(RN_ERR_UNSUPPORTED, "hidden (%lld) must be a multiple of %d for %s x (16-byte lane "
                 "vectors)", (long long)hidden, vec, dt_name(x));
+  if (qs == kQGroup128 && hidden % 128 != 0)
+    return fail(RN_ERR_UNSUPPORTED, "hidden (%lld) must be a multiple of 128 for per-128 scales",
+                (long long)hidden);
+  if (qs == kQMx32 && hidden % 32 != 0)
+    return fail(RN_ERR_UNSUPPORTED, "hidden (%lld) must be a multiple of 32 for MX scales", (long long)hidden);
   const int64_t max_vecs = (int64_t)64 * kMaxVecsPerLane * (max_threads_for_nv(kMaxVecsPerLane) / 64);
   const int64_t max_vecs2 = (int64_t)64 * 4 * kMaxWavesPerRow;
   const int64_t cap = (max_vecs > max_vecs2 ? max_vecs : max_vecs2) * vec;
@@ -92,6 +106,7 @@ rn_status check_row_shape(int64_t rows, int64_t hidden, uint32_t flags, bool has
   key->res = res;
   key->w = w;
   key->out = o;
+  key->qs = qs;
   key->bias = (flags & RN_FLAG_WEIGHT_PLUS_ONE) ? 1 : 0;
   key->nv = 0;
   return RN_OK;
@@ -123,8 +138,9 @@ static const int64_t kMaxGrid = 0x7FFFFFFF;
 // Fastest (waves, vectors per lane) measured on MI355X for prefill-sized row
 // counts (1.2 GB of traffic per call) with a bf16 weight: each entry won an
 // interleaved sweep of every variant covering at most twice the row, three
-// repetitions each.  Key: x dtype, residual dtype (kNone: no residual),
-// whether the output is fp8, hidden size.
+// repetitions each (kernel with nontemporal input loads and output stores).
+// Key: x dtype, residual dtype (kNone: no residual), whether the output is
+// quantized (fp8 / fp4), hidden size.
 struct Tuned {
   int x, res;
   bool fp8;
@@ -133,33 +149,33 @@ struct Tuned {
 };
 static const Tuned kTuned[] = {
     // bf16 x, f32 residual stream, bf16/f32 out
-    {kBF16, kF32, false, 2048, 6, 1},    {kBF16, kF32, false, 4096, 9, 1},
-    {kBF16, kF32, false, 5120, 11, 1},   {kBF16, kF32, false, 7168, 12, 2},
-    {kBF16, kF32, false, 8192, 6, 4},    {kBF16, kF32, false, 12288, 16, 2},
+    {kBF16, kF32, false, 2048, 6, 1},    {kBF16, kF32, false, 4096, 8, 1},
+    {kBF16, kF32, false, 5120, 11, 1},   {kBF16, kF32, false, 7168, 16, 1},
+    {kBF16, kF32, false, 8192, 16, 1},   {kBF16, kF32, false, 12288, 16, 2},
     {kBF16, kF32, false, 16384, 16, 2},
     // bf16 x, bf16 residual, bf16/f32 out
-    {kBF16, kBF16, false, 2048, 5, 1},   {kBF16, kBF16, false, 4096, 9, 1},
+    {kBF16, kBF16, false, 2048, 2, 2},   {kBF16, kBF16, false, 4096, 9, 1},
     {kBF16, kBF16, false, 5120, 9, 2},   {kBF16, kBF16, false, 7168, 9, 2},
-    {kBF16, kBF16, false, 8192, 9, 2},   {kBF16, kBF16, false, 12288, 16, 2},
-    {kBF16, kBF16, false, 16384, 12, 4},
-    // bf16 x, bf16 residual, fp8 out
+    {kBF16, kBF16, false, 8192, 16, 1},  {kBF16, kBF16, false, 12288, 12, 2},
+    {kBF16, kBF16, false, 16384, 16, 2},
+    // bf16 x, bf16 residual, fp8/fp4 out
     {kBF16, kBF16, true, 2048, 4, 1},    {kBF16, kBF16, true, 4096, 8, 1},
     {kBF16, kBF16, true, 5120, 5, 2},    {kBF16, kBF16, true, 7168, 7, 2},
-    {kBF16, kBF16, true, 8192, 16, 1},   {kBF16, kBF16, true, 12288, 12, 2},
-    {kBF16, kBF16, true, 16384, 16, 2},
-    // bf16 x, f32 residual stream, fp8 out
-    {kBF16, kF32, true, 2048, 5, 1},     {kBF16, kF32, true, 4096, 9, 1},
-    {kBF16, kF32, true, 5120, 10, 1},    {kBF16, kF32, true, 7168, 16, 1},
+    {kBF16, kBF16, true, 8192, 8, 2},    {kBF16, kBF16, true, 12288, 12, 2},
+    {kBF16, kBF16, true, 16384, 4, 8},
+    // bf16 x, f32 residual stream, fp8/fp4 out
+    {kBF16, kF32, true, 2048, 5, 1},     {kBF16, kF32, true, 4096, 8, 1},
+    {kBF16, kF32, true, 5120, 8, 2},     {kBF16, kF32, true, 7168, 16, 1},
     {kBF16, kF32, true, 8192, 16, 1},    {kBF16, kF32, true, 12288, 16, 2},
     {kBF16, kF32, true, 16384, 16, 2},
     // bf16 x, no residual, bf16/f32 out
-    {kBF16, kNone, false, 2048, 4, 1},   {kBF16, kNone, false, 4096, 8, 1},
-    {kBF16, kNone, false, 5120, 6, 2},   {kBF16, kNone, false, 7168, 5, 4},
+    {kBF16, kNone, false, 2048, 3, 2},   {kBF16, kNone, false, 4096, 5, 2},
+    {kBF16, kNone, false, 5120, 2, 8},   {kBF16, kNone, false, 7168, 4, 4},
     {kBF16, kNone, false, 8192, 8, 2},   {kBF16, kNone, false, 12288, 4, 8},
     {kBF16, kNone, false, 16384, 8, 4},
     // f32 x, f32 residual, f32/bf16 out
-    {kF32, kF32, false, 2048, 7, 2},     {kF32, kF32, false, 4096, 16, 1},
-    {kF32, kF32, false, 5120, 15, 2},    {kF32, kF32, false, 7168, 6, 8},
+    {kF32, kF32, false, 2048, 9, 1},     {kF32, kF32, false, 4096, 9, 2},
+    {kF32, kF32, false, 5120, 16, 2},    {kF32, kF32, false, 7168, 11, 4},
     {kF32, kF32, false, 8192, 15, 4},    {kF32, kF32, false, 12288, 16, 4},
     {kF32, kF32, false, 16384, 16, 4},
 };
@@ -173,7 +189,8 @@ rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int
   int waves = 0, nv = 0;
   if (rows > num_cus) {
     for (const Tuned& t : kTuned) {
-      if (t.x == key.x && t.res == key.res && t.fp8 == (key.out == kFP8) && t.hidden == hidden &&
+      if (t.x == key.x && t.res == key.res && t.fp8 == (key.out == kFP8 || key.out == kFP4) &&
+          t.hidden == hidden &&
           rows_variant_ok(t.waves, t.nv, nvec)) {
         waves = t.waves;
         nv = t.nv;

@@ -6,10 +6,12 @@ from __future__ import annotations
 import numpy as np
 import torch
 
+from oracle import blockquant as BQ
 from oracle import compare as C
 from oracle import rownorm as O
 
-TORCH_DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8_e4m3fn": torch.float8_e4m3fn}
+TORCH_DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8_e4m3fn": torch.float8_e4m3fn,
+                "fp4_e2m1": torch.float4_e2m1fn_x2}
 
 
 def to_dev(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -21,10 +23,10 @@ def to_dev(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
 
 
 def to_host(t: torch.Tensor) -> np.ndarray:
-    """Stored bits/values: bf16 -> uint16 bits, f32 -> float32, fp8 -> uint8 codes."""
+    """Stored bits/values: bf16 -> uint16 bits, f32 -> float32, fp8 / fp4 pairs / E8M0 -> uint8."""
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
-    if t.dtype == torch.float8_e4m3fn:
+    if t.dtype in (torch.float8_e4m3fn, torch.float4_e2m1fn_x2, torch.float8_e8m0fnu):
         return t.view(torch.uint8).cpu().numpy()
     if t.dtype == torch.float32:
         return t.cpu().numpy()
@@ -32,7 +34,8 @@ def to_host(t: torch.Tensor) -> np.ndarray:
 
 
 def judge_rows(inputs: dict, x_dtype: str, res_dtype, w_dtype: str, out_dtype: str, eps: float,
-               weight_plus_one: bool, out: np.ndarray, res_out, scale=None, amax=None) -> dict:
+               weight_plus_one: bool, out: np.ndarray, res_out, scale=None, amax=None,
+               scale_scheme: str = "row") -> dict:
     """Compare the outputs of some rows (already on the host) with the oracle.
 
     ``inputs`` holds the same rows of x / residual and the full weight, as the
@@ -48,17 +51,23 @@ def judge_rows(inputs: dict, x_dtype: str, res_dtype, w_dtype: str, out_dtype: s
         same = np.array_equal(np.asarray(res_out).view(np.uint8), np.asarray(expect).view(np.uint8))
         rep["res_out_bit_exact"] = same
         rep["ok"] &= same
+    y = ref["y"]
     if out_dtype == "bf16":
-        r = C.check_bf16(out, ref["y"])
+        r = C.check_bf16(out, y)
         rep["out"] = r
-        rep["out_frac_rne"] = float((out == O.bf16_encode(ref["y"])).mean())
+        rep["out_frac_rne"] = float((out == O.bf16_encode(y)).mean())
         rep["ok"] &= r["ok"]
     elif out_dtype == "f32":
-        r = C.check_f32(out, ref["y"])
+        r = C.check_f32(out, y)
         rep["out"] = r
         rep["ok"] &= r["ok"]
-    else:
-        q = O.fp8_quantize_rows(ref["y"])
+    elif scale_scheme in ("row", "group128"):
+        if scale_scheme == "row":
+            q = O.fp8_quantize_rows(y)
+            own = lambda sc: O.fp8_quantize_rows(y, scale=sc)["codes"]  # noqa: E731
+        else:
+            q = BQ.fp8_quantize_groups(y, 128)
+            own = lambda sc: BQ.fp8_quantize_groups(y, 128, scale=sc)["codes"]  # noqa: E731
         scale = np.asarray(scale, dtype=np.float32)
         sc = C.check_f32(scale, q["scale"])
         rep["scale"] = sc
@@ -70,8 +79,34 @@ def judge_rows(inputs: dict, x_dtype: str, res_dtype, w_dtype: str, out_dtype: s
             rep["scale_formula_bit_exact"] = formula
             rep["amax"] = C.check_f32(amax, q["amax"])
             rep["ok"] &= formula and rep["amax"]["ok"]
-        codes_ref = O.fp8_quantize_rows(ref["y"], scale=scale)["codes"]
-        cr = C.check_fp8_codes(out, codes_ref)
+        cr = C.check_fp8_codes(out, own(scale))
+        rep["codes"] = cr
+        rep["ok"] &= cr["ok"]
+    else:  # MX, E8M0 scale per 32 elements
+        q = BQ.mx_quantize(y, out_dtype)
+        se = np.asarray(scale, dtype=np.uint8).astype(np.int64) - 127
+        emax = BQ.EMAX_ELEM[out_dtype]
+        # the GPU's exponent follows from its own amax exactly ...
+        if amax is not None:
+            amax = np.asarray(amax, dtype=np.float32).astype(np.float64)
+            _, E = np.frexp(np.where(amax > 0, amax, 1.0))
+            own_se = np.where(amax > 0, np.clip(E - 1 - emax, -127, 127), -127)
+            rep["exp_formula_exact"] = bool(np.array_equal(own_se, se))
+            rep["amax"] = C.check_f32(amax, q["amax"])
+            rep["ok"] &= rep["exp_formula_exact"] and rep["amax"]["ok"]
+        # ... and matches the oracle's, except by one where the exact amax sits
+        # within float32 rounding of a power of two
+        d = np.abs(se - q["shared_exp"])
+        near_pow2 = np.abs(np.log2(np.where(q["amax"] > 0, q["amax"], 1.0)) -
+                           np.round(np.log2(np.where(q["amax"] > 0, q["amax"], 1.0)))) < 1e-5
+        exp_ok = (d == 0) | ((d == 1) & near_pow2)
+        rep["exp_match"] = float((d == 0).mean())
+        rep["ok"] &= bool(exp_ok.all())
+        codes_ref = BQ.mx_quantize(y, out_dtype, shared_exp=se)["codes"]
+        if out_dtype == "fp4_e2m1":
+            cr = C.check_fp4_codes(BQ.unpack_fp4(out), codes_ref)
+        else:
+            cr = C.check_fp8_codes(out, codes_ref)
         rep["codes"] = cr
         rep["ok"] &= cr["ok"]
     return rep

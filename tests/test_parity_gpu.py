@@ -27,7 +27,7 @@ def _announce(msg):
     print(f"\n[case] {msg}", flush=True)
 
 
-def run_rownorm(wl, inputs, config=None, inplace=False):
+def run_rownorm(wl, inputs, config=None, inplace=False, scale_scheme="row"):
     x = to_dev(inputs["x"], wl.x_dtype)
     res = None if inputs["residual"] is None else to_dev(inputs["residual"], wl.res_dtype)
     w = to_dev(inputs["weight"], wl.w_dtype)
@@ -38,22 +38,23 @@ def run_rownorm(wl, inputs, config=None, inplace=False):
         if res is not None:
             kw["residual_out"] = res
     r = R.fused_add_rmsnorm(x, res, w, wl.eps, weight_plus_one=wl.weight_plus_one,
-                            out_dtype=TORCH_DTYPES[wl.out_dtype], return_amax=wl.out_dtype == "fp8_e4m3fn",
-                            config=config, **kw)
+                            out_dtype=TORCH_DTYPES[wl.out_dtype],
+                            return_amax=wl.out_dtype in ("fp8_e4m3fn", "fp4_e2m1"),
+                            scale_scheme=scale_scheme, config=config, **kw)
     torch.cuda.synchronize()
     return r
 
 
-def judge(wl, inputs, r, rows=None):
+def judge(wl, inputs, r, rows=None, scale_scheme="row"):
     sel = slice(None) if rows is None else rows
     sub = {"x": inputs["x"][sel], "residual": None if inputs["residual"] is None else inputs["residual"][sel],
            "weight": inputs["weight"]}
     out = to_host(r.out)[sel]
     res_out = None if r.residual_out is None else to_host(r.residual_out)[sel]
-    scale = None if r.scale is None else r.scale.cpu().numpy()[sel]
-    amax = None if r.amax is None else r.amax.cpu().numpy()[sel]
+    scale = None if r.scale is None else to_host(r.scale)[sel]
+    amax = None if r.amax is None else to_host(r.amax)[sel]
     return judge_rows(sub, wl.x_dtype, wl.res_dtype, wl.w_dtype, wl.out_dtype, wl.eps, wl.weight_plus_one,
-                      out, res_out, scale, amax)
+                      out, res_out, scale, amax, scale_scheme=scale_scheme)
 
 
 ROW_WORKLOADS = ["decode_8x1024", "decode_256x4096", "prefill_16384x8192", "prefill_fp8_8192x7168"]
@@ -163,6 +164,76 @@ def test_every_launch_variant(hidden, x, out):
             assert rep["ok"], (W, NV, grid, rep)
             n += 1
     assert n > 0
+
+
+BLOCK_CASES = [
+    # scheme, out dtype, x, residual
+    ("group128", "fp8_e4m3fn", "bf16", "bf16"), ("group128", "fp8_e4m3fn", "bf16", "f32"),
+    ("group128", "fp8_e4m3fn", "f32", "f32"), ("group128", "fp8_e4m3fn", "bf16", None),
+    ("mx32", "fp8_e4m3fn", "bf16", "bf16"), ("mx32", "fp8_e4m3fn", "bf16", "f32"),
+    ("mx32", "fp8_e4m3fn", "f32", None), ("mx32", "fp4_e2m1", "bf16", "bf16"),
+    ("mx32", "fp4_e2m1", "bf16", "f32"), ("mx32", "fp4_e2m1", "f32", "f32"), ("mx32", "fp4_e2m1", "bf16", None),
+]
+
+
+@pytest.mark.parametrize("scheme,out,x,res", BLOCK_CASES)
+@pytest.mark.parametrize("rows,hidden", [(37, 1024), (300, 7168), (5, 8192)])
+def test_block_scaled_outputs(scheme, out, x, res, rows, hidden):
+    """fp8 with per-128 scales and OCP MX (fp8 / fp4 with E8M0 per 32): scales,
+    exponents and codes against the oracle, zero groups included."""
+    wl = WL.RowNormWorkload(name="block", kind="test", rows=rows, hidden=hidden, x_dtype=x, res_dtype=res,
+                            w_dtype="bf16", out_dtype=out, x_dist=WL.Dist(0, 1, 0.01, 20.0),
+                            res_dist=None if res is None else WL.Dist(0, 1, 0.01, 20.0),
+                            w_dist=WL.Dist(1, 0.1), weight_plus_one=False, eps=1e-6)
+    _announce(f"block scheme={scheme} out={out} x={x} res={res} rows={rows} H={hidden}")
+    inputs = WL.generate_rownorm(wl, seed=12)
+    # one all-zero group of 128 in row 0
+    if x == "bf16":
+        inputs["x"][0, 128:256] = 0
+    else:
+        inputs["x"][0, 128:256] = 0.0
+    if res is not None:
+        inputs["residual"][0, 128:256] = 0
+    r = run_rownorm(wl, inputs, scale_scheme=scheme)
+    rep = judge(wl, inputs, r, scale_scheme=scheme)
+    assert rep["ok"], rep
+    sc = to_host(r.scale)
+    if scheme == "mx32":
+        assert np.all(sc[0, 4:8] == 0)  # 2^-127 for the zero blocks
+    else:
+        assert np.all(sc[0, 1] == 0)
+
+
+@pytest.mark.parametrize("scheme,out", [("group128", "fp8_e4m3fn"), ("mx32", "fp4_e2m1"), ("mx32", "fp8_e4m3fn")])
+def test_block_scaled_every_launch_variant(scheme, out):
+    H = 7168
+    wl = WL.RowNormWorkload(name="bv", kind="test", rows=19, hidden=H, x_dtype="bf16", res_dtype="f32",
+                            w_dtype="bf16", out_dtype=out, x_dist=WL.Dist(0, 1), res_dist=WL.Dist(0, 4),
+                            w_dist=WL.Dist(1, 0.1), weight_plus_one=True, eps=1e-6)
+    inputs = WL.generate_rownorm(wl, seed=13)
+    n = 0
+    for W, NV in _variants(H, 8):
+        for grid in (wl.rows, 4):
+            cfg = L.LaunchConfig()
+            cfg.kernel, cfg.waves_per_row, cfg.vecs_per_lane, cfg.grid = L.RN_KERNEL_ROWS, W, NV, grid
+            _announce(f"block variant {scheme} {out} W={W} NV={NV} grid={grid}")
+            rep = judge(wl, inputs, run_rownorm(wl, inputs, config=cfg, scale_scheme=scheme), scale_scheme=scheme)
+            assert rep["ok"], (W, NV, grid, rep)
+            n += 1
+    assert n > 0
+
+
+@pytest.mark.parametrize("scheme,out", [("group128", "fp8_e4m3fn"), ("mx32", "fp4_e2m1")])
+def test_block_scaled_full_size_sampled(scheme, out):
+    wl = WL.WORKLOADS["prefill_fp8_8192x7168"]
+    wl = WL.RowNormWorkload(**{**wl.__dict__, "out_dtype": out})
+    _announce(f"block full size {scheme} {out} cfg={R.query_config(wl.rows, wl.hidden, res_dtype=wl.res_dtype, out_dtype=out, scale_scheme=scheme)}")
+    inputs = WL.generate_rownorm(wl, seed=0)
+    r = run_rownorm(wl, inputs, scale_scheme=scheme)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([np.arange(3), np.arange(wl.rows - 3, wl.rows), rng.integers(0, wl.rows, 40)]))
+    rep = judge(wl, inputs, r, rows, scale_scheme=scheme)
+    assert rep["ok"], rep
 
 
 def test_edge_cases():
