@@ -84,3 +84,15 @@ def test_end_to_end_quantized_norm_row():
     q = O.fp8_quantize_rows(y)
     assert list(q["codes"][0]) == [0x76, 0xF6, 0x7E, 0xFE]
     assert q["scale"][0] == np.float32(np.float32(2 / np.sqrt(2.5)) / np.float32(448))
+
+
+def test_f32_acceptance_rule_underflow_floor():
+    from oracle import compare as C
+    # relative 1e-5 in the normal range ...
+    assert C.check_f32(np.array([1.0 + 2e-6]), np.array([1.0]))["ok"]
+    assert not C.check_f32(np.array([1.0 + 2e-5]), np.array([1.0]))["ok"]
+    # ... and the smallest normal float32 as the bound below it: an exact value
+    # of 1e-67 rounds to 0 in float32, which must be accepted; 1e-30 must not.
+    assert C.check_f32(np.array([0.0]), np.array([1e-67]))["ok"]
+    assert C.check_f32(np.array([-0.0]), np.array([-3e-40]))["ok"]
+    assert not C.check_f32(np.array([0.0]), np.array([1e-30]))["ok"]
