@@ -203,6 +203,34 @@ rn_status qknorm_fwd_config(const void* q, const void* k, const void* q_weight, 
                             int64_t k_token_stride, float eps, uint32_t flags,
                             const rn_launch_config* cfg, void* stream);
 
+/*
+ * SiLU-and-mul (SwiGLU) over rows: out[r, i] = silu(x[r, i]) * x[r, d + i],
+ * silu(g) = g / (1 + exp(-g)), in float32.  The gated activation of the MLP:
+ * the "Tile-Level Activation Overlap for Efficient LLM Inference" summary
+ * describes the SwiGLU step as the combination of the gate and up projections,
+ * and "CuTeDSL at Perplexity" ("Inference at Perplexity") lists activation
+ * kernels in the same library.  Reading: each row of x is a merged gate/up
+ * projection, gate in its first half and up in its second half.
+ *
+ *   x          [rows, 2 d] of dtype flags.x (bf16 or f32)           (read)
+ *   out        [rows, d] of dtype flags.out (bf16, f32, fp8; fp4: d / 2 bytes per row) (write)
+ *   out_scale  quantized output only, laid out as for rmsnorm_fwd    (write)
+ *   out_amax   quantized output only, may be NULL                    (write)
+ *   rows >= 0; d >= 1, a multiple of the 16-byte vector of x and at most 32768 (bf16) /
+ *   16384 (f32); flags: bits 0-1 x dtype, bits 6-7 out dtype, bits 9-10 scale granularity
+ *   (as for rmsnorm_fwd); other bits must be zero.  out may not overlap x.
+ */
+rn_status silu_mul_fwd(const void* x, void* out, void* out_scale, float* out_amax, int64_t rows,
+                       int64_t d, uint32_t flags, void* stream);
+
+/* As silu_mul_fwd with an explicit launch configuration (as rmsnorm_fwd_config). */
+rn_status silu_mul_fwd_config(const void* x, void* out, void* out_scale, float* out_amax, int64_t rows,
+                              int64_t d, uint32_t flags, const rn_launch_config* cfg, void* stream);
+
+/* Host-only: the launch configuration silu_mul_fwd would use. */
+rn_status silu_mul_query_config(int64_t rows, int64_t d, uint32_t flags, int32_t num_cus,
+                                rn_launch_config* cfg);
+
 /* Host-only: the launch configuration rmsnorm_fwd would use for these sizes on
  * a device with num_cus compute units (num_cus <= 0: query the current device);
  * has_residual says whether the call passes a residual (its dtype bits are then

@@ -22,6 +22,8 @@ __all__ = [
     "fused_add_rmsnorm",
     "rmsnorm",
     "qk_norm",
+    "silu_mul",
+    "query_silu_mul_config",
     "query_config",
     "query_qknorm_config",
     "RNError",
@@ -227,4 +229,61 @@ def query_qknorm_config(tokens: int, num_q_heads: int, num_k_heads: int, head_di
     flags = _qk_flags(dtype, w_dtype, False)
     check(lib().qknorm_query_config(tokens, num_q_heads, num_k_heads, head_dim, flags, num_cus,
                                     ctypes.byref(cfg)))
+    return cfg.as_dict()
+
+
+def silu_mul(x: torch.Tensor, *, out_dtype: Optional[torch.dtype] = None, scale_scheme: str = "row",
+             return_amax: bool = False, out: Optional[torch.Tensor] = None,
+             config: Optional[LaunchConfig] = None) -> NormOutput:
+    """SwiGLU: ``silu(x[..., :d]) * x[..., d:]`` for ``x`` [..., 2 d] (bf16 or f32).
+
+    Outputs as for ``fused_add_rmsnorm`` (bf16, f32, fp8 e4m3fn with per-row /
+    per-128 / MX scales, fp4 e2m1 with MX scales); ``residual_out`` is None.
+    """
+    device = x.device
+    if device.type != "cuda":
+        raise ValueError("x must be a device tensor")
+    _dev_tensor(x, "x", device)
+    if x.shape[-1] % 2:
+        raise ValueError("the last dimension of x must be 2 d (gate, then up)")
+    d = x.shape[-1] // 2
+    rows = x.numel() // x.shape[-1] if x.shape[-1] else 0
+    xd = _name(x.dtype, "x")
+    od_t = out_dtype if out_dtype is not None else (out.dtype if out is not None else x.dtype)
+    od = _name(od_t, "out")
+    out_shape = (*x.shape[:-1], d // 2 if od == "fp4_e2m1" else d)
+    if out is None:
+        out = torch.empty(out_shape, dtype=od_t, device=device)
+    else:
+        _dev_tensor(out, "out", device)
+        if tuple(out.shape) != tuple(out_shape) or out.dtype != od_t:
+            raise ValueError("out has the wrong shape or dtype")
+    if scale_scheme not in _GROUP:
+        raise ValueError(f"scale_scheme must be one of {sorted(_GROUP)}")
+    scale = amax = None
+    if od in ("fp8_e4m3fn", "fp4_e2m1"):
+        g = _GROUP[scale_scheme]
+        nscale = (rows,) if g is None else (rows, d // g if d % g == 0 else 0)
+        sdt = torch.float8_e8m0fnu if scale_scheme == "mx32" else torch.float32
+        scale = torch.empty(nscale, dtype=sdt, device=device)
+        if return_amax:
+            amax = torch.empty(nscale, dtype=torch.float32, device=device)
+    flags = (_lib.DTYPE_CODES[xd] << _lib.RN_FLAGS_X_SHIFT) | (_lib.DTYPE_CODES[od] << _lib.RN_FLAGS_OUT_SHIFT)
+    flags |= _lib.SCALE_SCHEMES[scale_scheme] << _lib.RN_FLAGS_SCALE_SHIFT
+    L = lib()
+    if config is not None:
+        st = L.silu_mul_fwd_config(_p(x), _p(out), _p(scale), _p(amax), rows, d, flags, ctypes.byref(config),
+                                   _stream(device))
+    else:
+        st = L.silu_mul_fwd(_p(x), _p(out), _p(scale), _p(amax), rows, d, flags, _stream(device))
+    check(st)
+    return NormOutput(out, None, scale, amax)
+
+
+def query_silu_mul_config(rows: int, d: int, *, x_dtype: str = "bf16", out_dtype: str = "bf16",
+                          scale_scheme: str = "row", num_cus: int = 256) -> dict:
+    cfg = LaunchConfig()
+    flags = (_lib.DTYPE_CODES[x_dtype] << _lib.RN_FLAGS_X_SHIFT) | (_lib.DTYPE_CODES[out_dtype] << _lib.RN_FLAGS_OUT_SHIFT)
+    flags |= _lib.SCALE_SCHEMES[scale_scheme] << _lib.RN_FLAGS_SCALE_SHIFT
+    check(lib().silu_mul_query_config(rows, d, flags, num_cus, ctypes.byref(cfg)))
     return cfg.as_dict()

@@ -172,6 +172,47 @@ rn_status heads_entry(const void* q, const void* k, const void* q_weight, const 
   return launch(fn, cfg.grid, cfg.block_threads, &a, stream);
 }
 
+rn_status act_entry(const void* x, void* out, void* out_scale, float* out_amax, int64_t rows, int64_t d,
+                    uint32_t flags, const rn_launch_config* explicit_cfg, void* stream) {
+  clear_error();
+  ActKey key;
+  rn_status st = check_act_shape(rows, d, flags, &key);
+  if (st != RN_OK) return st;
+  const bool quant = key.out == kFP8 || key.out == kFP4;
+  if (!quant && (out_scale != nullptr || out_amax != nullptr))
+    return fail(RN_ERR_INVALID_ARG, "out_scale / out_amax are only for fp8 / fp4 output");
+  if (rows == 0) return RN_OK;
+  if (x == nullptr || out == nullptr) return fail(RN_ERR_INVALID_ARG, "x and out must not be NULL");
+  if (quant && out_scale == nullptr) return fail(RN_ERR_INVALID_ARG, "quantized output needs out_scale");
+  if (!aligned(x, 16) || !aligned(out, 16)) return fail(RN_ERR_MISALIGNED, "x and out must be 16-byte aligned");
+  if ((out_scale && key.qs != kQMx32 && !aligned(out_scale, 4)) || (out_amax && !aligned(out_amax, 4)))
+    return fail(RN_ERR_MISALIGNED, "float32 scales / out_amax must be 4-byte aligned");
+
+  rn_launch_config cfg;
+  if (explicit_cfg != nullptr) {
+    RowKey rk;
+    rk.x = key.x;
+    st = check_row_config(rows, d, rk, explicit_cfg, &cfg);
+  } else {
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != RN_OK) return st;
+    st = select_act_config(rows, d, key, cus, &cfg);
+  }
+  if (st != RN_OK) return st;
+  key.nv = cfg.vecs_per_lane;
+  const void* fn = pick_act_kernel(key);
+  if (fn == nullptr) return fail(RN_ERR_UNSUPPORTED, "no silu_mul kernel built for this combination");
+  ActArgs a;
+  a.x = x;
+  a.out = out;
+  a.scale = out_scale;
+  a.amax = out_amax;
+  a.rows = rows;
+  a.d = static_cast<int32_t>(d);
+  return launch(fn, cfg.grid, cfg.block_threads, &a, stream);
+}
+
 }  // namespace
 }  // namespace rn
 
@@ -255,6 +296,35 @@ rn_status qknorm_query_config(int64_t tokens, int32_t num_q_heads, int32_t num_k
     if (st != RN_OK) return st;
   }
   return select_head_config(tokens > 0 ? tokens : 1, num_q_heads, num_k_heads, key, cus, cfg);
+}
+
+rn_status silu_mul_fwd(const void* x, void* out, void* out_scale, float* out_amax, int64_t rows,
+                       int64_t d, uint32_t flags, void* stream) {
+  return act_entry(x, out, out_scale, out_amax, rows, d, flags, nullptr, stream);
+}
+
+rn_status silu_mul_fwd_config(const void* x, void* out, void* out_scale, float* out_amax, int64_t rows,
+                              int64_t d, uint32_t flags, const rn_launch_config* cfg, void* stream) {
+  if (cfg == nullptr) {
+    clear_error();
+    return fail(RN_ERR_INVALID_ARG, "launch config is NULL");
+  }
+  return act_entry(x, out, out_scale, out_amax, rows, d, flags, cfg, stream);
+}
+
+rn_status silu_mul_query_config(int64_t rows, int64_t d, uint32_t flags, int32_t num_cus,
+                                rn_launch_config* cfg) {
+  clear_error();
+  if (cfg == nullptr) return fail(RN_ERR_INVALID_ARG, "cfg is NULL");
+  ActKey key;
+  rn_status st = check_act_shape(rows, d, flags, &key);
+  if (st != RN_OK) return st;
+  int cus = num_cus;
+  if (cus <= 0) {
+    st = device_cus(&cus);
+    if (st != RN_OK) return st;
+  }
+  return select_act_config(rows > 0 ? rows : 1, d, key, cus, cfg);
 }
 
 rn_status rn_launch_empty(void* stream) {

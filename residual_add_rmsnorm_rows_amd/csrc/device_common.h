@@ -308,3 +308,51 @@ __device__ __forceinline__ float group_reduce(float v) {
 }
 
 }  // namespace rn
+
+namespace rn {
+
+// ---------------------------------------------------------------------------
+// Block-scaled quantization of one chunk of U consecutive elements whose
+// scale group spans GL = group / U neighbouring lanes (group = 128 for the
+// per-128 fp8 scheme, 32 for MX).  The values to quantize are v[i] * mul with
+// mul > 0; the group's amax is max|v| over the group times mul (multiplying
+// by a positive number is monotone, so this is the max of the products).
+// Writes the scaled values into y (ready for pack<OD>) and, from the group's
+// first lane, the scale (float32 amax / 448, or E8M0 byte e + 127) at index
+// gidx of the row's scale resource, and the amax when requested.
+// ---------------------------------------------------------------------------
+
+template <int QS>
+constexpr int scale_group() { return QS == kQGroup128 ? 128 : QS == kQMx32 ? 32 : 0; }
+
+template <int OD, int QS, int U>
+__device__ __forceinline__ void quantize_group_chunk(const float (&v)[U], float mul, int lane, uint32_t gidx,
+                                                     __amdgpu_buffer_rsrc_t sr, __amdgpu_buffer_rsrc_t ar,
+                                                     bool want_amax, float (&y)[U]) {
+  constexpr int QG = scale_group<QS>();
+  constexpr int GL = QG / U;
+  constexpr int EMAX = OD == kFP8 ? 8 : 2;  // MX: exponent of the element format's top binade
+  static_assert(QG % U == 0 && GL <= 64, "scale groups");
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < U; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[i]));
+  const float gamax = group_reduce<GL, OpMax>(m) * mul;
+  const bool leader = (lane % GL) == 0;
+  if constexpr (QS == kQGroup128) {
+    const float gq = gamax > 0.f ? 448.0f / gamax : 0.f;
+#pragma unroll
+    for (int i = 0; i < U; ++i) y[i] = (v[i] * mul) * gq;
+    if (leader) buffer_store_f32(sr, gidx * 4, gamax / 448.0f);
+  } else {
+    // MX: shared exponent floor(log2 amax) - EMAX, clamped to E8M0's range;
+    // an all-zero block takes the smallest scale, 2^-127.
+    int se = gamax > 0.f ? __builtin_amdgcn_frexp_expf(gamax) - 1 - EMAX : -127;
+    se = se < -127 ? -127 : (se > 127 ? 127 : se);
+#pragma unroll
+    for (int i = 0; i < U; ++i) y[i] = __builtin_amdgcn_ldexpf(v[i] * mul, -se);
+    if (leader) buffer_store_u8(sr, gidx, static_cast<uint32_t>(se + 127));
+  }
+  if (leader && want_amax) buffer_store_f32(ar, gidx * 4, gamax);
+}
+
+}  // namespace rn

@@ -50,12 +50,27 @@ struct HeadArgs {
   float eps;
 };
 
+// Kernel arguments of the SiLU-and-mul kernel.
+struct ActArgs {
+  const void* x;         // [rows, 2 d]: gate in [0, d), up in [d, 2 d)
+  void* out;             // [rows, d]
+  void* scale;           // quantized output only
+  float* amax;           // quantized output only, may be nullptr
+  int64_t rows;
+  int32_t d;
+};
+
 // Everything the launcher needs to pick a compiled kernel.
 struct RowKey {
   int x, res, w, out;  // res == kNone: no residual
   int qs;              // QScheme (kQRow unless the output is quantized)
   int bias;            // 0 or 1
   int nv;              // vectors per lane: 1, 2, 4, 8
+};
+
+struct ActKey {
+  int x, out, qs;
+  int nv;
 };
 
 struct HeadKey {
@@ -91,6 +106,11 @@ rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int
 // Checks an explicit configuration and fills the derived fields.
 rn_status check_row_config(int64_t rows, int64_t hidden, const RowKey& key,
                            const rn_launch_config* in, rn_launch_config* out);
+
+// SiLU-and-mul: flags (x dtype, out dtype, scale scheme) and sizes.
+rn_status check_act_shape(int64_t rows, int64_t d, uint32_t flags, ActKey* key);
+// Selector for the SiLU-and-mul kernel (same launch shapes as the rows kernel).
+rn_status select_act_config(int64_t rows, int64_t d, const ActKey& key, int num_cus, rn_launch_config* cfg);
 
 rn_status check_head_shape(int64_t tokens, int32_t nq, int32_t nk, int32_t head_dim,
                            uint32_t flags, HeadKey* key);
@@ -131,6 +151,8 @@ const void* pick_row_kernel_f32_fp8_mx(const RowKey& key);
 const void* pick_row_kernel_f32_fp4_mx(const RowKey& key);
 // heads_kernel.hip
 const void* pick_head_kernel(const HeadKey& key);
+// act_kernel.hip
+const void* pick_act_kernel(const ActKey& key);
 // empty_kernel.hip
 const void* empty_kernel_address();
 }  // namespace rn

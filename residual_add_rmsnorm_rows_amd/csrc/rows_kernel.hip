@@ -86,8 +86,6 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowA
   constexpr int OCB = U * OBITS / 8;        // output bytes per chunk
   constexpr int OW = words_for<OD, U>();    // dwords holding one output chunk
   constexpr int QG = QS == kQGroup128 ? 128 : QS == kQMx32 ? 32 : 0;  // elements per scale
-  constexpr int GL = QG ? QG / U : 1;       // lanes per scale group
-  constexpr int EMAX = OD == kFP8 ? 8 : 2;  // MX: exponent of the element format's top binade
   static_assert(SUB == 1 || SUB == 2, "chunking");
   static_assert(!QUANT || QS == kQRow || (QG % U == 0 && (64 * U) % QG == 0), "scale groups");
   static_assert(QS == kQRow || QUANT, "scale groups only for quantized outputs");
@@ -222,27 +220,7 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowA
 #pragma unroll
           for (int i = 0; i < U; ++i) y[i] = (h[s][c][i] * inv) * qmul;
         } else if constexpr (QUANT) {
-          float m = 0.f;
-#pragma unroll
-          for (int i = 0; i < U; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(h[s][c][i]));
-          const float gamax = group_reduce<GL, OpMax>(m) * inv;
-          const uint32_t gidx = elem_of(s, c) / QG;
-          const bool leader = (lane % GL) == 0;
-          if constexpr (QS == kQGroup128) {
-            const float gq = gamax > 0.f ? 448.0f / gamax : 0.f;
-#pragma unroll
-            for (int i = 0; i < U; ++i) y[i] = (h[s][c][i] * inv) * gq;
-            if (leader) buffer_store_f32(sr, gidx * 4, gamax / 448.0f);
-          } else {
-            // MX: shared exponent floor(log2 amax) - EMAX, clamped to E8M0's
-            // range; an all-zero block takes the smallest scale, 2^-127.
-            int se = gamax > 0.f ? __builtin_amdgcn_frexp_expf(gamax) - 1 - EMAX : -127;
-            se = se < -127 ? -127 : (se > 127 ? 127 : se);
-#pragma unroll
-            for (int i = 0; i < U; ++i) y[i] = __builtin_amdgcn_ldexpf(h[s][c][i] * inv, -se);
-            if (leader) buffer_store_u8(sr, gidx, static_cast<uint32_t>(se + 127));
-          }
-          if (leader && a.amax != nullptr) buffer_store_f32(ar, gidx * 4, gamax);
+          quantize_group_chunk<OD, QS, U>(h[s][c], inv, lane, elem_of(s, c) / QG, sr, ar, a.amax != nullptr, y);
         } else {
           float wf[U];
           unpack<WD, U>(ww[s][c], wf);

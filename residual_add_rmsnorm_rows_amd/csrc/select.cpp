@@ -180,14 +180,16 @@ static const Tuned kTuned[] = {
     {kF32, kF32, false, 16384, 16, 4},
 };
 
-rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int num_cus,
-                            rn_launch_config* cfg) {
+// Launch shape for rows of `hidden` elements; `use_table` consults kTuned
+// (measured for the fused add + RMSNorm with a bf16 weight).
+static rn_status select_rows_shape(int64_t rows, int64_t hidden, const RowKey& key, int num_cus,
+                                   bool use_table, rn_launch_config* cfg) {
   if (num_cus < 1) return fail(RN_ERR_INVALID_ARG, "num_cus must be >= 1");
   const int vec = 16 / (key.x == kBF16 ? 2 : 4);
   const int64_t nvec = hidden / vec;
   const int choices[4] = {1, 2, 4, 8};
   int waves = 0, nv = 0;
-  if (rows > num_cus) {
+  if (rows > num_cus && use_table) {
     for (const Tuned& t : kTuned) {
       if (t.x == key.x && t.res == key.res && t.fp8 == (key.out == kFP8 || key.out == kFP4) &&
           t.hidden == hidden &&
@@ -214,6 +216,11 @@ rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int
   return RN_OK;
 }
 
+rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int num_cus,
+                            rn_launch_config* cfg) {
+  return select_rows_shape(rows, hidden, key, num_cus, key.w == kBF16, cfg);
+}
+
 rn_status check_row_config(int64_t rows, int64_t hidden, const RowKey& key,
                            const rn_launch_config* in, rn_launch_config* out) {
   if (in == nullptr) return fail(RN_ERR_INVALID_ARG, "launch config is NULL");
@@ -227,6 +234,35 @@ rn_status check_row_config(int64_t rows, int64_t hidden, const RowKey& key,
     return fail(RN_ERR_INVALID_ARG, "config grid %lld outside [1, rows]", (long long)in->grid);
   fill_rows_cfg(vec, in->waves_per_row, in->vecs_per_lane, rows > 0 ? rows : 1, in->grid, out);
   return RN_OK;
+}
+
+rn_status check_act_shape(int64_t rows, int64_t d, uint32_t flags, ActKey* key) {
+  if (rows < 0) return fail(RN_ERR_INVALID_ARG, "rows must be >= 0 (got %lld)", (long long)rows);
+  if (d < 1) return fail(RN_ERR_INVALID_ARG, "d must be >= 1 (got %lld)", (long long)d);
+  const uint32_t allowed = (3u << RN_FLAGS_X_SHIFT) | (3u << RN_FLAGS_OUT_SHIFT) | (3u << RN_FLAGS_SCALE_SHIFT);
+  if (flags & ~allowed)
+    return fail(RN_ERR_INVALID_ARG, "silu_mul flags 0x%x use bits other than x, out and scale", flags);
+  // the output checks are those of the rows kernel (no residual, bf16 weight)
+  RowKey rk;
+  rn_status st = check_row_shape(rows, d, flags, false, &rk);
+  if (st != RN_OK) return st;
+  key->x = rk.x;
+  key->out = rk.out;
+  key->qs = rk.qs;
+  key->nv = 0;
+  return RN_OK;
+}
+
+rn_status select_act_config(int64_t rows, int64_t d, const ActKey& key, int num_cus, rn_launch_config* cfg) {
+  RowKey rk;
+  rk.x = key.x;
+  rk.res = kNone;
+  rk.w = kBF16;
+  rk.out = key.out;
+  rk.qs = key.qs;
+  rk.bias = 0;
+  rk.nv = 0;
+  return select_rows_shape(rows, d, rk, num_cus, false, cfg);
 }
 
 rn_status check_head_shape(int64_t tokens, int32_t nq, int32_t nk, int32_t head_dim,

@@ -52,6 +52,15 @@ def judge_rows(inputs: dict, x_dtype: str, res_dtype, w_dtype: str, out_dtype: s
         rep["res_out_bit_exact"] = same
         rep["ok"] &= same
     y = ref["y"]
+    rep.update(judge_y(y, out_dtype, out, scale, amax, scale_scheme))
+    rep["ok"] = rep["ok"] and rep.pop("y_ok")
+    return rep
+
+
+def judge_y(y: np.ndarray, out_dtype: str, out: np.ndarray, scale=None, amax=None,
+            scale_scheme: str = "row") -> dict:
+    """Judge an output tensor (host bits) against the exact pre-rounding values y [rows, n]."""
+    rep = {"ok": True}
     if out_dtype == "bf16":
         r = C.check_bf16(out, y)
         rep["out"] = r
@@ -109,4 +118,5 @@ def judge_rows(inputs: dict, x_dtype: str, res_dtype, w_dtype: str, out_dtype: s
             cr = C.check_fp8_codes(out, codes_ref)
         rep["codes"] = cr
         rep["ok"] &= cr["ok"]
+    rep["y_ok"] = rep.pop("ok")
     return rep

@@ -18,7 +18,8 @@ import workloads as WL
 from oracle import compare as C
 from oracle import rownorm as O
 from residual_add_rmsnorm_rows_amd import _lib as L
-from tests.gpu_util import TORCH_DTYPES, judge_rows, to_dev, to_host
+from oracle import activation as ACT
+from tests.gpu_util import TORCH_DTYPES, judge_rows, judge_y, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -387,3 +388,70 @@ def test_deterministic():
 def test_empty_kernel_launch():
     L.check(L.lib().rn_launch_empty(torch.cuda.current_stream().cuda_stream))
     torch.cuda.synchronize()
+
+
+ACT_OUTS = [("bf16", "row"), ("f32", "row"), ("fp8_e4m3fn", "row"), ("fp8_e4m3fn", "group128"),
+            ("fp8_e4m3fn", "mx32"), ("fp4_e2m1", "mx32")]
+
+
+def run_act(wl, x_np, scale_scheme, config=None):
+    x = to_dev(x_np, wl.x_dtype)
+    r = R.silu_mul(x, out_dtype=TORCH_DTYPES[wl.out_dtype], scale_scheme=scale_scheme,
+                   return_amax=wl.out_dtype in ("fp8_e4m3fn", "fp4_e2m1"), config=config)
+    torch.cuda.synchronize()
+    return r
+
+
+def judge_act(wl, x_np, r, scale_scheme, rows=None):
+    sel = slice(None) if rows is None else rows
+    y = ACT.silu_mul_rows(O.decode(x_np[sel], wl.x_dtype), wl.d)
+    scale = None if r.scale is None else to_host(r.scale)[sel]
+    amax = None if r.amax is None else to_host(r.amax)[sel]
+    rep = judge_y(y, wl.out_dtype, to_host(r.out)[sel], scale, amax, scale_scheme)
+    rep["ok"] = rep.pop("y_ok")
+    return rep
+
+
+@pytest.mark.parametrize("out,scheme", ACT_OUTS)
+@pytest.mark.parametrize("x", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,d", [(37, 1024), (300, 3584), (3, 14336)])
+def test_silu_mul_parity(out, scheme, x, rows, d):
+    wl = WL.ActWorkload(name="act", rows=rows, d=d, x_dtype=x, out_dtype=out, x_dist=WL.Dist(0, 2, 0.01, 20.0))
+    _announce(f"silu_mul x={x} out={out} scheme={scheme} rows={rows} d={d}")
+    xn = WL.generate_act(wl, seed=17)
+    if x == "bf16":
+        xn[0, 256:512] = 0  # a zero group of the output (gate zero)
+    else:
+        xn[0, 256:512] = 0.0
+    rep = judge_act(wl, xn, run_act(wl, xn, scheme), scheme)
+    assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("out,scheme", [("bf16", "row"), ("fp8_e4m3fn", "row"), ("fp4_e2m1", "mx32")])
+def test_silu_mul_every_launch_variant(out, scheme):
+    d = 3584
+    wl = WL.ActWorkload(name="actv", rows=23, d=d, x_dtype="bf16", out_dtype=out, x_dist=WL.Dist(0, 1))
+    xn = WL.generate_act(wl, seed=18)
+    n = 0
+    for W, NV in _variants(d, 8):
+        for grid in (wl.rows, 4):
+            cfg = L.LaunchConfig()
+            cfg.kernel, cfg.waves_per_row, cfg.vecs_per_lane, cfg.grid = L.RN_KERNEL_ROWS, W, NV, grid
+            _announce(f"silu_mul variant out={out} W={W} NV={NV} grid={grid}")
+            rep = judge_act(wl, xn, run_act(wl, xn, scheme, config=cfg), scheme)
+            assert rep["ok"], (W, NV, grid, rep)
+            n += 1
+    assert n > 0
+
+
+@pytest.mark.parametrize("out,scheme", [("bf16", "row"), ("fp8_e4m3fn", "mx32")])
+def test_silu_mul_full_size_sampled(out, scheme):
+    wl = WL.WORKLOADS["silu_mul_8192x14336"]
+    wl = WL.ActWorkload(**{**wl.__dict__, "out_dtype": out})
+    _announce(f"silu_mul full size out={out} scheme={scheme} cfg={R.query_silu_mul_config(wl.rows, wl.d, out_dtype=out, scale_scheme=scheme)}")
+    xn = WL.generate_act(wl, seed=0)
+    r = run_act(wl, xn, scheme)
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([np.arange(3), np.arange(wl.rows - 3, wl.rows), rng.integers(0, wl.rows, 30)]))
+    rep = judge_act(wl, xn, r, scheme, rows)
+    assert rep["ok"], rep

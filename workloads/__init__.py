@@ -41,6 +41,8 @@ __all__ = [
     "Dist",
     "RowNormWorkload",
     "QKNormWorkload",
+    "ActWorkload",
+    "generate_act",
     "WORKLOADS",
     "generate_rownorm",
     "generate_qknorm",
@@ -110,6 +112,22 @@ class QKNormWorkload:
         return replace(self, tokens=tokens)
 
 
+@dataclass(frozen=True)
+class ActWorkload:
+    """SiLU-and-mul over rows of a merged gate/up projection ``[rows, 2 d]``."""
+
+    name: str
+    rows: int
+    d: int
+    x_dtype: str
+    out_dtype: str
+    x_dist: Dist
+    description: str = ""
+
+    def with_rows(self, rows: int) -> "ActWorkload":
+        return replace(self, rows=rows)
+
+
 N01 = Dist(0.0, 1.0)
 W_N1 = Dist(1.0, 0.1)
 
@@ -144,6 +162,11 @@ WORKLOADS: Dict[str, object] = {
         weight_plus_one=False, eps=1e-6,
         description="prefill with fp8 e4m3fn out + per-row scale amax/448, 8192 x 7168 bf16, "
                     "1% outliers x20 on x and residual",
+    ),
+    "silu_mul_8192x14336": ActWorkload(
+        name="silu_mul_8192x14336", rows=8192, d=14336, x_dtype="bf16", out_dtype="bf16", x_dist=N01,
+        description="SwiGLU silu(gate) * up, 8192 tokens, merged gate/up projection 2 x 14336 bf16 "
+                    "~ N(0,1), bf16 out",
     ),
 }
 
@@ -234,3 +257,8 @@ def generate_qknorm(wl: QKNormWorkload, seed: int = 0) -> Dict[str, Optional[np.
     qw = draw_tensor(seed, STREAM_W, None, (1, D), wl.w_dist, wl.w_dtype)[0]
     kw = draw_tensor(seed, STREAM_MASK_X, None, (1, D), wl.w_dist, wl.w_dtype)[0]
     return {"q": q, "k": k, "q_weight": qw, "k_weight": kw}
+
+
+def generate_act(wl: ActWorkload, seed: int = 0, row_range: Optional[Tuple[int, int]] = None) -> np.ndarray:
+    """Input ``x`` [rows, 2 d] of a SiLU-and-mul workload (stream x, outliers on the x mask stream)."""
+    return draw_tensor(seed, STREAM_X, STREAM_MASK_X, (wl.rows, 2 * wl.d), wl.x_dist, wl.x_dtype, row_range)
