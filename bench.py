@@ -17,9 +17,10 @@ The same line carries:
   * ``secondary``: the other workloads -- decode calls (us/call against an
     empty kernel launched the same way), per-head QK-norm, the fp8-output
     prefill with per-row scales, and the same prefill with block-scaled
-    outputs (fp8 per-128 scales, MXFP8, MXFP4) (GB/s, with rotating buffer
-    sets larger than the 256 MB Infinity Cache so that every call streams
-    from HBM).
+    outputs (fp8 per-128 scales, MXFP8, MXFP4), and the SiLU-and-mul
+    activation (bf16, MXFP8, MXFP4 out) (GB/s, with rotating buffer sets
+    larger than the 256 MB Infinity Cache so that every call streams from
+    HBM).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
 """
@@ -259,6 +260,47 @@ def qknorm_metrics(steps: int, warmup: int, sets: int = 8) -> dict:
             "buffer_sets": sets}
 
 
+def act_metrics(steps: int, warmup: int, out_dtype: str = "bf16", scale_scheme: str = "row", sets: int = 2) -> dict:
+    """SiLU-and-mul on the 8192 x 14336 workload (bytes: x read once, out and scales written once)."""
+    import torch
+
+    import workloads as WL
+    from residual_add_rmsnorm_rows_amd import _lib as L
+    from tests.gpu_util import TORCH_DTYPES, to_dev
+
+    wl = WL.WORKLOADS["silu_mul_8192x14336"]
+    x0 = to_dev(WL.generate_act(wl, seed=0), wl.x_dtype)
+    quant = out_dtype in ("fp8_e4m3fn", "fp4_e2m1")
+    out_cols = wl.d // 2 if out_dtype == "fp4_e2m1" else wl.d
+    sb = SCALE_BYTES[scale_scheme](wl.d) if quant else 0
+    bufs = []
+    for i in range(sets):
+        x = x0 if i == 0 else x0.clone()
+        o = torch.empty((wl.rows, out_cols), dtype=TORCH_DTYPES[out_dtype], device="cuda")
+        sc = torch.empty((wl.rows, sb), dtype=torch.uint8, device="cuda") if quant else None
+        bufs.append((x, o, sc))
+    lib = L.lib()
+    flags = (L.DTYPE_CODES[wl.x_dtype] << L.RN_FLAGS_X_SHIFT) | (L.DTYPE_CODES[out_dtype] << L.RN_FLAGS_OUT_SHIFT)
+    flags |= L.SCALE_SCHEMES[scale_scheme] << L.RN_FLAGS_SCALE_SHIFT
+    state = {"i": 0}
+
+    def call(stream):
+        x, o, sc = bufs[state["i"]]
+        state["i"] = (state["i"] + 1) % sets
+        st = lib.silu_mul_fwd(x.data_ptr(), o.data_ptr(), None if sc is None else sc.data_ptr(), None, wl.rows,
+                              wl.d, flags, stream)
+        if st != 0:
+            L.check(st)
+
+    ms = time_stream_loop(call, steps, warmup)
+    size = {"bf16": 2, "f32": 4, "fp8_e4m3fn": 1, "fp4_e2m1": 0.5}
+    b = int(wl.rows * (2 * wl.d * size[wl.x_dtype] + wl.d * size[out_dtype] + sb))
+    return {"workload": wl.description, "out": out_dtype, "scale_scheme": scale_scheme,
+            "us_per_call": round(ms * 1000, 3), "algorithmic_bytes": b,
+            "GBps": round(b / (ms * 1e-3) / 1e9, 1), "frac_of_peak": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "buffer_sets": sets}
+
+
 def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
     """The oracle as it stands, timed on a bounded sample of the workload's rows."""
     import numpy as np
@@ -386,6 +428,10 @@ def main() -> int:
                                                         scale_scheme="mx32")
         sec["prefill_8192x7168_mxfp4"] = stream_metrics("prefill_fp8_8192x7168", args.steps, args.warmup, sets=3,
                                                         out_dtype="fp4_e2m1", scale_scheme="mx32")
+        log("silu_mul_8192x14336")
+        sec["silu_mul_8192x14336"] = act_metrics(args.steps, args.warmup)
+        sec["silu_mul_8192x14336_mxfp8"] = act_metrics(args.steps, args.warmup, "fp8_e4m3fn", "mx32")
+        sec["silu_mul_8192x14336_mxfp4"] = act_metrics(args.steps, args.warmup, "fp4_e2m1", "mx32")
         result["secondary"] = sec
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

@@ -7,7 +7,8 @@
 // half and the up projection in its second half (a merged gate/up GEMM
 // output).  silu(g) = g * sigmoid(g), evaluated in float32 as
 // g * (e / (1 + e)) for g < 0 and g / (1 + e) otherwise, with e = exp(-|g|),
-// so that no intermediate overflows.
+// so that no intermediate overflows (library exp and division for float32
+// outputs, the hardware exp2 and reciprocal for the narrower outputs).
 //
 // Same machinery as the rows kernel: one workgroup of W wave64s per row, each
 // lane holding NV steps of one 16-byte chunk of the gate and the matching
@@ -26,9 +27,26 @@ namespace {
 constexpr int act_bits(int dt) { return dt == kBF16 ? 16 : dt == kF32 ? 32 : dt == kFP8 ? 8 : 4; }
 constexpr int act_max(int a, int b) { return a > b ? a : b; }
 
+// ACCURATE (float32 outputs): library expf and an IEEE division, a few ulp of
+// float32 overall.  Otherwise (bf16 / fp8 / fp4 outputs, whose rounding step
+// is 2^-8 relative or coarser): the hardware exp2 and reciprocal
+// (v_exp_f32 with a rescale for subnormal results, v_rcp_f32), whose error
+// grows as |g| * 2^-24 relative -- far below those formats' steps -- at a
+// third of the instructions, which keeps the kernel memory-bound.
+template <bool ACCURATE>
 __device__ __forceinline__ float silu_f32(float g) {
-  const float e = expf(-__builtin_fabsf(g));  // in (0, 1]
-  const float r = 1.0f / (1.0f + e);
+  const float ng = -__builtin_fabsf(g);
+  float e, r;
+  if constexpr (ACCURATE) {
+    e = expf(ng);  // in (0, 1]
+    r = 1.0f / (1.0f + e);
+  } else {
+    // exp(ng) = 2^(ng * log2(e)); the generic exp2 keeps float32 subnormal
+    // results (the bare instruction flushes them), which a large up value can
+    // carry back into the normal range.
+    e = __builtin_exp2f(ng * 1.4426950408889634f);
+    r = __builtin_amdgcn_rcpf(1.0f + e);
+  }
   return g * (g >= 0.f ? r : e * r);
 }
 
@@ -58,7 +76,7 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void silu_mul_kernel(const 
   const char* __restrict__ xp = static_cast<const char*>(a.x);
   char* __restrict__ op = static_cast<char*>(a.out);
   const uint32_t d = static_cast<uint32_t>(a.d);
-  const uint32_t groups = QG ? d / QG : 1;
+  const uint32_t groups = d / (QG ? QG : d);  // scales per row
   constexpr int SCALE_BYTES = QS == kQMx32 ? 1 : 4;
 
   auto elem_of = [&](int s, int c) -> uint32_t {
@@ -93,7 +111,7 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void silu_mul_kernel(const 
         unpack<XD, U>(uw[s][c], u);
 #pragma unroll
         for (int i = 0; i < U; ++i) {
-          y[s][c][i] = silu_f32(g[i]) * u[i];
+          y[s][c][i] = silu_f32<OD == kF32>(g[i]) * u[i];
           if constexpr (ROW_MAX) mx = __builtin_fmaxf(mx, __builtin_fabsf(y[s][c][i]));
         }
       }

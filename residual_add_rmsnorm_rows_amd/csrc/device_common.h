@@ -1,6 +1,6 @@
 // Device-side building blocks for the gfx950 (CDNA4, wave64) kernels:
 // element codecs, 16-byte lane-vector loads/stores, DPP reductions across
-// lanes, and the fp8 E4M3FN encoder.
+// lanes, and the fp8 / fp4 conversions.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -173,41 +173,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// float32 -> OCP fp8 E4M3FN code: round to nearest even, saturate to +-448.
-// E4M3FN: bias 7, 3 fraction bits, subnormal quantum 2^-9, largest finite
-// 1.75 * 2^8 = 448 (code 0x7E); 0x7F is NaN, so rounding past 448 clamps.
-__device__ __forceinline__ uint32_t e4m3fn_code(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = __builtin_fabsf(v);
-  uint32_t mag;
-  if (a < 0.015625f) {
-    // below 2^-6: a multiple of 2^-9 (v_rndne_f32 rounds to nearest even);
-    // a result of 8 is code 0x08, the smallest normal, as it should be.
-    mag = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
-  } else {
-    // keep 3 fraction bits with round to nearest even, then rebias the
-    // exponent from 127 to 7: ((e + 127) << 3 | m) - (120 << 3).
-    uint32_t u = __float_as_uint(a);
-    u += 0x7FFFFu + ((u >> 20) & 1u);
-    mag = (u >> 20) - (120u << 3);
-    mag = mag > 0x7Eu ? 0x7Eu : mag;
-  }
-  return sign | mag;
+// float32 -> OCP fp8 E4M3FN (bias 7, 3 fraction bits, largest finite 448 =
+// code 0x7E) and OCP MX fp4 E2M1 (values 0, 0.5, 1, 1.5, 2, 3, 4, 6) use the
+// gfx950 conversion instructions, two elements per instruction, first operand
+// in the low byte / low nibble.  Both round to nearest even.  The fp8
+// conversion turns magnitudes past the format into NaN (0x7F), so values are
+// first clamped to +-448 (v_med3), which makes it the saturating conversion;
+// the fp4 conversion saturates at 6 by itself.  On MI355X both matched an
+// encoder written from the format definitions bit for bit on every code, on
+// every midpoint between neighbouring codes and its float32 neighbours, on
+// out-of-range values and on 400k random values.
+template <int BYTE>
+__device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t old, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, BYTE);
 }
 
-// float32 -> OCP fp4 E2M1 code (values 0, 0.5, 1, 1.5, 2, 3, 4, 6): round to
-// nearest with ties to the even code, saturate to 6.  The magnitude code is
-// the number of decision points at or below |v|; the decision points are the
-// midpoints between neighbouring values, each taken as "above" when the even
-// neighbour is the upper one (0.75, 1.75, 3.5) and "strictly above" otherwise.
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 28) & 0x8u;
-  const float a = __builtin_fabsf(v);
-  const uint32_t mag = static_cast<uint32_t>(a > 0.25f) + static_cast<uint32_t>(a >= 0.75f) +
-                       static_cast<uint32_t>(a > 1.25f) + static_cast<uint32_t>(a >= 1.75f) +
-                       static_cast<uint32_t>(a > 2.5f) + static_cast<uint32_t>(a >= 3.5f) +
-                       static_cast<uint32_t>(a > 5.0f);
-  return sign | mag;
+template <bool HIGH_HALF>
+__device__ __forceinline__ uint32_t cvt_fp8x2(float a, float b, uint32_t old) {
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, static_cast<int>(old), HIGH_HALF));
 }
 
 // Unpack a lane vector of VEC elements of dtype DT to floats.
@@ -241,16 +226,19 @@ __device__ __forceinline__ void pack(const float (&f)[VEC], uint32_t (&w)[words_
     static_assert(VEC % 4 == 0, "fp8 lane vectors are whole dwords");
 #pragma unroll
     for (int i = 0; i < VEC / 4; ++i) {
-      w[i] = e4m3fn_code(f[4 * i]) | (e4m3fn_code(f[4 * i + 1]) << 8) |
-             (e4m3fn_code(f[4 * i + 2]) << 16) | (e4m3fn_code(f[4 * i + 3]) << 24);
+      const uint32_t lo = cvt_fp8x2<false>(f[4 * i], f[4 * i + 1], 0u);
+      w[i] = cvt_fp8x2<true>(f[4 * i + 2], f[4 * i + 3], lo);
     }
   } else {
     static_assert(DT == kFP4, "outputs are bf16, f32, fp8 or fp4");
-    static_assert(VEC % 4 == 0, "fp4 lane vectors are whole 16-bit halves");
-#pragma unroll
-    for (int j = 0; j < words_for<DT, VEC>(); ++j) w[j] = 0;
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) w[i / 8] |= e2m1_code(f[i]) << (4 * (i % 8));
+    static_assert(VEC == 4 || VEC == 8, "fp4 lane vectors are 16 or 32 bits");
+    uint32_t word = cvt_fp4x2<0>(0u, f[0], f[1]);
+    word = cvt_fp4x2<1>(word, f[2], f[3]);
+    if constexpr (VEC == 8) {
+      word = cvt_fp4x2<2>(word, f[4], f[5]);
+      word = cvt_fp4x2<3>(word, f[6], f[7]);
+    }
+    w[0] = word;
   }
 }
 

@@ -102,7 +102,7 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowA
   char* __restrict__ op = static_cast<char*>(a.out);
   char* __restrict__ rop = static_cast<char*>(a.res_out);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, static_cast<uint32_t>(a.hidden) * WB);
-  const uint32_t groups = QG ? static_cast<uint32_t>(a.hidden) / QG : 1;  // scales per row
+  const uint32_t groups = static_cast<uint32_t>(a.hidden) / (QG ? QG : a.hidden);  // scales per row
   constexpr int SCALE_BYTES = QS == kQMx32 ? 1 : 4;
 
   // Element offset of chunk (s, c) of this lane from the row start:
