@@ -83,7 +83,18 @@ def read_traffic(workload: str):
         return None
 
 
+def attach_traffic(name: str, entry: dict) -> None:
+    """Add the counter-measured HBM bytes per launch of a secondary workload
+    (null where no summary of the current sources exists)."""
+    t = read_traffic(name)
+    entry["traffic_bytes"] = t
+    entry["traffic_over_algorithmic"] = None if t is None else round(t / entry["algorithmic_bytes"], 4)
+
+
 SCALE_BYTES = {"row": lambda h: 4, "group128": lambda h: 4 * (h // 128), "mx32": lambda h: h // 32}
+SCHEME_TEXT = {"row": "a float32 scale amax/448 per row", "group128": "a float32 scale per 128 elements",
+               "mx32": "an E8M0 scale per 32 elements (MX)"}
+QUANT_TEXT = {"fp8_e4m3fn": "fp8 e4m3fn", "fp4_e2m1": "fp4 e2m1"}
 
 
 def rownorm_bytes(wl, rows=None, scale_scheme: str = "row") -> int:
@@ -223,7 +234,11 @@ def stream_metrics(name: str, steps: int, warmup: int, sets: int, out_dtype=None
     call = RowCall(wl, WL.generate_rownorm(wl, seed=0), sets=sets, scale_scheme=scale_scheme)
     ms = time_stream_loop(call, steps, warmup)
     b = rownorm_bytes(wl, scale_scheme=scale_scheme)
-    return {"workload": wl.description, "out": wl.out_dtype, "scale_scheme": scale_scheme,
+    desc = wl.description
+    if wl.out_dtype in QUANT_TEXT:
+        desc = (f"prefill fused add+RMSNorm, {wl.rows} x {wl.hidden} {wl.x_dtype} x and residual "
+                f"(1% outliers x20), {QUANT_TEXT[wl.out_dtype]} out with {SCHEME_TEXT[scale_scheme]}")
+    return {"workload": desc, "out": wl.out_dtype, "scale_scheme": scale_scheme,
             "us_per_call": round(ms * 1000, 3), "algorithmic_bytes": b,
             "GBps": round(b / (ms * 1e-3) / 1e9, 1), "frac_of_peak": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "buffer_sets": sets}
@@ -295,7 +310,11 @@ def act_metrics(steps: int, warmup: int, out_dtype: str = "bf16", scale_scheme: 
     ms = time_stream_loop(call, steps, warmup)
     size = {"bf16": 2, "f32": 4, "fp8_e4m3fn": 1, "fp4_e2m1": 0.5}
     b = int(wl.rows * (2 * wl.d * size[wl.x_dtype] + wl.d * size[out_dtype] + sb))
-    return {"workload": wl.description, "out": out_dtype, "scale_scheme": scale_scheme,
+    desc = wl.description
+    if quant:
+        desc = (f"SwiGLU silu(gate) * up, {wl.rows} tokens, merged gate/up projection 2 x {wl.d} {wl.x_dtype} "
+                f"~ N(0,1), {QUANT_TEXT[out_dtype]} out with {SCHEME_TEXT[scale_scheme]}")
+    return {"workload": desc, "out": out_dtype, "scale_scheme": scale_scheme,
             "us_per_call": round(ms * 1000, 3), "algorithmic_bytes": b,
             "GBps": round(b / (ms * 1e-3) / 1e9, 1), "frac_of_peak": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "buffer_sets": sets}
@@ -342,6 +361,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode latency lines (thousands of tiny launches; for counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of 1 GiB (torch copy_), the reference for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -414,7 +435,7 @@ def main() -> int:
         torch.cuda.empty_cache()
     if not args.no_secondary:
         sec = {}
-        for name in ("decode_8x1024", "decode_256x4096"):
+        for name in () if args.no_decode else ("decode_8x1024", "decode_256x4096"):
             log(f"decode {name}")
             sec[name] = decode_metrics(name)
         log("qknorm_4096x32x128")
@@ -432,6 +453,9 @@ def main() -> int:
         sec["silu_mul_8192x14336"] = act_metrics(args.steps, args.warmup)
         sec["silu_mul_8192x14336_mxfp8"] = act_metrics(args.steps, args.warmup, "fp8_e4m3fn", "mx32")
         sec["silu_mul_8192x14336_mxfp4"] = act_metrics(args.steps, args.warmup, "fp4_e2m1", "mx32")
+        for name, entry in sec.items():
+            if "GBps" in entry:
+                attach_traffic(name, entry)
         result["secondary"] = sec
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

@@ -14,7 +14,7 @@ Two summaries:
 Usage:
   python -m residual_add_rmsnorm_rows_amd.rocprof_summary stats CSV --command CMD --out FILE
   python -m residual_add_rmsnorm_rows_amd.rocprof_summary traffic --fetch CSV --write CSV \\
-      --kernel SUBSTR --bench-out FILE --command CMD --out FILE
+      --kernel SUBSTR --bench-out FILE --command CMD --out FILE [--entry SECONDARY_NAME]
 """
 
 from __future__ import annotations
@@ -54,12 +54,16 @@ def _counter(rows, counter: str, match) -> List[float]:
     return [float(r["Counter_Value"]) for r in rows if r["Counter_Name"] == counter and match(r)]
 
 
-def _copy_rows(rows):
-    copies = [r for r in rows if r["Kernel_Name"] == COPY_KERNEL]
+def _copy_rows(rows, counter: str):
+    """The calibration copies: the runtime copy kernel's dispatches with the
+    largest reading (the 1 GiB copies are the largest copies the benchmark
+    makes; its other copies, e.g. tensor clones, share the same grid)."""
+    copies = [r for r in rows if r["Kernel_Name"] == COPY_KERNEL and r["Counter_Name"] == counter]
     if not copies:
         raise SystemExit("no copy-calibration dispatches in the counter file")
-    big = max(int(r["Grid_Size"]) for r in copies)
-    return lambda r: r["Kernel_Name"] == COPY_KERNEL and int(r["Grid_Size"]) == big
+    top = max(float(r["Counter_Value"]) for r in copies)
+    ids = {r["Dispatch_Id"] for r in copies if float(r["Counter_Value"]) >= 0.99 * top}
+    return lambda r: r["Kernel_Name"] == COPY_KERNEL and r["Dispatch_Id"] in ids
 
 
 def _last_json(path: str) -> dict:
@@ -70,7 +74,7 @@ def _last_json(path: str) -> dict:
     return json.loads(lines[-1])
 
 
-def traffic(fetch_csv: str, write_csv: str, kernel: str, bench_out: str, command: str) -> str:
+def traffic(fetch_csv: str, write_csv: str, kernel: str, bench_out: str, command: str, entry: str = "") -> str:
     fr, wr = _rows(fetch_csv), _rows(write_csv)
     names = sorted({r["Kernel_Name"] for r in fr + wr if kernel in r["Kernel_Name"]})
     if len(names) != 1:
@@ -78,25 +82,31 @@ def traffic(fetch_csv: str, write_csv: str, kernel: str, bench_out: str, command
     main = lambda r: r["Kernel_Name"] == names[0]  # noqa: E731
     fetch_k = _counter(fr, "FETCH_SIZE", main)
     write_k = _counter(wr, "WRITE_SIZE", main)
-    cf = _counter(fr, "FETCH_SIZE", _copy_rows(fr))
-    cw = _counter(wr, "WRITE_SIZE", _copy_rows(wr))
+    cf = _counter(fr, "FETCH_SIZE", _copy_rows(fr, "FETCH_SIZE"))
+    cw = _counter(wr, "WRITE_SIZE", _copy_rows(wr, "WRITE_SIZE"))
     fetch_factor = COPY_BYTES / (statistics.mean(cf) * 1024)
     write_factor = COPY_BYTES / (statistics.mean(cw) * 1024)
     fetch_b = statistics.mean(fetch_k) * 1024 * fetch_factor
     write_b = statistics.mean(write_k) * 1024 * write_factor
     bench = _last_json(bench_out)
-    alg = bench["config"]["algorithmic_bytes_per_step"]
+    if entry:  # a secondary workload of the benchmark
+        alg = bench["secondary"][entry]["algorithmic_bytes"]
+        workload = f"{entry}: {bench['secondary'][entry]['workload']}"
+    else:
+        alg = bench["config"]["algorithmic_bytes_per_step"]
+        workload = bench["config"]["workload"]
     lines = [
         "# HBM traffic per launch from rocprofv3 counters (FETCH_SIZE and WRITE_SIZE runs),",
         "# each scaled by the same counter's reading for a 1 GiB device copy in the same run.",
         f"# command (FETCH_SIZE; the WRITE_SIZE run differs only in the counter): {command}",
         f"kernel: {names[0]}",
-        f"workload: {bench['config']['workload']}",
+        f"workload: {workload}",
         f"source_sha256: {bench['config']['source_sha256']}",
         f"dispatches_fetch: {len(fetch_k)}",
         f"dispatches_write: {len(write_k)}",
         f"fetch_size_kib_per_dispatch: {statistics.mean(fetch_k):.1f}",
         f"write_size_kib_per_dispatch: {statistics.mean(write_k):.1f}",
+        f"copy_dispatches: {len(cf)} fetch, {len(cw)} write",
         f"copy_fetch_size_kib_per_GiB: {statistics.mean(cf):.1f}",
         f"copy_write_size_kib_per_GiB: {statistics.mean(cw):.1f}",
         f"fetch_scale: {fetch_factor:.4f}",
@@ -125,9 +135,10 @@ def main(argv=None) -> int:
     t.add_argument("--bench-out", required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--out", required=True)
+    t.add_argument("--entry", default="", help="secondary workload of the benchmark line (default: the main one)")
     a = ap.parse_args(argv)
     text = stats(a.csv, a.command, a.note) if a.what == "stats" else traffic(a.fetch, a.write, a.kernel, a.bench_out,
-                                                                        a.command)
+                                                                        a.command, a.entry)
     with open(a.out, "w") as f:
         f.write(text)
     print(text)
