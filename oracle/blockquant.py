@@ -19,13 +19,22 @@ public format specifications, and the readings are stated per function:
     nearest to v / X (ties to even), values past the element format's largest
     normal saturating to it.  Reading for blocks the specification leaves
     open: an all-zero block gets the smallest scale (E8M0 code 0, 2^-127) and
-    zero codes, and the shared exponent is clamped to E8M0's range [-127, 127].
+    zero codes, and the shared exponent is clamped to E8M0's range [-127, 127];
+  * NVFP4 (the same section: an absolute maximum over 16 elements): E2M1
+    elements, one FP8 E4M3FN scale per block of 16 and one float32 scale per
+    tensor, supplied by the caller.  Reading: the two scales together map the
+    block's maximum onto E2M1's largest value 6, so the block scale is the
+    E4M3FN rounding of ``amax_b / (6 s_t)`` and the elements are the E2M1
+    roundings of ``y / (s_b s_t)``.
 
-Pins (tests/test_oracle_blockquant.py): the E2M1 and E8M0 value tables of the
-MX specification (tests/golden/mx_landmarks.txt), brute-force nearest-value
-rounding for E2M1, closed forms for power-of-two block maxima, the top-binade
-invariant, format error bounds, and per-group fp8 with one group per row
-equal to the (separately pinned) per-row scheme.
+Pins (tests/test_oracle_blockquant.py, tests/test_oracle_nvfp4.py): the E2M1
+and E8M0 value tables of the MX specification (tests/golden/mx_landmarks.txt),
+brute-force nearest-value rounding for E2M1, closed forms for power-of-two
+block maxima, the top-binade invariant, format error bounds, and per-group
+fp8 with one group per row equal to the (separately pinned) per-row scheme;
+for NVFP4, block maxima that are exact multiples of E4M3FN values, the error
+bounds of both roundings, zero, underflowing and saturating block scales,
+power-of-two invariance, and planted mistakes that each fail a pin.
 """
 
 from __future__ import annotations
@@ -34,7 +43,7 @@ from typing import Dict, Optional
 
 import numpy as np
 
-from .rownorm import Format, e4m3fn_encode, fp8_scale_from_amax, round_to_format
+from .rownorm import Format, e4m3fn_decode, e4m3fn_encode, fp8_scale_from_amax, round_to_format
 
 __all__ = [
     "E2M1",
@@ -44,6 +53,7 @@ __all__ = [
     "e8m0_decode",
     "fp8_quantize_groups",
     "mx_quantize",
+    "nvfp4_quantize",
     "pack_fp4",
     "unpack_fp4",
 ]
@@ -154,3 +164,34 @@ def mx_quantize(y: np.ndarray, elem: str, block: int = 32, shared_exp: Optional[
     codes = e4m3fn_encode(scaled) if elem == "fp8_e4m3fn" else e2m1_encode(scaled)
     return {"amax": amax, "shared_exp": own, "scale_codes": (own + 127).astype(np.uint8),
             "codes": codes.reshape(np.asarray(y).shape)}
+
+
+def nvfp4_quantize(y: np.ndarray, tensor_scale: float, block: int = 16,
+                   scale_codes: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """NVFP4 quantization of rows ``y`` [rows, H] with the per-tensor scale ``tensor_scale``.
+
+    For each block of ``block`` consecutive elements: ``amax_b = max |y|``,
+    block scale code ``s_b = RNE_e4m3fn(amax_b / (6 * s_t))`` (saturating at
+    448), element codes ``RNE_e2m1(y / (decode(s_b) * s_t))`` (saturating at
+    6); a block scale that rounds to zero gives zero codes.  ``s_t`` is used
+    as the exact value of the float32 the caller passes.  When
+    ``scale_codes`` is given it is used for the element codes (to judge codes
+    against the block scales another implementation chose).  Both quotients
+    are rounded once to double and then to the narrow format; a double
+    rounding would need the double quotient to fall on a narrow-format
+    midpoint that the exact quotient misses, which the 5- and 3-bit grids make
+    vanishingly rare.  Returns amax [rows, H/block], scale_codes (uint8 E4M3FN,
+    same shape) and codes [rows, H] (4-bit codes, unpacked).
+    """
+    st = float(np.float32(tensor_scale))
+    if not (np.isfinite(st) and st > 0):
+        raise ValueError("tensor_scale must be a positive finite float32")
+    b = _blocks(y, block)
+    amax = np.max(np.abs(b), axis=2)
+    own = e4m3fn_encode(amax / (6.0 * st))
+    sc = own if scale_codes is None else np.asarray(scale_codes, dtype=np.uint8)
+    d = e4m3fn_decode(sc) * st
+    safe = np.where(d > 0, d, 1.0)
+    codes = e2m1_encode(b / safe[:, :, None])
+    codes[d == 0] = 0
+    return {"amax": amax, "scale_codes": own, "codes": codes.reshape(np.asarray(y).shape)}
