@@ -91,9 +91,14 @@ def attach_traffic(name: str, entry: dict) -> None:
     entry["traffic_over_algorithmic"] = None if t is None else round(t / entry["algorithmic_bytes"], 4)
 
 
-SCALE_BYTES = {"row": lambda h: 4, "group128": lambda h: 4 * (h // 128), "mx32": lambda h: h // 32}
+SCALE_BYTES = {"row": lambda h: 4, "group128": lambda h: 4 * (h // 128), "mx32": lambda h: h // 32,
+               "nv16": lambda h: h // 16}
 SCHEME_TEXT = {"row": "a float32 scale amax/448 per row", "group128": "a float32 scale per 128 elements",
-               "mx32": "an E8M0 scale per 32 elements (MX)"}
+               "mx32": "an E8M0 scale per 32 elements (MX)",
+               "nv16": "an E4M3FN scale per 16 elements and a float32 tensor scale (NVFP4)"}
+# NVFP4 tensor scales: fixed values near amax / (6 * 448) of each workload's
+# outputs (any positive value is a valid input; the traffic does not depend on it).
+NV_TENSOR_SCALE = {"prefill_fp8_8192x7168": 2.0 ** -5, "silu_mul_8192x14336": 2.0 ** -7}
 QUANT_TEXT = {"fp8_e4m3fn": "fp8 e4m3fn", "fp4_e2m1": "fp4 e2m1"}
 
 
@@ -141,15 +146,18 @@ class RowCall:
             self.sets.append((xs, rs, out, ro, sc))
         self.flags = L.make_flags(wl.x_dtype, wl.res_dtype, wl.w_dtype, wl.out_dtype, wl.weight_plus_one,
                                   scale_scheme)
+        self.ts = (torch.tensor([NV_TENSOR_SCALE[wl.name]], dtype=torch.float32, device="cuda")
+                   if scale_scheme == "nv16" else None)
         self.i = 0
 
     def __call__(self, stream: int) -> None:
         xs, rs, out, ro, sc = self.sets[self.i]
         self.i = (self.i + 1) % len(self.sets)
-        st = self.L.rmsnorm_fwd(xs.data_ptr(), None if rs is None else rs.data_ptr(), self.w.data_ptr(),
-                                out.data_ptr(), None if ro is None else ro.data_ptr(),
-                                None if sc is None else sc.data_ptr(), self.wl.rows, self.wl.hidden,
-                                self.wl.eps, self.flags, stream)
+        st = self.L.rmsnorm_fwd_ex(xs.data_ptr(), None if rs is None else rs.data_ptr(), self.w.data_ptr(),
+                                   out.data_ptr(), None if ro is None else ro.data_ptr(),
+                                   None if sc is None else sc.data_ptr(), None,
+                                   None if self.ts is None else self.ts.data_ptr(), self.wl.rows, self.wl.hidden,
+                                   self.wl.eps, self.flags, stream)
         if st != 0:
             from residual_add_rmsnorm_rows_amd._lib import check
             check(st)
@@ -297,13 +305,16 @@ def act_metrics(steps: int, warmup: int, out_dtype: str = "bf16", scale_scheme: 
     lib = L.lib()
     flags = (L.DTYPE_CODES[wl.x_dtype] << L.RN_FLAGS_X_SHIFT) | (L.DTYPE_CODES[out_dtype] << L.RN_FLAGS_OUT_SHIFT)
     flags |= L.SCALE_SCHEMES[scale_scheme] << L.RN_FLAGS_SCALE_SHIFT
+    ts_t = (torch.tensor([NV_TENSOR_SCALE[wl.name]], dtype=torch.float32, device="cuda")
+            if scale_scheme == "nv16" else None)
+    ts = None if ts_t is None else ts_t.data_ptr()
     state = {"i": 0}
 
     def call(stream):
         x, o, sc = bufs[state["i"]]
         state["i"] = (state["i"] + 1) % sets
-        st = lib.silu_mul_fwd(x.data_ptr(), o.data_ptr(), None if sc is None else sc.data_ptr(), None, wl.rows,
-                              wl.d, flags, stream)
+        st = lib.silu_mul_fwd(x.data_ptr(), o.data_ptr(), None if sc is None else sc.data_ptr(), None, ts,
+                              wl.rows, wl.d, flags, stream)
         if st != 0:
             L.check(st)
 
@@ -449,10 +460,13 @@ def main() -> int:
                                                         scale_scheme="mx32")
         sec["prefill_8192x7168_mxfp4"] = stream_metrics("prefill_fp8_8192x7168", args.steps, args.warmup, sets=3,
                                                         out_dtype="fp4_e2m1", scale_scheme="mx32")
+        sec["prefill_8192x7168_nvfp4"] = stream_metrics("prefill_fp8_8192x7168", args.steps, args.warmup, sets=3,
+                                                        out_dtype="fp4_e2m1", scale_scheme="nv16")
         log("silu_mul_8192x14336")
         sec["silu_mul_8192x14336"] = act_metrics(args.steps, args.warmup)
         sec["silu_mul_8192x14336_mxfp8"] = act_metrics(args.steps, args.warmup, "fp8_e4m3fn", "mx32")
         sec["silu_mul_8192x14336_mxfp4"] = act_metrics(args.steps, args.warmup, "fp4_e2m1", "mx32")
+        sec["silu_mul_8192x14336_nvfp4"] = act_metrics(args.steps, args.warmup, "fp4_e2m1", "nv16")
         for name, entry in sec.items():
             if "GBps" in entry:
                 attach_traffic(name, entry)

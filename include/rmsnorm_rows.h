@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define RN_ABI_VERSION 1
+#define RN_ABI_VERSION 2
 
 typedef enum rn_status {
   RN_OK = 0,
@@ -72,10 +72,10 @@ typedef enum rn_status {
 #define RN_DTYPE_F32 1u        /* IEEE binary32 */
 #define RN_DTYPE_FP8_E4M3FN 2u /* OCP fp8 E4M3FN, outputs only, with scales (see RN_SCALE_*) */
 #define RN_DTYPE_FP4_E2M1 3u   /* OCP MX fp4 E2M1, outputs only, two codes per byte (element 2k
-                                  in the low nibble), with MX scales */
+                                  in the low nibble), with MX or NVFP4 scales */
 
 /* Scale granularity of a quantized output (flags bits 9-10), after the
- * block-scaled schemes of the "Blackwell support" section (MXFP8, MXFP4, FP8
+ * block-scaled schemes of the "Blackwell support" section (MXFP8, MXFP4, NVFP4, FP8
  * block-wise scaling), with the formats of the OCP FP8 and MX specifications:
  *   RN_SCALE_ROW       fp8: one float32 scale amax/448 per row, amax = max|y| of the row
  *   RN_SCALE_GROUP128  fp8: one float32 scale amax/448 per 128 consecutive elements
@@ -84,10 +84,19 @@ typedef enum rn_status {
  *                      == 0) holding e + 127 with e = clamp(floor(log2 amax) - emax, -127,
  *                      127), emax = 8 (fp8) or 2 (fp4); codes encode y * 2^-e with
  *                      saturation; an all-zero block has e = -127
+ *   RN_SCALE_NV16      fp4 only (NVFP4, named with its absolute maximum over 16 elements in
+ *                      the same section): one OCP E4M3FN byte per 16 consecutive elements
+ *                      (hidden % 16 == 0) and a float32 tensor scale s_t > 0 supplied by the
+ *                      caller (tensor_scale, device memory).  Reading: block scale code
+ *                      s_b = e4m3fn(amax / (6 s_t)) -- float32 division by fl32(6 s_t),
+ *                      then nearest-even, saturating at 448 -- and element codes
+ *                      e2m1(y * (1 / fl32(value(s_b) * s_t))); a block scale of 0 gives zero
+ *                      codes.  Dequantize as value(code) * value(s_b) * s_t.
  * Codes round to nearest, ties to even, and saturate at the format's largest value. */
 #define RN_SCALE_ROW 0u
 #define RN_SCALE_GROUP128 1u
 #define RN_SCALE_MX32 2u
+#define RN_SCALE_NV16 3u
 
 /* flags: bits 0-1 dtype of x, bits 2-3 dtype of residual and residual_out,
  * bits 4-5 dtype of weight, bits 6-7 dtype of out, bit 8 weight form (1 + w),
@@ -133,15 +142,18 @@ typedef struct rn_launch_config {
  *                byte (hidden / 2 bytes per row)                      (write)
  *   residual_out [rows, hidden] of dtype flags.res; must be NULL iff residual is NULL (write)
  *   out_scale    quantized output only (else NULL): float32 [rows] (RN_SCALE_ROW),
- *                float32 [rows, hidden/128] (RN_SCALE_GROUP128) or uint8 E8M0
- *                [rows, hidden/32] (RN_SCALE_MX32)                     (write)
+ *                float32 [rows, hidden/128] (RN_SCALE_GROUP128), uint8 E8M0
+ *                [rows, hidden/32] (RN_SCALE_MX32) or uint8 E4M3FN [rows, hidden/16]
+ *                (RN_SCALE_NV16)                                       (write)
  *   rows         >= 0;  hidden >= 1, a multiple of the lane vector (8 for bf16 x,
  *                4 for f32 x) and at most 32768 (bf16 x) / 16384 (f32 x): the
  *                whole row is held in registers, 4096 lane vectors at most
  *   eps          finite, >= 0, used as given (a float32)
  *   flags        RN_MAKE_FLAGS(...) | (scale << RN_FLAGS_SCALE_SHIFT); x is bf16 or f32;
  *                the residual dtype is the x dtype or f32; weight bf16 or f32; out bf16,
- *                f32, fp8 (any scale granularity) or fp4 (RN_SCALE_MX32 only).
+ *                f32, fp8 (row, per-128 or MX scales) or fp4 (MX or NVFP4 scales).
+ *                RN_SCALE_NV16 needs rmsnorm_fwd_ex's tensor_scale: rmsnorm_fwd
+ *                rejects it with RN_ERR_INVALID_ARG.
  *
  * Residual reading (not on the pages): h = x + residual is rounded once to the
  * residual dtype, written to residual_out, and normalized; out == RMSNorm(h).
@@ -157,10 +169,13 @@ rn_status rmsnorm_fwd(const void* x, const void* residual, const void* weight, v
 
 /* As rmsnorm_fwd; for a quantized output, out_amax (may be NULL) also receives
  * the float32 amax from which each scale was computed (one per row, group or
- * block, laid out like the scales).  out_amax must be NULL for other outputs. */
+ * block, laid out like the scales).  out_amax must be NULL for other outputs.
+ * tensor_scale: RN_SCALE_NV16 only (else NULL), a device pointer to one
+ * float32, the per-tensor scale s_t, read by the kernel (4-byte aligned; it
+ * should be positive and finite: other values give unspecified codes). */
 rn_status rmsnorm_fwd_ex(const void* x, const void* residual, const void* weight, void* out,
-                         void* residual_out, void* out_scale, float* out_amax, int64_t rows,
-                         int64_t hidden, float eps, uint32_t flags, void* stream);
+                         void* residual_out, void* out_scale, float* out_amax, const float* tensor_scale,
+                         int64_t rows, int64_t hidden, float eps, uint32_t flags, void* stream);
 
 /* As rmsnorm_fwd_ex, with an explicit launch configuration instead of the
  * selector's (for tuning and for testing every kernel variant).  cfg->kernel
@@ -168,9 +183,9 @@ rn_status rmsnorm_fwd_ex(const void* x, const void* residual, const void* weight
  * 64 * waves_per_row * vecs_per_lane * vec >= hidden, 1 <= grid <= rows;
  * block_threads, lanes_per_row and rows_per_lane are derived and ignored. */
 rn_status rmsnorm_fwd_config(const void* x, const void* residual, const void* weight, void* out,
-                             void* residual_out, void* out_scale, float* out_amax, int64_t rows,
-                             int64_t hidden, float eps, uint32_t flags,
-                             const rn_launch_config* cfg, void* stream);
+                             void* residual_out, void* out_scale, float* out_amax,
+                             const float* tensor_scale, int64_t rows, int64_t hidden, float eps,
+                             uint32_t flags, const rn_launch_config* cfg, void* stream);
 
 /*
  * Per-head RMSNorm of Q and K ("CuTeDSL at Perplexity", section "QK Norm").
@@ -216,16 +231,18 @@ rn_status qknorm_fwd_config(const void* q, const void* k, const void* q_weight, 
  *   out        [rows, d] of dtype flags.out (bf16, f32, fp8; fp4: d / 2 bytes per row) (write)
  *   out_scale  quantized output only, laid out as for rmsnorm_fwd    (write)
  *   out_amax   quantized output only, may be NULL                    (write)
+ *   tensor_scale  RN_SCALE_NV16 only (else NULL): device float32 s_t, as for rmsnorm_fwd_ex
  *   rows >= 0; d >= 1, a multiple of the 16-byte vector of x and at most 32768 (bf16) /
  *   16384 (f32); flags: bits 0-1 x dtype, bits 6-7 out dtype, bits 9-10 scale granularity
  *   (as for rmsnorm_fwd); other bits must be zero.  out may not overlap x.
  */
-rn_status silu_mul_fwd(const void* x, void* out, void* out_scale, float* out_amax, int64_t rows,
-                       int64_t d, uint32_t flags, void* stream);
+rn_status silu_mul_fwd(const void* x, void* out, void* out_scale, float* out_amax, const float* tensor_scale,
+                       int64_t rows, int64_t d, uint32_t flags, void* stream);
 
 /* As silu_mul_fwd with an explicit launch configuration (as rmsnorm_fwd_config). */
-rn_status silu_mul_fwd_config(const void* x, void* out, void* out_scale, float* out_amax, int64_t rows,
-                              int64_t d, uint32_t flags, const rn_launch_config* cfg, void* stream);
+rn_status silu_mul_fwd_config(const void* x, void* out, void* out_scale, float* out_amax,
+                              const float* tensor_scale, int64_t rows, int64_t d, uint32_t flags,
+                              const rn_launch_config* cfg, void* stream);
 
 /* Host-only: the launch configuration silu_mul_fwd would use. */
 rn_status silu_mul_query_config(int64_t rows, int64_t d, uint32_t flags, int32_t num_cus,

@@ -33,14 +33,17 @@ __all__ = [
 
 _NAMES = {torch.bfloat16: "bf16", torch.float32: "f32", torch.float8_e4m3fn: "fp8_e4m3fn",
           torch.float4_e2m1fn_x2: "fp4_e2m1"}
-_GROUP = {"row": None, "group128": 128, "mx32": 32}
+_GROUP = {"row": None, "group128": 128, "mx32": 32, "nv16": 16}
+_SCALE_DTYPE = {"row": torch.float32, "group128": torch.float32, "mx32": torch.float8_e8m0fnu,
+                "nv16": torch.float8_e4m3fn}
 _TORCH = {v: k for k, v in _NAMES.items()}
 
 
 class NormOutput(NamedTuple):
     out: torch.Tensor
     residual_out: Optional[torch.Tensor]
-    scale: Optional[torch.Tensor]  # quantized output: float32 [rows] / [rows, H/128], or E8M0 [rows, H/32]
+    scale: Optional[torch.Tensor]  # quantized output: float32 [rows] / [rows, H/128], E8M0 [rows, H/32]
+                                   # or E4M3FN [rows, H/16] (NVFP4)
     amax: Optional[torch.Tensor]   # quantized output when requested: float32, one per scale
 
 
@@ -67,11 +70,39 @@ def _p(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
 
+def _quant_buffers(od: str, scale_scheme: str, rows: int, n: int, device: torch.device, return_amax: bool,
+                   tensor_scale) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor], Optional[torch.Tensor]]:
+    """Scale (and amax) outputs of a quantized output, and the NVFP4 tensor scale
+    as a one-element float32 device tensor."""
+    if scale_scheme not in _GROUP:
+        raise ValueError(f"scale_scheme must be one of {sorted(_GROUP)}")
+    if (scale_scheme == "nv16") != (tensor_scale is not None):
+        raise ValueError("tensor_scale is given exactly for scale_scheme='nv16'")
+    ts = None
+    if tensor_scale is not None:
+        if isinstance(tensor_scale, torch.Tensor):
+            _dev_tensor(tensor_scale, "tensor_scale", device)
+            if tensor_scale.dtype != torch.float32 or tensor_scale.numel() != 1:
+                raise ValueError("tensor_scale must be a one-element float32 tensor")
+            ts = tensor_scale
+        else:
+            ts = torch.tensor([float(tensor_scale)], dtype=torch.float32, device=device)
+    scale = amax = None
+    if od in ("fp8_e4m3fn", "fp4_e2m1"):
+        g = _GROUP[scale_scheme]
+        nscale = (rows,) if g is None else (rows, n // g if n % g == 0 else 0)
+        scale = torch.empty(nscale, dtype=_SCALE_DTYPE[scale_scheme], device=device)
+        if return_amax:
+            amax = torch.empty(nscale, dtype=torch.float32, device=device)
+    return scale, amax, ts
+
+
 def fused_add_rmsnorm(x: torch.Tensor, residual: Optional[torch.Tensor], weight: torch.Tensor,
                       eps: float, *, weight_plus_one: bool = False,
                       out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
                       residual_out: Optional[torch.Tensor] = None, return_amax: bool = False,
-                      scale_scheme: str = "row", config: Optional[LaunchConfig] = None) -> NormOutput:
+                      scale_scheme: str = "row", tensor_scale=None,
+                      config: Optional[LaunchConfig] = None) -> NormOutput:
     """``residual_out = x + residual``; ``out = RMSNorm(residual_out) * (w [+ 1])``.
 
     ``x`` is [..., H] (bf16 or f32), ``residual`` the same shape (x dtype or
@@ -79,9 +110,12 @@ def fused_add_rmsnorm(x: torch.Tensor, residual: Optional[torch.Tensor], weight:
     ``torch.float8_e4m3fn`` or ``torch.float4_e2m1fn_x2`` (two codes per byte,
     [..., H/2]).  Quantized outputs carry scales per ``scale_scheme``:
     ``"row"`` (fp8; float32 [rows]), ``"group128"`` (fp8; float32
-    [rows, H/128]) or ``"mx32"`` (fp8 or fp4; E8M0 ``torch.float8_e8m0fnu``
-    [rows, H/32]).  ``out=x`` and ``residual_out=residual`` are allowed (in
-    place).  ``config`` forces a launch configuration.
+    [rows, H/128]), ``"mx32"`` (fp8 or fp4; E8M0 ``torch.float8_e8m0fnu``
+    [rows, H/32]) or ``"nv16"`` (fp4; E4M3FN ``torch.float8_e4m3fn``
+    [rows, H/16], with the per-tensor float32 ``tensor_scale``: a
+    one-element device tensor, or a number copied to the device).
+    ``out=x`` and ``residual_out=residual`` are allowed (in place).
+    ``config`` forces a launch configuration.
     """
     device = x.device
     if device.type != "cuda":
@@ -111,8 +145,6 @@ def fused_add_rmsnorm(x: torch.Tensor, residual: Optional[torch.Tensor], weight:
         _dev_tensor(out, "out", device)
         if tuple(out.shape) != tuple(out_shape) or out.dtype != od_t:
             raise ValueError("out has the wrong shape or dtype")
-    if scale_scheme not in _GROUP:
-        raise ValueError(f"scale_scheme must be one of {sorted(_GROUP)}")
     if residual is not None:
         if residual_out is None:
             residual_out = torch.empty_like(residual)
@@ -122,22 +154,15 @@ def fused_add_rmsnorm(x: torch.Tensor, residual: Optional[torch.Tensor], weight:
                 raise ValueError("residual_out must match residual's shape and dtype")
     elif residual_out is not None:
         raise ValueError("residual_out given without residual")
-    scale = amax = None
-    if od in ("fp8_e4m3fn", "fp4_e2m1"):
-        g = _GROUP[scale_scheme]
-        nscale = (rows,) if g is None else (rows, H // g if H % g == 0 else 0)
-        sdt = torch.float8_e8m0fnu if scale_scheme == "mx32" else torch.float32
-        scale = torch.empty(nscale, dtype=sdt, device=device)
-        if return_amax:
-            amax = torch.empty(nscale, dtype=torch.float32, device=device)
+    scale, amax, ts = _quant_buffers(od, scale_scheme, rows, H, device, return_amax, tensor_scale)
     flags = make_flags(xd, rd, wd, od, weight_plus_one, scale_scheme)
     L = lib()
     if config is not None:
         st = L.rmsnorm_fwd_config(_p(x), _p(residual), _p(weight), _p(out), _p(residual_out), _p(scale),
-                                  _p(amax), rows, H, eps, flags, ctypes.byref(config), _stream(device))
+                                  _p(amax), _p(ts), rows, H, eps, flags, ctypes.byref(config), _stream(device))
     else:
         st = L.rmsnorm_fwd_ex(_p(x), _p(residual), _p(weight), _p(out), _p(residual_out), _p(scale),
-                              _p(amax), rows, H, eps, flags, _stream(device))
+                              _p(amax), _p(ts), rows, H, eps, flags, _stream(device))
     check(st)
     return NormOutput(out, residual_out, scale, amax)
 
@@ -233,12 +258,13 @@ def query_qknorm_config(tokens: int, num_q_heads: int, num_k_heads: int, head_di
 
 
 def silu_mul(x: torch.Tensor, *, out_dtype: Optional[torch.dtype] = None, scale_scheme: str = "row",
-             return_amax: bool = False, out: Optional[torch.Tensor] = None,
+             return_amax: bool = False, out: Optional[torch.Tensor] = None, tensor_scale=None,
              config: Optional[LaunchConfig] = None) -> NormOutput:
     """SwiGLU: ``silu(x[..., :d]) * x[..., d:]`` for ``x`` [..., 2 d] (bf16 or f32).
 
     Outputs as for ``fused_add_rmsnorm`` (bf16, f32, fp8 e4m3fn with per-row /
-    per-128 / MX scales, fp4 e2m1 with MX scales); ``residual_out`` is None.
+    per-128 / MX scales, fp4 e2m1 with MX or NVFP4 scales); ``residual_out``
+    is None.
     """
     device = x.device
     if device.type != "cuda":
@@ -258,24 +284,15 @@ def silu_mul(x: torch.Tensor, *, out_dtype: Optional[torch.dtype] = None, scale_
         _dev_tensor(out, "out", device)
         if tuple(out.shape) != tuple(out_shape) or out.dtype != od_t:
             raise ValueError("out has the wrong shape or dtype")
-    if scale_scheme not in _GROUP:
-        raise ValueError(f"scale_scheme must be one of {sorted(_GROUP)}")
-    scale = amax = None
-    if od in ("fp8_e4m3fn", "fp4_e2m1"):
-        g = _GROUP[scale_scheme]
-        nscale = (rows,) if g is None else (rows, d // g if d % g == 0 else 0)
-        sdt = torch.float8_e8m0fnu if scale_scheme == "mx32" else torch.float32
-        scale = torch.empty(nscale, dtype=sdt, device=device)
-        if return_amax:
-            amax = torch.empty(nscale, dtype=torch.float32, device=device)
+    scale, amax, ts = _quant_buffers(od, scale_scheme, rows, d, device, return_amax, tensor_scale)
     flags = (_lib.DTYPE_CODES[xd] << _lib.RN_FLAGS_X_SHIFT) | (_lib.DTYPE_CODES[od] << _lib.RN_FLAGS_OUT_SHIFT)
     flags |= _lib.SCALE_SCHEMES[scale_scheme] << _lib.RN_FLAGS_SCALE_SHIFT
     L = lib()
     if config is not None:
-        st = L.silu_mul_fwd_config(_p(x), _p(out), _p(scale), _p(amax), rows, d, flags, ctypes.byref(config),
-                                   _stream(device))
+        st = L.silu_mul_fwd_config(_p(x), _p(out), _p(scale), _p(amax), _p(ts), rows, d, flags,
+                                   ctypes.byref(config), _stream(device))
     else:
-        st = L.silu_mul_fwd(_p(x), _p(out), _p(scale), _p(amax), rows, d, flags, _stream(device))
+        st = L.silu_mul_fwd(_p(x), _p(out), _p(scale), _p(amax), _p(ts), rows, d, flags, _stream(device))
     check(st)
     return NormOutput(out, None, scale, amax)
 

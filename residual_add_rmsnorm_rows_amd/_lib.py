@@ -31,7 +31,7 @@ RN_FLAGS_W_SHIFT = 4
 RN_FLAGS_OUT_SHIFT = 6
 RN_FLAG_WEIGHT_PLUS_ONE = 1 << 8
 RN_FLAGS_SCALE_SHIFT = 9
-SCALE_SCHEMES = {"row": 0, "group128": 1, "mx32": 2}
+SCALE_SCHEMES = {"row": 0, "group128": 1, "mx32": 2, "nv16": 3}
 
 RN_KERNEL_ROWS = 0
 RN_KERNEL_HEADS = 1
@@ -45,7 +45,7 @@ EXPORTED_SYMBOLS = (
     "rmsnorm_query_config", "qknorm_query_config", "silu_mul_fwd", "silu_mul_fwd_config",
     "silu_mul_query_config", "rn_launch_empty", "rn_status_string", "rn_last_error", "rn_abi_version",
 )
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 def make_flags(x: str, res: str | None, w: str, out: str, weight_plus_one: bool,
@@ -86,8 +86,8 @@ _fp = ctypes.POINTER(ctypes.c_float)
 
 _SIGNATURES = {
     "rmsnorm_fwd": ([_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _u32, _vp], ctypes.c_int),
-    "rmsnorm_fwd_ex": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _u32, _vp], ctypes.c_int),
-    "rmsnorm_fwd_config": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _u32,
+    "rmsnorm_fwd_ex": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _u32, _vp], ctypes.c_int),
+    "rmsnorm_fwd_config": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _u32,
                             ctypes.POINTER(LaunchConfig), _vp], ctypes.c_int),
     "qknorm_fwd": ([_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i64, _f32, _u32, _vp],
                    ctypes.c_int),
@@ -95,8 +95,8 @@ _SIGNATURES = {
                            ctypes.POINTER(LaunchConfig), _vp], ctypes.c_int),
     "rmsnorm_query_config": ([_i64, _i64, _u32, _i32, _i32, ctypes.POINTER(LaunchConfig)], ctypes.c_int),
     "qknorm_query_config": ([_i64, _i32, _i32, _i32, _u32, _i32, ctypes.POINTER(LaunchConfig)], ctypes.c_int),
-    "silu_mul_fwd": ([_vp, _vp, _vp, _vp, _i64, _i64, _u32, _vp], ctypes.c_int),
-    "silu_mul_fwd_config": ([_vp, _vp, _vp, _vp, _i64, _i64, _u32, ctypes.POINTER(LaunchConfig), _vp],
+    "silu_mul_fwd": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _u32, _vp], ctypes.c_int),
+    "silu_mul_fwd_config": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _u32, ctypes.POINTER(LaunchConfig), _vp],
                             ctypes.c_int),
     "silu_mul_query_config": ([_i64, _i64, _u32, _i32, ctypes.POINTER(LaunchConfig)], ctypes.c_int),
     "rn_launch_empty": ([_vp], ctypes.c_int),

@@ -46,7 +46,8 @@ ROW_VARIANTS = [  # (x dtype, out dtype, scale scheme, name)
     for x, xn in (("kBF16", "bf16"), ("kF32", "f32"))
     for out, on, qs, qn in (("kBF16", "bf16", "kQRow", ""), ("kF32", "f32", "kQRow", ""),
                             ("kFP8", "fp8", "kQRow", "row"), ("kFP8", "fp8", "kQGroup128", "g128"),
-                            ("kFP8", "fp8", "kQMx32", "mx"), ("kFP4", "fp4", "kQMx32", "mx"))
+                            ("kFP8", "fp8", "kQMx32", "mx"), ("kFP4", "fp4", "kQMx32", "mx"),
+                            ("kFP4", "fp4", "kQNv16", "nv"))
 ]
 
 

@@ -40,13 +40,33 @@ const void* pick_row_kernel(const RowKey& k) {
   const void* (*const pickers[])(const RowKey&) = {
       pick_row_kernel_bf16_bf16,    pick_row_kernel_bf16_f32,     pick_row_kernel_bf16_fp8_row,
       pick_row_kernel_bf16_fp8_g128, pick_row_kernel_bf16_fp8_mx, pick_row_kernel_bf16_fp4_mx,
-      pick_row_kernel_f32_bf16,     pick_row_kernel_f32_f32,      pick_row_kernel_f32_fp8_row,
-      pick_row_kernel_f32_fp8_g128, pick_row_kernel_f32_fp8_mx,   pick_row_kernel_f32_fp4_mx};
+      pick_row_kernel_bf16_fp4_nv,  pick_row_kernel_f32_bf16,     pick_row_kernel_f32_f32,
+      pick_row_kernel_f32_fp8_row,  pick_row_kernel_f32_fp8_g128, pick_row_kernel_f32_fp8_mx,
+      pick_row_kernel_f32_fp4_mx,   pick_row_kernel_f32_fp4_nv};
   for (auto p : pickers) {
     const void* f = p(k);
     if (f) return f;
   }
   return nullptr;
+}
+
+// Pointers that come with a quantized output: out_scale (required), out_amax
+// (optional) and the NVFP4 tensor scale (required for RN_SCALE_NV16, else NULL).
+rn_status check_quant_ptrs(int out, int qs, const void* out_scale, const float* out_amax,
+                           const float* tensor_scale, bool rows_nonzero) {
+  const bool quant = out == kFP8 || out == kFP4;
+  if (!quant && (out_scale != nullptr || out_amax != nullptr))
+    return fail(RN_ERR_INVALID_ARG, "out_scale / out_amax are only for fp8 / fp4 output");
+  if ((qs == kQNv16) != (tensor_scale != nullptr))
+    return fail(RN_ERR_INVALID_ARG, qs == kQNv16 ? "NVFP4 scales (RN_SCALE_NV16) need tensor_scale"
+                                                   : "tensor_scale is only for NVFP4 scales (RN_SCALE_NV16)");
+  if (!rows_nonzero) return RN_OK;
+  if (quant && out_scale == nullptr) return fail(RN_ERR_INVALID_ARG, "quantized output needs out_scale");
+  const bool byte_scales = qs == kQMx32 || qs == kQNv16;
+  if ((out_scale && !byte_scales && !aligned(out_scale, 4)) || (out_amax && !aligned(out_amax, 4)) ||
+      (tensor_scale && !aligned(tensor_scale, 4)))
+    return fail(RN_ERR_MISALIGNED, "float32 scales, out_amax and tensor_scale must be 4-byte aligned");
+  return RN_OK;
 }
 
 rn_status launch(const void* fn, int64_t grid, int block, void* args, void* stream) {
@@ -58,7 +78,7 @@ rn_status launch(const void* fn, int64_t grid, int block, void* args, void* stre
 }
 
 rn_status rows_entry(const void* x, const void* residual, const void* weight, void* out,
-                     void* residual_out, void* out_scale, float* out_amax, int64_t rows,
+                     void* residual_out, void* out_scale, float* out_amax, const float* tensor_scale, int64_t rows,
                      int64_t hidden, float eps, uint32_t flags, const rn_launch_config* explicit_cfg,
                      void* stream) {
   clear_error();
@@ -66,22 +86,20 @@ rn_status rows_entry(const void* x, const void* residual, const void* weight, vo
   rn_status st = check_row_shape(rows, hidden, flags, residual != nullptr, &key);
   if (st != RN_OK) return st;
   if (!(eps >= 0.0f) || eps == __builtin_inff()) return fail(RN_ERR_INVALID_ARG, "eps must be finite and >= 0");
-  const bool quant = key.out == kFP8 || key.out == kFP4;
-  if (!quant && (out_scale != nullptr || out_amax != nullptr))
-    return fail(RN_ERR_INVALID_ARG, "out_scale / out_amax are only for fp8 / fp4 output");
+  st = check_quant_ptrs(key.out, key.qs, out_scale, out_amax, tensor_scale, false);
+  if (st != RN_OK) return st;
   if (rows == 0) return RN_OK;
   if (x == nullptr || weight == nullptr || out == nullptr)
     return fail(RN_ERR_INVALID_ARG, "x, weight and out must not be NULL");
   if ((residual == nullptr) != (residual_out == nullptr))
     return fail(RN_ERR_INVALID_ARG, "residual and residual_out must both be given or both be NULL");
-  if (quant && out_scale == nullptr) return fail(RN_ERR_INVALID_ARG, "quantized output needs out_scale");
   if (residual_out != nullptr && residual_out == out)
     return fail(RN_ERR_INVALID_ARG, "out and residual_out must be different buffers");
   const void* ptrs16[] = {x, residual, weight, out, residual_out};
   for (const void* p : ptrs16)
     if (p != nullptr && !aligned(p, 16)) return fail(RN_ERR_MISALIGNED, "tensor pointer %p is not 16-byte aligned", p);
-  if ((out_scale && key.qs != kQMx32 && !aligned(out_scale, 4)) || (out_amax && !aligned(out_amax, 4)))
-    return fail(RN_ERR_MISALIGNED, "float32 scales / out_amax must be 4-byte aligned");
+  st = check_quant_ptrs(key.out, key.qs, out_scale, out_amax, tensor_scale, true);
+  if (st != RN_OK) return st;
 
   rn_launch_config cfg;
   if (explicit_cfg != nullptr) {
@@ -105,6 +123,7 @@ rn_status rows_entry(const void* x, const void* residual, const void* weight, vo
   a.res_out = residual_out;
   a.scale = out_scale;
   a.amax = out_amax;
+  a.tscale = tensor_scale;
   a.rows = rows;
   a.hidden = static_cast<int32_t>(hidden);
   a.eps = eps;
@@ -172,25 +191,23 @@ rn_status heads_entry(const void* q, const void* k, const void* q_weight, const 
   return launch(fn, cfg.grid, cfg.block_threads, &a, stream);
 }
 
-rn_status act_entry(const void* x, void* out, void* out_scale, float* out_amax, int64_t rows, int64_t d,
-                    uint32_t flags, const rn_launch_config* explicit_cfg, void* stream) {
+rn_status act_entry(const void* x, void* out, void* out_scale, float* out_amax, const float* tensor_scale,
+                    int64_t rows, int64_t d, uint32_t flags, const rn_launch_config* explicit_cfg, void* stream) {
   clear_error();
   ActKey key;
   rn_status st = check_act_shape(rows, d, flags, &key);
   if (st != RN_OK) return st;
-  const bool quant = key.out == kFP8 || key.out == kFP4;
-  if (!quant && (out_scale != nullptr || out_amax != nullptr))
-    return fail(RN_ERR_INVALID_ARG, "out_scale / out_amax are only for fp8 / fp4 output");
+  st = check_quant_ptrs(key.out, key.qs, out_scale, out_amax, tensor_scale, false);
+  if (st != RN_OK) return st;
   if (rows == 0) return RN_OK;
   if (x == nullptr || out == nullptr) return fail(RN_ERR_INVALID_ARG, "x and out must not be NULL");
-  if (quant && out_scale == nullptr) return fail(RN_ERR_INVALID_ARG, "quantized output needs out_scale");
   if (!aligned(x, 16) || !aligned(out, 16)) return fail(RN_ERR_MISALIGNED, "x and out must be 16-byte aligned");
-  if ((out_scale && key.qs != kQMx32 && !aligned(out_scale, 4)) || (out_amax && !aligned(out_amax, 4)))
-    return fail(RN_ERR_MISALIGNED, "float32 scales / out_amax must be 4-byte aligned");
+  st = check_quant_ptrs(key.out, key.qs, out_scale, out_amax, tensor_scale, true);
+  if (st != RN_OK) return st;
 
   rn_launch_config cfg;
   if (explicit_cfg != nullptr) {
-    RowKey rk;
+    RowKey rk{};
     rk.x = key.x;
     st = check_row_config(rows, d, rk, explicit_cfg, &cfg);
   } else {
@@ -208,6 +225,7 @@ rn_status act_entry(const void* x, void* out, void* out_scale, float* out_amax, 
   a.out = out;
   a.scale = out_scale;
   a.amax = out_amax;
+  a.tscale = tensor_scale;
   a.rows = rows;
   a.d = static_cast<int32_t>(d);
   return launch(fn, cfg.grid, cfg.block_threads, &a, stream);
@@ -223,27 +241,27 @@ extern "C" {
 rn_status rmsnorm_fwd(const void* x, const void* residual, const void* weight, void* out,
                       void* residual_out, void* out_scale, int64_t rows, int64_t hidden, float eps,
                       uint32_t flags, void* stream) {
-  return rows_entry(x, residual, weight, out, residual_out, out_scale, nullptr, rows, hidden, eps,
+  return rows_entry(x, residual, weight, out, residual_out, out_scale, nullptr, nullptr, rows, hidden, eps,
                     flags, nullptr, stream);
 }
 
 rn_status rmsnorm_fwd_ex(const void* x, const void* residual, const void* weight, void* out,
-                         void* residual_out, void* out_scale, float* out_amax, int64_t rows,
-                         int64_t hidden, float eps, uint32_t flags, void* stream) {
-  return rows_entry(x, residual, weight, out, residual_out, out_scale, out_amax, rows, hidden, eps,
-                    flags, nullptr, stream);
+                         void* residual_out, void* out_scale, float* out_amax, const float* tensor_scale,
+                         int64_t rows, int64_t hidden, float eps, uint32_t flags, void* stream) {
+  return rows_entry(x, residual, weight, out, residual_out, out_scale, out_amax, tensor_scale, rows, hidden,
+                    eps, flags, nullptr, stream);
 }
 
 rn_status rmsnorm_fwd_config(const void* x, const void* residual, const void* weight, void* out,
-                             void* residual_out, void* out_scale, float* out_amax, int64_t rows,
-                             int64_t hidden, float eps, uint32_t flags,
-                             const rn_launch_config* cfg, void* stream) {
+                             void* residual_out, void* out_scale, float* out_amax,
+                             const float* tensor_scale, int64_t rows, int64_t hidden, float eps,
+                             uint32_t flags, const rn_launch_config* cfg, void* stream) {
   if (cfg == nullptr) {
     clear_error();
     return fail(RN_ERR_INVALID_ARG, "launch config is NULL");
   }
-  return rows_entry(x, residual, weight, out, residual_out, out_scale, out_amax, rows, hidden, eps,
-                    flags, cfg, stream);
+  return rows_entry(x, residual, weight, out, residual_out, out_scale, out_amax, tensor_scale, rows, hidden,
+                    eps, flags, cfg, stream);
 }
 
 rn_status qknorm_fwd(const void* q, const void* k, const void* q_weight, const void* k_weight,
@@ -298,18 +316,19 @@ rn_status qknorm_query_config(int64_t tokens, int32_t num_q_heads, int32_t num_k
   return select_head_config(tokens > 0 ? tokens : 1, num_q_heads, num_k_heads, key, cus, cfg);
 }
 
-rn_status silu_mul_fwd(const void* x, void* out, void* out_scale, float* out_amax, int64_t rows,
-                       int64_t d, uint32_t flags, void* stream) {
-  return act_entry(x, out, out_scale, out_amax, rows, d, flags, nullptr, stream);
+rn_status silu_mul_fwd(const void* x, void* out, void* out_scale, float* out_amax, const float* tensor_scale,
+                       int64_t rows, int64_t d, uint32_t flags, void* stream) {
+  return act_entry(x, out, out_scale, out_amax, tensor_scale, rows, d, flags, nullptr, stream);
 }
 
-rn_status silu_mul_fwd_config(const void* x, void* out, void* out_scale, float* out_amax, int64_t rows,
-                              int64_t d, uint32_t flags, const rn_launch_config* cfg, void* stream) {
+rn_status silu_mul_fwd_config(const void* x, void* out, void* out_scale, float* out_amax,
+                              const float* tensor_scale, int64_t rows, int64_t d, uint32_t flags,
+                              const rn_launch_config* cfg, void* stream) {
   if (cfg == nullptr) {
     clear_error();
     return fail(RN_ERR_INVALID_ARG, "launch config is NULL");
   }
-  return act_entry(x, out, out_scale, out_amax, rows, d, flags, cfg, stream);
+  return act_entry(x, out, out_scale, out_amax, tensor_scale, rows, d, flags, cfg, stream);
 }
 
 rn_status silu_mul_query_config(int64_t rows, int64_t d, uint32_t flags, int32_t num_cus,

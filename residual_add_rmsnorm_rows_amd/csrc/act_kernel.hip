@@ -15,7 +15,7 @@
 // chunk of the up half, buffer resources sized to each half row (ragged ends
 // read zeros and write nothing), nontemporal loads and stores.  Outputs:
 // bf16 / f32, or quantized (fp8 e4m3fn with a per-row, per-128 or MX scale;
-// fp4 e2m1 with an MX scale).  Only the per-row scale needs a reduction across
+// fp4 e2m1 with an MX or NVFP4 scale).  Only the per-row scale needs a reduction across
 // the row (DPP + readlane, then LDS across waves); every other output is local
 // to a lane or to a lane group.
 
@@ -65,7 +65,8 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void silu_mul_kernel(const 
   constexpr bool ROW_MAX = QUANT && QS == kQRow;
   static_assert(SUB == 1 || SUB == 2, "chunking");
   static_assert(QS == kQRow || QUANT, "scale groups only for quantized outputs");
-  static_assert(OD != kFP4 || QS == kQMx32, "fp4 output is MX-scaled");
+  static_assert(OD != kFP4 || QS == kQMx32 || QS == kQNv16, "fp4 output is MX- or NVFP4-scaled");
+  static_assert(QS != kQNv16 || OD == kFP4, "NVFP4 scales are for fp4 output");
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -77,7 +78,9 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void silu_mul_kernel(const 
   char* __restrict__ op = static_cast<char*>(a.out);
   const uint32_t d = static_cast<uint32_t>(a.d);
   const uint32_t groups = d / (QG ? QG : d);  // scales per row
-  constexpr int SCALE_BYTES = QS == kQMx32 ? 1 : 4;
+  constexpr int SCALE_BYTES = QS == kQMx32 || QS == kQNv16 ? 1 : 4;
+  float tscale = 0.f;  // NVFP4's tensor scale, one uniform load
+  if constexpr (QS == kQNv16) tscale = *a.tscale;
 
   auto elem_of = [&](int s, int c) -> uint32_t {
     return static_cast<uint32_t>((((s * nw + wave) * SUB + c) * 64 + lane) * U);
@@ -145,7 +148,8 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void silu_mul_kernel(const 
 #pragma unroll
           for (int i = 0; i < U; ++i) q[i] = y[s][c][i] * qmul;
         } else if constexpr (QUANT) {
-          quantize_group_chunk<OD, QS, U>(y[s][c], 1.0f, lane, elem_of(s, c) / QG, sr, ar, a.amax != nullptr, q);
+          quantize_group_chunk<OD, QS, U>(y[s][c], 1.0f, lane, elem_of(s, c) / QG, sr, ar, a.amax != nullptr, q,
+                                          tscale);
         } else {
 #pragma unroll
           for (int i = 0; i < U; ++i) q[i] = y[s][c][i];
@@ -183,6 +187,7 @@ const void* pick_act_out(const ActKey& k) {
   if (k.out == kFP8 && k.qs == kQGroup128) return pick_act_nv<XD, kFP8, kQGroup128>(k.nv);
   if (k.out == kFP8 && k.qs == kQMx32) return pick_act_nv<XD, kFP8, kQMx32>(k.nv);
   if (k.out == kFP4 && k.qs == kQMx32) return pick_act_nv<XD, kFP4, kQMx32>(k.nv);
+  if (k.out == kFP4 && k.qs == kQNv16) return pick_act_nv<XD, kFP4, kQNv16>(k.nv);
   return nullptr;
 }
 

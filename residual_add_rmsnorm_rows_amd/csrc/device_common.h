@@ -271,13 +271,13 @@ struct OpMax {
   __device__ __forceinline__ static float apply(float a, float b) { return __builtin_fmaxf(a, b); }
 };
 
-// Reduce over aligned groups of G lanes (G = 4, 8, 16, 32 or 64); every lane
-// of a group receives the group's result.
+// Reduce over aligned groups of G lanes (G = 2, 4, 8, 16, 32 or 64); every
+// lane of a group receives the group's result.
 template <int G, class Op>
 __device__ __forceinline__ float group_reduce(float v) {
-  static_assert(G == 4 || G == 8 || G == 16 || G == 32 || G == 64, "group size");
+  static_assert(G == 2 || G == 4 || G == 8 || G == 16 || G == 32 || G == 64, "group size");
   v = Op::apply(v, dpp_mov<kDppQuadXor1>(v));
-  v = Op::apply(v, dpp_mov<kDppQuadXor2>(v));
+  if constexpr (G >= 4) v = Op::apply(v, dpp_mov<kDppQuadXor2>(v));
   if constexpr (G >= 8) v = Op::apply(v, dpp_mov<kDppRowHalfMirror>(v));
   if constexpr (G >= 16) v = Op::apply(v, dpp_mov<kDppRowMirror>(v));
   if constexpr (G == 32) {
@@ -311,12 +311,20 @@ namespace rn {
 // ---------------------------------------------------------------------------
 
 template <int QS>
-constexpr int scale_group() { return QS == kQGroup128 ? 128 : QS == kQMx32 ? 32 : 0; }
+constexpr int scale_group() { return QS == kQGroup128 ? 128 : QS == kQMx32 ? 32 : QS == kQNv16 ? 16 : 0; }
+
+// Value of a non-negative OCP E4M3FN code (bias 7; subnormals m * 2^-9), exact.
+__device__ __forceinline__ float e4m3fn_value(uint32_t code) {
+  const int e = static_cast<int>((code >> 3) & 0xF);
+  const int m = static_cast<int>(code & 0x7);
+  return e == 0 ? __builtin_amdgcn_ldexpf(static_cast<float>(m), -9)
+                : __builtin_amdgcn_ldexpf(static_cast<float>(8 + m), e - 10);
+}
 
 template <int OD, int QS, int U>
 __device__ __forceinline__ void quantize_group_chunk(const float (&v)[U], float mul, int lane, uint32_t gidx,
                                                      __amdgpu_buffer_rsrc_t sr, __amdgpu_buffer_rsrc_t ar,
-                                                     bool want_amax, float (&y)[U]) {
+                                                     bool want_amax, float (&y)[U], float tensor_scale = 0.f) {
   constexpr int QG = scale_group<QS>();
   constexpr int GL = QG / U;
   constexpr int EMAX = OD == kFP8 ? 8 : 2;  // MX: exponent of the element format's top binade
@@ -331,6 +339,16 @@ __device__ __forceinline__ void quantize_group_chunk(const float (&v)[U], float 
 #pragma unroll
     for (int i = 0; i < U; ++i) y[i] = (v[i] * mul) * gq;
     if (leader) buffer_store_f32(sr, gidx * 4, gamax / 448.0f);
+  } else if constexpr (QS == kQNv16) {
+    // NVFP4: block scale code RNE_e4m3fn(amax / (6 s_t)) (saturating), element
+    // codes of v / (s_b s_t) through one reciprocal; a zero block scale gives
+    // zero codes.
+    const uint32_t sc = cvt_fp8x2<false>(gamax / (6.0f * tensor_scale), 0.f, 0u) & 0xFFu;
+    const float d = e4m3fn_value(sc) * tensor_scale;
+    const float r = d > 0.f ? 1.0f / d : 0.f;
+#pragma unroll
+    for (int i = 0; i < U; ++i) y[i] = (v[i] * mul) * r;
+    if (leader) buffer_store_u8(sr, gidx, sc);
   } else {
     // MX: shared exponent floor(log2 amax) - EMAX, clamped to E8M0's range;
     // an all-zero block takes the smallest scale, 2^-127.

@@ -18,6 +18,7 @@ enum QScheme : int {
   kQRow = 0,       // one float32 scale amax / 448 per row (fp8)
   kQGroup128 = 1,  // one float32 scale amax / 448 per 128 consecutive elements (fp8)
   kQMx32 = 2,      // OCP MX: one E8M0 scale per 32 consecutive elements (fp8 e4m3 or fp4 e2m1)
+  kQNv16 = 3,      // NVFP4: one E4M3FN scale per 16 elements and a float32 tensor scale (fp4 e2m1)
 };
 
 // Kernel arguments of the rows kernel, passed by value as the only argument.
@@ -29,6 +30,7 @@ struct RowArgs {
   void* res_out;         // nullptr iff res is nullptr
   void* scale;           // quantized output only: float32 per row / per group, or E8M0 per block
   float* amax;           // quantized output only, may be nullptr: float32 amax per scale
+  const float* tscale;   // NVFP4 only: the float32 tensor scale (one value, device memory)
   int64_t rows;
   int32_t hidden;        // elements per row
   float eps;
@@ -56,6 +58,7 @@ struct ActArgs {
   void* out;             // [rows, d]
   void* scale;           // quantized output only
   float* amax;           // quantized output only, may be nullptr
+  const float* tscale;   // NVFP4 only: the float32 tensor scale
   int64_t rows;
   int32_t d;
 };
@@ -143,12 +146,14 @@ const void* pick_row_kernel_bf16_fp8_row(const RowKey& key);
 const void* pick_row_kernel_bf16_fp8_g128(const RowKey& key);
 const void* pick_row_kernel_bf16_fp8_mx(const RowKey& key);
 const void* pick_row_kernel_bf16_fp4_mx(const RowKey& key);
+const void* pick_row_kernel_bf16_fp4_nv(const RowKey& key);
 const void* pick_row_kernel_f32_bf16(const RowKey& key);
 const void* pick_row_kernel_f32_f32(const RowKey& key);
 const void* pick_row_kernel_f32_fp8_row(const RowKey& key);
 const void* pick_row_kernel_f32_fp8_g128(const RowKey& key);
 const void* pick_row_kernel_f32_fp8_mx(const RowKey& key);
 const void* pick_row_kernel_f32_fp4_mx(const RowKey& key);
+const void* pick_row_kernel_f32_fp4_nv(const RowKey& key);
 // heads_kernel.hip
 const void* pick_head_kernel(const HeadKey& key);
 // act_kernel.hip

@@ -85,11 +85,12 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowA
   constexpr int WW = U * WB / 4;            // dwords of weight per chunk
   constexpr int OCB = U * OBITS / 8;        // output bytes per chunk
   constexpr int OW = words_for<OD, U>();    // dwords holding one output chunk
-  constexpr int QG = QS == kQGroup128 ? 128 : QS == kQMx32 ? 32 : 0;  // elements per scale
+  constexpr int QG = scale_group<QS>();      // elements per scale (0: one per row)
   static_assert(SUB == 1 || SUB == 2, "chunking");
   static_assert(!QUANT || QS == kQRow || (QG % U == 0 && (64 * U) % QG == 0), "scale groups");
   static_assert(QS == kQRow || QUANT, "scale groups only for quantized outputs");
-  static_assert(OD != kFP4 || QS == kQMx32, "fp4 output is MX-scaled");
+  static_assert(OD != kFP4 || QS == kQMx32 || QS == kQNv16, "fp4 output is MX- or NVFP4-scaled");
+  static_assert(QS != kQNv16 || OD == kFP4, "NVFP4 scales are for fp4 output");
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -103,7 +104,9 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowA
   char* __restrict__ rop = static_cast<char*>(a.res_out);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, static_cast<uint32_t>(a.hidden) * WB);
   const uint32_t groups = static_cast<uint32_t>(a.hidden) / (QG ? QG : a.hidden);  // scales per row
-  constexpr int SCALE_BYTES = QS == kQMx32 ? 1 : 4;
+  constexpr int SCALE_BYTES = QS == kQMx32 || QS == kQNv16 ? 1 : 4;
+  float tscale = 0.f;  // NVFP4's tensor scale, one uniform load
+  if constexpr (QS == kQNv16) tscale = *a.tscale;
 
   // Element offset of chunk (s, c) of this lane from the row start:
   // (((s * W + wave) * SUB + c) * 64 + lane) * U.  Chunks past the row end
@@ -220,7 +223,8 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowA
 #pragma unroll
           for (int i = 0; i < U; ++i) y[i] = (h[s][c][i] * inv) * qmul;
         } else if constexpr (QUANT) {
-          quantize_group_chunk<OD, QS, U>(h[s][c], inv, lane, elem_of(s, c) / QG, sr, ar, a.amax != nullptr, y);
+          quantize_group_chunk<OD, QS, U>(h[s][c], inv, lane, elem_of(s, c) / QG, sr, ar, a.amax != nullptr, y,
+                                          tscale);
         } else {
           float wf[U];
           unpack<WD, U>(ww[s][c], wf);

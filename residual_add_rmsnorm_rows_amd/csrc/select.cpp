@@ -70,15 +70,16 @@ rn_status check_row_shape(int64_t rows, int64_t hidden, uint32_t flags, bool has
   const int qs = (flags >> RN_FLAGS_SCALE_SHIFT) & 3;
   if (x == 3 || w == 3 || (has_residual && r == 3))
     return fail(RN_ERR_INVALID_ARG, "dtype code 3 is not an input dtype (flags 0x%x)", flags);
-  if (qs == 3) return fail(RN_ERR_INVALID_ARG, "scale granularity 3 does not exist (flags 0x%x)", flags);
   if (x == kFP8) return fail(RN_ERR_UNSUPPORTED, "x must be bf16 or f32");
   if (w == kFP8) return fail(RN_ERR_UNSUPPORTED, "weight must be bf16 or f32");
   const int o = o_code == 3 ? kFP4 : o_code;
   const bool quant = o == kFP8 || o == kFP4;
   if (!quant && qs != kQRow)
     return fail(RN_ERR_INVALID_ARG, "a scale granularity needs an fp8 or fp4 output");
-  if (o == kFP4 && qs != kQMx32)
-    return fail(RN_ERR_UNSUPPORTED, "fp4 e2m1 output is built with MX scales (RN_SCALE_MX32) only");
+  if (o == kFP4 && qs != kQMx32 && qs != kQNv16)
+    return fail(RN_ERR_UNSUPPORTED, "fp4 e2m1 output takes MX (RN_SCALE_MX32) or NVFP4 (RN_SCALE_NV16) scales");
+  if (qs == kQNv16 && o != kFP4)
+    return fail(RN_ERR_UNSUPPORTED, "NVFP4 scales (RN_SCALE_NV16) are for fp4 e2m1 output only");
   int res = kNone;
   if (has_residual) {
     if (r == kFP8) return fail(RN_ERR_UNSUPPORTED, "residual must be bf16 or f32");
@@ -96,6 +97,9 @@ rn_status check_row_shape(int64_t rows, int64_t hidden, uint32_t flags, bool has
                 (long long)hidden);
   if (qs == kQMx32 && hidden % 32 != 0)
     return fail(RN_ERR_UNSUPPORTED, "hidden (%lld) must be a multiple of 32 for MX scales", (long long)hidden);
+  if (qs == kQNv16 && hidden % 16 != 0)
+    return fail(RN_ERR_UNSUPPORTED, "hidden (%lld) must be a multiple of 16 for NVFP4 scales",
+                (long long)hidden);
   const int64_t max_vecs = (int64_t)64 * kMaxVecsPerLane * (max_threads_for_nv(kMaxVecsPerLane) / 64);
   const int64_t max_vecs2 = (int64_t)64 * 4 * kMaxWavesPerRow;
   const int64_t cap = (max_vecs > max_vecs2 ? max_vecs : max_vecs2) * vec;

@@ -33,9 +33,14 @@ def to_host(t: torch.Tensor) -> np.ndarray:
     raise ValueError(t.dtype)
 
 
+def nvfp4_tensor_scale(y: np.ndarray) -> float:
+    """The usual per-tensor NVFP4 scale, amax / (6 * 448), as a float32 value."""
+    return float(np.float32(np.max(np.abs(y)) / (6.0 * 448.0)))
+
+
 def judge_rows(inputs: dict, x_dtype: str, res_dtype, w_dtype: str, out_dtype: str, eps: float,
                weight_plus_one: bool, out: np.ndarray, res_out, scale=None, amax=None,
-               scale_scheme: str = "row") -> dict:
+               scale_scheme: str = "row", tensor_scale=None) -> dict:
     """Compare the outputs of some rows (already on the host) with the oracle.
 
     ``inputs`` holds the same rows of x / residual and the full weight, as the
@@ -52,13 +57,13 @@ def judge_rows(inputs: dict, x_dtype: str, res_dtype, w_dtype: str, out_dtype: s
         rep["res_out_bit_exact"] = same
         rep["ok"] &= same
     y = ref["y"]
-    rep.update(judge_y(y, out_dtype, out, scale, amax, scale_scheme))
+    rep.update(judge_y(y, out_dtype, out, scale, amax, scale_scheme, tensor_scale))
     rep["ok"] = rep["ok"] and rep.pop("y_ok")
     return rep
 
 
 def judge_y(y: np.ndarray, out_dtype: str, out: np.ndarray, scale=None, amax=None,
-            scale_scheme: str = "row") -> dict:
+            scale_scheme: str = "row", tensor_scale=None) -> dict:
     """Judge an output tensor (host bits) against the exact pre-rounding values y [rows, n]."""
     rep = {"ok": True}
     if out_dtype == "bf16":
@@ -89,6 +94,26 @@ def judge_y(y: np.ndarray, out_dtype: str, out: np.ndarray, scale=None, amax=Non
             rep["amax"] = C.check_f32(amax, q["amax"])
             rep["ok"] &= formula and rep["amax"]["ok"]
         cr = C.check_fp8_codes(out, own(scale))
+        rep["codes"] = cr
+        rep["ok"] &= cr["ok"]
+    elif scale_scheme == "nv16":  # NVFP4: E4M3FN block scale per 16, float32 tensor scale
+        q = BQ.nvfp4_quantize(y, tensor_scale)
+        sc = np.asarray(scale, dtype=np.uint8)
+        # the GPU's block scale follows from its own amax exactly:
+        # e4m3fn(fl32(amax / fl32(6 s_t))), nearest even, saturating
+        if amax is not None:
+            amax = np.asarray(amax, dtype=np.float32)
+            t6 = np.float32(6.0) * np.float32(tensor_scale)
+            own = O.e4m3fn_encode((amax / t6).astype(np.float32).astype(np.float64))
+            rep["scale_formula_exact"] = bool(np.array_equal(own, sc))
+            rep["amax"] = C.check_f32(amax, q["amax"])
+            rep["ok"] &= rep["scale_formula_exact"] and rep["amax"]["ok"]
+        # ... and is within one step of the oracle's
+        rep["scale_codes"] = C.check_fp8_codes(sc, q["scale_codes"])
+        rep["scale_frac_exact"] = float((sc == q["scale_codes"]).mean())
+        rep["ok"] &= rep["scale_codes"]["ok"]
+        codes_ref = BQ.nvfp4_quantize(y, tensor_scale, scale_codes=sc)["codes"]
+        cr = C.check_fp4_codes(BQ.unpack_fp4(out), codes_ref)
         rep["codes"] = cr
         rep["ok"] &= cr["ok"]
     else:  # MX, E8M0 scale per 32 elements

@@ -52,8 +52,8 @@ BF = L.make_flags("bf16", "bf16", "bf16", "bf16", False)
 
 
 def _fwd(lib, x=FAKE, res=FAKE, w=FAKE, out=FAKE + 0x1000, res_out=FAKE + 0x2000, scale=None, amax=None,
-         rows=4, hidden=1024, eps=1e-6, flags=BF):
-    return lib.rmsnorm_fwd_ex(x, res, w, out, res_out, scale, amax, rows, hidden, eps, flags, None)
+         ts=None, rows=4, hidden=1024, eps=1e-6, flags=BF):
+    return lib.rmsnorm_fwd_ex(x, res, w, out, res_out, scale, amax, ts, rows, hidden, eps, flags, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -83,6 +83,80 @@ def _fwd(lib, x=FAKE, res=FAKE, w=FAKE, out=FAKE + 0x1000, res_out=FAKE + 0x2000
 def test_rmsnorm_rejects_before_any_hip_call(lib, kw, status):
     assert _fwd(lib, **kw) == status
     assert lib.rn_last_error().decode() != ""
+
+
+def _qflags(out, scheme, x="bf16", res="bf16"):
+    return L.make_flags(x, res, "bf16", out, False, scheme)
+
+
+FP8_G = _qflags("fp8_e4m3fn", "group128")
+FP8_MX = _qflags("fp8_e4m3fn", "mx32")
+FP4_MX = _qflags("fp4_e2m1", "mx32")
+FP4_NV = _qflags("fp4_e2m1", "nv16")
+SC = FAKE + 0x3000  # scale buffer
+TS = FAKE + 0x4000  # NVFP4 tensor scale
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=FP8_G, scale=SC, hidden=1024 + 64), L.RN_ERR_UNSUPPORTED),   # per-128 needs H % 128
+    (dict(flags=FP8_MX, scale=SC, hidden=1024 + 16), L.RN_ERR_UNSUPPORTED),  # MX needs H % 32
+    (dict(flags=FP4_NV, scale=SC, ts=TS, hidden=1024 + 8), L.RN_ERR_UNSUPPORTED),  # NVFP4 needs H % 16
+    (dict(flags=_qflags("fp4_e2m1", "row"), scale=SC), L.RN_ERR_UNSUPPORTED),  # fp4 takes MX or NVFP4 scales
+    (dict(flags=_qflags("fp4_e2m1", "group128"), scale=SC), L.RN_ERR_UNSUPPORTED),
+    (dict(flags=_qflags("fp8_e4m3fn", "nv16"), scale=SC, ts=TS), L.RN_ERR_UNSUPPORTED),  # NVFP4 is fp4 only
+    (dict(flags=FP4_NV, scale=SC), L.RN_ERR_INVALID_ARG),                    # NVFP4 without tensor scale
+    (dict(flags=FP4_MX, scale=SC, ts=TS), L.RN_ERR_INVALID_ARG),             # tensor scale without NVFP4
+    (dict(flags=BF, ts=TS), L.RN_ERR_INVALID_ARG),
+    (dict(flags=FP4_NV, ts=TS), L.RN_ERR_INVALID_ARG),                       # no scale buffer
+    (dict(flags=FP4_NV, scale=SC, ts=TS + 2), L.RN_ERR_MISALIGNED),
+    (dict(flags=FP8_G, scale=SC + 2), L.RN_ERR_MISALIGNED),                  # float32 scales
+    (dict(flags=FP8_G, scale=SC, amax=SC + 0x1002), L.RN_ERR_MISALIGNED),
+    (dict(flags=BF, amax=SC), L.RN_ERR_INVALID_ARG),                         # amax without quantized out
+])
+def test_block_scaled_outputs_are_checked(lib, kw, status):
+    assert _fwd(lib, **kw) == status
+    assert lib.rn_last_error().decode() != ""
+
+
+def test_byte_scales_need_no_alignment_and_base_entry_rejects_nvfp4(lib):
+    # E8M0 / E4M3FN scales are bytes: an odd address passes every pointer check,
+    # and the call stops at the (deliberately uncovering) explicit launch
+    # configuration, checked after the pointers and before any HIP call
+    cfg = L.LaunchConfig()
+    cfg.kernel, cfg.waves_per_row, cfg.vecs_per_lane, cfg.grid = 0, 1, 1, 4
+    for flags, ts in ((FP4_MX, None), (FP4_NV, TS)):
+        st = lib.rmsnorm_fwd_config(FAKE, FAKE, FAKE, FAKE + 0x1000, FAKE + 0x2000, SC + 1, None, ts, 4, 1024,
+                                    1e-6, flags, ctypes.byref(cfg), None)
+        assert st == L.RN_ERR_INVALID_ARG and "config" in lib.rn_last_error().decode()
+    # rmsnorm_fwd has no tensor_scale argument: NVFP4 is rejected there
+    st = lib.rmsnorm_fwd(FAKE, FAKE, FAKE, FAKE + 0x1000, FAKE + 0x2000, SC, 4, 1024, 1e-6, FP4_NV, None)
+    assert st == L.RN_ERR_INVALID_ARG and "tensor_scale" in lib.rn_last_error().decode()
+
+
+def test_silu_mul_rejects_before_any_hip_call(lib):
+    def call(x=FAKE, out=FAKE + 0x1000, scale=None, amax=None, ts=None, rows=4, d=1024,
+             flags=(L.RN_DTYPE_BF16 << L.RN_FLAGS_X_SHIFT) | (L.RN_DTYPE_BF16 << L.RN_FLAGS_OUT_SHIFT)):
+        return lib.silu_mul_fwd(x, out, scale, amax, ts, rows, d, flags, None)
+
+    nv = (L.RN_DTYPE_FP4_E2M1 << L.RN_FLAGS_OUT_SHIFT) | (3 << L.RN_FLAGS_SCALE_SHIFT)
+    assert call(rows=-1) == L.RN_ERR_INVALID_ARG
+    assert call(d=0) == L.RN_ERR_INVALID_ARG
+    assert call(flags=1 << L.RN_FLAGS_RES_SHIFT) == L.RN_ERR_INVALID_ARG  # residual bits are not silu_mul's
+    assert call(flags=L.RN_FLAG_WEIGHT_PLUS_ONE) == L.RN_ERR_INVALID_ARG
+    assert call(x=None) == L.RN_ERR_INVALID_ARG
+    assert call(out=None) == L.RN_ERR_INVALID_ARG
+    assert call(scale=SC) == L.RN_ERR_INVALID_ARG
+    assert call(d=1004) == L.RN_ERR_UNSUPPORTED  # not a multiple of the 8-element bf16 vector
+    assert call(x=FAKE + 8) == L.RN_ERR_MISALIGNED
+    assert call(flags=nv, scale=SC) == L.RN_ERR_INVALID_ARG  # NVFP4 without tensor scale
+    assert call(flags=nv, scale=SC, ts=TS + 1) == L.RN_ERR_MISALIGNED
+    assert call(flags=nv, scale=SC, ts=TS, d=1024 + 8) == L.RN_ERR_UNSUPPORTED
+    assert call(rows=0, x=None, out=None) == L.RN_OK
+    cfg = L.LaunchConfig()
+    assert lib.silu_mul_fwd_config(FAKE, FAKE, None, None, None, 4, 1024, 0, None, None) == L.RN_ERR_INVALID_ARG
+    cfg.kernel, cfg.waves_per_row, cfg.vecs_per_lane, cfg.grid = 0, 1, 1, 4  # covers 512 of 1024
+    assert lib.silu_mul_fwd_config(FAKE, FAKE + 0x1000, None, None, None, 4, 1024, 0, ctypes.byref(cfg),
+                                   None) == L.RN_ERR_INVALID_ARG
 
 
 def test_rows_zero_is_a_noop(lib):
@@ -210,14 +284,14 @@ def test_explicit_config_is_checked(lib):
     cfg = L.LaunchConfig()
     cfg.kernel, cfg.waves_per_row, cfg.vecs_per_lane, cfg.grid = 0, 1, 1, 4
     # 64 lanes x 1 vector x 8 < 1024 elements: rejected before any HIP call
-    st = lib.rmsnorm_fwd_config(FAKE, FAKE, FAKE, FAKE + 0x1000, FAKE + 0x2000, None, None, 4, 1024, 1e-6, BF,
+    st = lib.rmsnorm_fwd_config(FAKE, FAKE, FAKE, FAKE + 0x1000, FAKE + 0x2000, None, None, None, 4, 1024, 1e-6, BF,
                                 ctypes.byref(cfg), None)
     assert st == L.RN_ERR_INVALID_ARG
     cfg.waves_per_row, cfg.vecs_per_lane = 16, 8  # 1024 threads with 8 vectors per lane: not built
-    st = lib.rmsnorm_fwd_config(FAKE, FAKE, FAKE, FAKE + 0x1000, FAKE + 0x2000, None, None, 4, 1024, 1e-6, BF,
+    st = lib.rmsnorm_fwd_config(FAKE, FAKE, FAKE, FAKE + 0x1000, FAKE + 0x2000, None, None, None, 4, 1024, 1e-6, BF,
                                 ctypes.byref(cfg), None)
     assert st == L.RN_ERR_INVALID_ARG
     cfg.waves_per_row, cfg.vecs_per_lane, cfg.grid = 2, 1, 5  # grid above rows
-    st = lib.rmsnorm_fwd_config(FAKE, FAKE, FAKE, FAKE + 0x1000, FAKE + 0x2000, None, None, 4, 1024, 1e-6, BF,
+    st = lib.rmsnorm_fwd_config(FAKE, FAKE, FAKE, FAKE + 0x1000, FAKE + 0x2000, None, None, None, 4, 1024, 1e-6, BF,
                                 ctypes.byref(cfg), None)
     assert st == L.RN_ERR_INVALID_ARG

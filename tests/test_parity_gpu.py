@@ -19,7 +19,7 @@ from oracle import compare as C
 from oracle import rownorm as O
 from residual_add_rmsnorm_rows_amd import _lib as L
 from oracle import activation as ACT
-from tests.gpu_util import TORCH_DTYPES, judge_rows, judge_y, to_dev, to_host
+from tests.gpu_util import TORCH_DTYPES, judge_rows, judge_y, nvfp4_tensor_scale, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -28,7 +28,15 @@ def _announce(msg):
     print(f"\n[case] {msg}", flush=True)
 
 
-def run_rownorm(wl, inputs, config=None, inplace=False, scale_scheme="row"):
+def oracle_y(wl, inputs):
+    """The oracle's unrounded outputs y for the given rows (to pick an NVFP4 tensor scale)."""
+    X = O.decode(inputs["x"], wl.x_dtype)
+    RES = None if inputs.get("residual") is None else O.decode(inputs["residual"], wl.res_dtype)
+    return O.rmsnorm_rows(X, O.decode(inputs["weight"], wl.w_dtype), wl.eps, 1.0 if wl.weight_plus_one else 0.0,
+                          residual=RES, res_dtype=wl.res_dtype)["y"]
+
+
+def run_rownorm(wl, inputs, config=None, inplace=False, scale_scheme="row", tensor_scale=None):
     x = to_dev(inputs["x"], wl.x_dtype)
     res = None if inputs["residual"] is None else to_dev(inputs["residual"], wl.res_dtype)
     w = to_dev(inputs["weight"], wl.w_dtype)
@@ -41,12 +49,12 @@ def run_rownorm(wl, inputs, config=None, inplace=False, scale_scheme="row"):
     r = R.fused_add_rmsnorm(x, res, w, wl.eps, weight_plus_one=wl.weight_plus_one,
                             out_dtype=TORCH_DTYPES[wl.out_dtype],
                             return_amax=wl.out_dtype in ("fp8_e4m3fn", "fp4_e2m1"),
-                            scale_scheme=scale_scheme, config=config, **kw)
+                            scale_scheme=scale_scheme, tensor_scale=tensor_scale, config=config, **kw)
     torch.cuda.synchronize()
     return r
 
 
-def judge(wl, inputs, r, rows=None, scale_scheme="row"):
+def judge(wl, inputs, r, rows=None, scale_scheme="row", tensor_scale=None):
     sel = slice(None) if rows is None else rows
     sub = {"x": inputs["x"][sel], "residual": None if inputs["residual"] is None else inputs["residual"][sel],
            "weight": inputs["weight"]}
@@ -55,7 +63,7 @@ def judge(wl, inputs, r, rows=None, scale_scheme="row"):
     scale = None if r.scale is None else to_host(r.scale)[sel]
     amax = None if r.amax is None else to_host(r.amax)[sel]
     return judge_rows(sub, wl.x_dtype, wl.res_dtype, wl.w_dtype, wl.out_dtype, wl.eps, wl.weight_plus_one,
-                      out, res_out, scale, amax, scale_scheme=scale_scheme)
+                      out, res_out, scale, amax, scale_scheme=scale_scheme, tensor_scale=tensor_scale)
 
 
 ROW_WORKLOADS = ["decode_8x1024", "decode_256x4096", "prefill_16384x8192", "prefill_fp8_8192x7168"]
@@ -174,13 +182,16 @@ BLOCK_CASES = [
     ("mx32", "fp8_e4m3fn", "bf16", "bf16"), ("mx32", "fp8_e4m3fn", "bf16", "f32"),
     ("mx32", "fp8_e4m3fn", "f32", None), ("mx32", "fp4_e2m1", "bf16", "bf16"),
     ("mx32", "fp4_e2m1", "bf16", "f32"), ("mx32", "fp4_e2m1", "f32", "f32"), ("mx32", "fp4_e2m1", "bf16", None),
+    ("nv16", "fp4_e2m1", "bf16", "bf16"), ("nv16", "fp4_e2m1", "bf16", "f32"), ("nv16", "fp4_e2m1", "f32", "f32"),
+    ("nv16", "fp4_e2m1", "bf16", None),
 ]
 
 
 @pytest.mark.parametrize("scheme,out,x,res", BLOCK_CASES)
 @pytest.mark.parametrize("rows,hidden", [(37, 1024), (300, 7168), (5, 8192)])
 def test_block_scaled_outputs(scheme, out, x, res, rows, hidden):
-    """fp8 with per-128 scales and OCP MX (fp8 / fp4 with E8M0 per 32): scales,
+    """fp8 with per-128 scales, OCP MX (fp8 / fp4 with E8M0 per 32) and NVFP4
+    (fp4 with E4M3FN per 16 and the usual tensor scale amax / 2688): scales,
     exponents and codes against the oracle, zero groups included."""
     wl = WL.RowNormWorkload(name="block", kind="test", rows=rows, hidden=hidden, x_dtype=x, res_dtype=res,
                             w_dtype="bf16", out_dtype=out, x_dist=WL.Dist(0, 1, 0.01, 20.0),
@@ -195,46 +206,76 @@ def test_block_scaled_outputs(scheme, out, x, res, rows, hidden):
         inputs["x"][0, 128:256] = 0.0
     if res is not None:
         inputs["residual"][0, 128:256] = 0
-    r = run_rownorm(wl, inputs, scale_scheme=scheme)
-    rep = judge(wl, inputs, r, scale_scheme=scheme)
+    ts = nvfp4_tensor_scale(oracle_y(wl, inputs)) if scheme == "nv16" else None
+    r = run_rownorm(wl, inputs, scale_scheme=scheme, tensor_scale=ts)
+    rep = judge(wl, inputs, r, scale_scheme=scheme, tensor_scale=ts)
     assert rep["ok"], rep
     sc = to_host(r.scale)
     if scheme == "mx32":
         assert np.all(sc[0, 4:8] == 0)  # 2^-127 for the zero blocks
+    elif scheme == "nv16":
+        assert np.all(sc[0, 8:16] == 0)  # scale 0 for the zero blocks
     else:
         assert np.all(sc[0, 1] == 0)
 
 
-@pytest.mark.parametrize("scheme,out", [("group128", "fp8_e4m3fn"), ("mx32", "fp4_e2m1"), ("mx32", "fp8_e4m3fn")])
+@pytest.mark.parametrize("scheme,out", [("group128", "fp8_e4m3fn"), ("mx32", "fp4_e2m1"), ("mx32", "fp8_e4m3fn"),
+                                        ("nv16", "fp4_e2m1")])
 def test_block_scaled_every_launch_variant(scheme, out):
     H = 7168
     wl = WL.RowNormWorkload(name="bv", kind="test", rows=19, hidden=H, x_dtype="bf16", res_dtype="f32",
                             w_dtype="bf16", out_dtype=out, x_dist=WL.Dist(0, 1), res_dist=WL.Dist(0, 4),
                             w_dist=WL.Dist(1, 0.1), weight_plus_one=True, eps=1e-6)
     inputs = WL.generate_rownorm(wl, seed=13)
+    ts = nvfp4_tensor_scale(oracle_y(wl, inputs)) if scheme == "nv16" else None
     n = 0
     for W, NV in _variants(H, 8):
         for grid in (wl.rows, 4):
             cfg = L.LaunchConfig()
             cfg.kernel, cfg.waves_per_row, cfg.vecs_per_lane, cfg.grid = L.RN_KERNEL_ROWS, W, NV, grid
             _announce(f"block variant {scheme} {out} W={W} NV={NV} grid={grid}")
-            rep = judge(wl, inputs, run_rownorm(wl, inputs, config=cfg, scale_scheme=scheme), scale_scheme=scheme)
+            r = run_rownorm(wl, inputs, config=cfg, scale_scheme=scheme, tensor_scale=ts)
+            rep = judge(wl, inputs, r, scale_scheme=scheme, tensor_scale=ts)
             assert rep["ok"], (W, NV, grid, rep)
             n += 1
     assert n > 0
 
 
-@pytest.mark.parametrize("scheme,out", [("group128", "fp8_e4m3fn"), ("mx32", "fp4_e2m1")])
+@pytest.mark.parametrize("scheme,out", [("group128", "fp8_e4m3fn"), ("mx32", "fp4_e2m1"), ("nv16", "fp4_e2m1")])
 def test_block_scaled_full_size_sampled(scheme, out):
     wl = WL.WORKLOADS["prefill_fp8_8192x7168"]
     wl = WL.RowNormWorkload(**{**wl.__dict__, "out_dtype": out})
     _announce(f"block full size {scheme} {out} cfg={R.query_config(wl.rows, wl.hidden, res_dtype=wl.res_dtype, out_dtype=out, scale_scheme=scheme)}")
     inputs = WL.generate_rownorm(wl, seed=0)
-    r = run_rownorm(wl, inputs, scale_scheme=scheme)
     rng = np.random.default_rng(5)
     rows = np.unique(np.concatenate([np.arange(3), np.arange(wl.rows - 3, wl.rows), rng.integers(0, wl.rows, 40)]))
-    rep = judge(wl, inputs, r, rows, scale_scheme=scheme)
+    sub = {"x": inputs["x"][rows], "residual": inputs["residual"][rows], "weight": inputs["weight"]}
+    # NVFP4: the tensor scale from the sampled rows' amax (any positive value is a valid input)
+    ts = nvfp4_tensor_scale(oracle_y(wl, sub)) if scheme == "nv16" else None
+    r = run_rownorm(wl, inputs, scale_scheme=scheme, tensor_scale=ts)
+    rep = judge(wl, inputs, r, rows, scale_scheme=scheme, tensor_scale=ts)
     assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("factor", [2.0 ** -6, 2.0 ** 14])
+def test_nvfp4_tensor_scale_extremes(factor):
+    """A tensor scale far below the usual one (block scales saturate at 448,
+    elements at 6) and far above it (block scales in E4M3FN's subnormal range
+    and rounding to zero)."""
+    wl = WL.RowNormWorkload(name="nvx", kind="test", rows=64, hidden=2048, x_dtype="bf16", res_dtype="bf16",
+                            w_dtype="bf16", out_dtype="fp4_e2m1", x_dist=WL.Dist(0, 1, 0.01, 20.0),
+                            res_dist=WL.Dist(0, 1), w_dist=WL.Dist(1, 0.1), weight_plus_one=False, eps=1e-6)
+    inputs = WL.generate_rownorm(wl, seed=14)
+    ts = float(np.float32(nvfp4_tensor_scale(oracle_y(wl, inputs)) * factor))
+    _announce(f"nvfp4 tensor scale x{factor}: {ts}")
+    r = run_rownorm(wl, inputs, scale_scheme="nv16", tensor_scale=ts)
+    rep = judge(wl, inputs, r, scale_scheme="nv16", tensor_scale=ts)
+    assert rep["ok"], rep
+    sc = to_host(r.scale)
+    if factor < 1:
+        assert np.mean(sc == 0x7E) > 0.5  # mostly saturated block scales
+    else:
+        assert np.mean(sc < 0x08) > 0.5 and np.any(sc == 0)  # subnormal and zero block scales
 
 
 def test_edge_cases():
@@ -391,23 +432,32 @@ def test_empty_kernel_launch():
 
 
 ACT_OUTS = [("bf16", "row"), ("f32", "row"), ("fp8_e4m3fn", "row"), ("fp8_e4m3fn", "group128"),
-            ("fp8_e4m3fn", "mx32"), ("fp4_e2m1", "mx32")]
+            ("fp8_e4m3fn", "mx32"), ("fp4_e2m1", "mx32"), ("fp4_e2m1", "nv16")]
 
 
-def run_act(wl, x_np, scale_scheme, config=None):
+def act_tensor_scale(wl, x_np, scale_scheme, rows=None):
+    """NVFP4: the usual tensor scale from the oracle's outputs (of the given rows); else None."""
+    if scale_scheme != "nv16":
+        return None
+    sel = slice(None) if rows is None else rows
+    return nvfp4_tensor_scale(ACT.silu_mul_rows(O.decode(x_np[sel], wl.x_dtype), wl.d))
+
+
+def run_act(wl, x_np, scale_scheme, config=None, tensor_scale=None):
     x = to_dev(x_np, wl.x_dtype)
     r = R.silu_mul(x, out_dtype=TORCH_DTYPES[wl.out_dtype], scale_scheme=scale_scheme,
-                   return_amax=wl.out_dtype in ("fp8_e4m3fn", "fp4_e2m1"), config=config)
+                   return_amax=wl.out_dtype in ("fp8_e4m3fn", "fp4_e2m1"), tensor_scale=tensor_scale,
+                   config=config)
     torch.cuda.synchronize()
     return r
 
 
-def judge_act(wl, x_np, r, scale_scheme, rows=None):
+def judge_act(wl, x_np, r, scale_scheme, rows=None, tensor_scale=None):
     sel = slice(None) if rows is None else rows
     y = ACT.silu_mul_rows(O.decode(x_np[sel], wl.x_dtype), wl.d)
     scale = None if r.scale is None else to_host(r.scale)[sel]
     amax = None if r.amax is None else to_host(r.amax)[sel]
-    rep = judge_y(y, wl.out_dtype, to_host(r.out)[sel], scale, amax, scale_scheme)
+    rep = judge_y(y, wl.out_dtype, to_host(r.out)[sel], scale, amax, scale_scheme, tensor_scale)
     rep["ok"] = rep.pop("y_ok")
     return rep
 
@@ -423,35 +473,39 @@ def test_silu_mul_parity(out, scheme, x, rows, d):
         xn[0, 256:512] = 0  # a zero group of the output (gate zero)
     else:
         xn[0, 256:512] = 0.0
-    rep = judge_act(wl, xn, run_act(wl, xn, scheme), scheme)
+    ts = act_tensor_scale(wl, xn, scheme)
+    rep = judge_act(wl, xn, run_act(wl, xn, scheme, tensor_scale=ts), scheme, tensor_scale=ts)
     assert rep["ok"], rep
 
 
-@pytest.mark.parametrize("out,scheme", [("bf16", "row"), ("fp8_e4m3fn", "row"), ("fp4_e2m1", "mx32")])
+@pytest.mark.parametrize("out,scheme", [("bf16", "row"), ("fp8_e4m3fn", "row"), ("fp4_e2m1", "mx32"),
+                                        ("fp4_e2m1", "nv16")])
 def test_silu_mul_every_launch_variant(out, scheme):
     d = 3584
     wl = WL.ActWorkload(name="actv", rows=23, d=d, x_dtype="bf16", out_dtype=out, x_dist=WL.Dist(0, 1))
     xn = WL.generate_act(wl, seed=18)
+    ts = act_tensor_scale(wl, xn, scheme)
     n = 0
     for W, NV in _variants(d, 8):
         for grid in (wl.rows, 4):
             cfg = L.LaunchConfig()
             cfg.kernel, cfg.waves_per_row, cfg.vecs_per_lane, cfg.grid = L.RN_KERNEL_ROWS, W, NV, grid
             _announce(f"silu_mul variant out={out} W={W} NV={NV} grid={grid}")
-            rep = judge_act(wl, xn, run_act(wl, xn, scheme, config=cfg), scheme)
+            rep = judge_act(wl, xn, run_act(wl, xn, scheme, config=cfg, tensor_scale=ts), scheme, tensor_scale=ts)
             assert rep["ok"], (W, NV, grid, rep)
             n += 1
     assert n > 0
 
 
-@pytest.mark.parametrize("out,scheme", [("bf16", "row"), ("fp8_e4m3fn", "mx32")])
+@pytest.mark.parametrize("out,scheme", [("bf16", "row"), ("fp8_e4m3fn", "mx32"), ("fp4_e2m1", "nv16")])
 def test_silu_mul_full_size_sampled(out, scheme):
     wl = WL.WORKLOADS["silu_mul_8192x14336"]
     wl = WL.ActWorkload(**{**wl.__dict__, "out_dtype": out})
     _announce(f"silu_mul full size out={out} scheme={scheme} cfg={R.query_silu_mul_config(wl.rows, wl.d, out_dtype=out, scale_scheme=scheme)}")
     xn = WL.generate_act(wl, seed=0)
-    r = run_act(wl, xn, scheme)
     rng = np.random.default_rng(6)
     rows = np.unique(np.concatenate([np.arange(3), np.arange(wl.rows - 3, wl.rows), rng.integers(0, wl.rows, 30)]))
-    rep = judge_act(wl, xn, r, scheme, rows)
+    ts = act_tensor_scale(wl, xn, scheme, rows)
+    r = run_act(wl, xn, scheme, tensor_scale=ts)
+    rep = judge_act(wl, xn, r, scheme, rows, tensor_scale=ts)
     assert rep["ok"], rep
