@@ -90,8 +90,9 @@ typedef enum rn_status {
  *                      caller (tensor_scale, device memory).  Reading: block scale code
  *                      s_b = e4m3fn(amax / (6 s_t)) -- float32 division by fl32(6 s_t),
  *                      then nearest-even, saturating at 448 -- and element codes
- *                      e2m1(y * (1 / fl32(value(s_b) * s_t))); a block scale of 0 gives zero
- *                      codes.  Dequantize as value(code) * value(s_b) * s_t.
+ *                      e2m1(y * rcp(fl32(value(s_b) * s_t))), rcp the hardware reciprocal
+ *                      (within an ulp); a block scale of 0 gives zero codes.
+ *                      Dequantize as value(code) * value(s_b) * s_t.
  * Codes round to nearest, ties to even, and saturate at the format's largest value. */
 #define RN_SCALE_ROW 0u
 #define RN_SCALE_GROUP128 1u

@@ -29,22 +29,22 @@ constexpr int act_max(int a, int b) { return a > b ? a : b; }
 
 // ACCURATE (float32 outputs): library expf and an IEEE division, a few ulp of
 // float32 overall.  Otherwise (bf16 / fp8 / fp4 outputs, whose rounding step
-// is 2^-8 relative or coarser): the hardware exp2 and reciprocal
-// (v_exp_f32 with a rescale for subnormal results, v_rcp_f32), whose error
-// grows as |g| * 2^-24 relative -- far below those formats' steps -- at a
-// third of the instructions, which keeps the kernel memory-bound.
+// is 2^-8 relative or coarser): the hardware exp2 and reciprocal (v_exp_f32,
+// v_rcp_f32).  v_exp_f32 flushes subnormal results, and e = exp(-|g|) is
+// subnormal for |g| > 87 while g * e * up can still be a normal number, so
+// the exponent is taken 64 higher and e rescaled by an exact 2^-64 multiply:
+// e = 2^(64 - |g| log2(e)) * 2^-64.  The argument's rounding near 64 costs
+// about 2^-18 relative, far below those formats' steps, at about half the
+// instructions of the generic exp2's own range check.
 template <bool ACCURATE>
 __device__ __forceinline__ float silu_f32(float g) {
-  const float ng = -__builtin_fabsf(g);
   float e, r;
   if constexpr (ACCURATE) {
-    e = expf(ng);  // in (0, 1]
+    e = expf(-__builtin_fabsf(g));  // in (0, 1]
     r = 1.0f / (1.0f + e);
   } else {
-    // exp(ng) = 2^(ng * log2(e)); the generic exp2 keeps float32 subnormal
-    // results (the bare instruction flushes them), which a large up value can
-    // carry back into the normal range.
-    e = __builtin_exp2f(ng * 1.4426950408889634f);
+    e = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_fabsf(g), -1.4426950408889634f, 64.0f)) *
+        0x1p-64f;
     r = __builtin_amdgcn_rcpf(1.0f + e);
   }
   return g * (g >= 0.f ? r : e * r);

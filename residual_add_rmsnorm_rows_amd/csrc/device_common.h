@@ -341,11 +341,11 @@ __device__ __forceinline__ void quantize_group_chunk(const float (&v)[U], float 
     if (leader) buffer_store_f32(sr, gidx * 4, gamax / 448.0f);
   } else if constexpr (QS == kQNv16) {
     // NVFP4: block scale code RNE_e4m3fn(amax / (6 s_t)) (saturating), element
-    // codes of v / (s_b s_t) through one reciprocal; a zero block scale gives
-    // zero codes.
+    // codes of v / (s_b s_t) through the hardware reciprocal (within an ulp of
+    // float32, far below E2M1's steps); a zero block scale gives zero codes.
     const uint32_t sc = cvt_fp8x2<false>(gamax / (6.0f * tensor_scale), 0.f, 0u) & 0xFFu;
     const float d = e4m3fn_value(sc) * tensor_scale;
-    const float r = d > 0.f ? 1.0f / d : 0.f;
+    const float r = d > 0.f ? __builtin_amdgcn_rcpf(d) : 0.f;
 #pragma unroll
     for (int i = 0; i < U; ++i) y[i] = (v[i] * mul) * r;
     if (leader) buffer_store_u8(sr, gidx, sc);
