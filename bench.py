@@ -417,6 +417,15 @@ def main() -> int:
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
+    # per-launch spread: each launch bracketed by its own events (after the timed region)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record()
+        call(stream)
+        b.record()
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) * 1000.0 for a, b in evs)
+    pick = lambda q: round(per[min(len(per) - 1, int(q * len(per)))], 2)  # noqa: E731
     nbytes = rownorm_bytes(wl)
     gbs = nbytes / (ms * 1e-3) / 1e9
     log(f"{MAIN}: {ms * 1000:.1f} us/step, {gbs:.1f} GB/s")
@@ -431,8 +440,29 @@ def main() -> int:
                    "source_sha256": source_digest()},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic},
+        "launch_us": {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9), "launches": len(per)},
     }
     del call
+    torch.cuda.empty_cache()
+    # practical ceiling in the same run: the library's plain streaming copy
+    # moving the same bytes (half read, half written), timed the same way
+    half = (nbytes // 2) // 16 * 16
+    src = torch.empty(half, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    lib = L.lib()
+
+    def copy(stream):
+        st = lib.rn_launch_copy(src.data_ptr(), dst.data_ptr(), half, stream)
+        if st != 0:
+            L.check(st)
+
+    cms = time_stream_loop(copy, args.steps, args.warmup)
+    cgbs = 2 * half / (cms * 1e-3) / 1e9
+    log(f"copy ceiling: {cms * 1000:.1f} us, {cgbs:.1f} GB/s")
+    result["ceiling"] = {"kernel": "rn_launch_copy: nontemporal 16-byte loads and stores, 8 KiB per workgroup",
+                         "bytes_per_launch": 2 * half, "GBps": round(cgbs, 1),
+                         "frac_of_peak": round(cgbs / PEAK_HBM_GBS, 4), "value_over_ceiling": round(gbs / cgbs, 4)}
+    del src, dst
     torch.cuda.empty_cache()
     if args.copy_calibration:
         n = 1 << 30

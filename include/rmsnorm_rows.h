@@ -266,6 +266,14 @@ rn_status qknorm_query_config(int64_t tokens, int32_t num_q_heads, int32_t num_k
  * when decode-sized calls are timed. */
 rn_status rn_launch_empty(void* stream);
 
+/* Enqueues a plain streaming copy of `bytes` bytes from src to dst (device
+ * memory, 16-byte aligned, not overlapping; bytes a multiple of 16): one
+ * nontemporal 16-byte load and store per lane, 8 KiB per workgroup.  The
+ * practical bandwidth ceiling for a stream that reads and writes the same
+ * number of bytes, measured through the same launch path as the entry points
+ * above.  bytes == 0 is a no-op. */
+rn_status rn_launch_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
 /* Static description of a status code. */
 const char* rn_status_string(rn_status status);
 

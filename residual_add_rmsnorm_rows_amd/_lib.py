@@ -43,7 +43,8 @@ DTYPE_CODES = {"bf16": RN_DTYPE_BF16, "f32": RN_DTYPE_F32, "fp8_e4m3fn": RN_DTYP
 EXPORTED_SYMBOLS = (
     "rmsnorm_fwd", "rmsnorm_fwd_ex", "rmsnorm_fwd_config", "qknorm_fwd", "qknorm_fwd_config",
     "rmsnorm_query_config", "qknorm_query_config", "silu_mul_fwd", "silu_mul_fwd_config",
-    "silu_mul_query_config", "rn_launch_empty", "rn_status_string", "rn_last_error", "rn_abi_version",
+    "silu_mul_query_config", "rn_launch_empty", "rn_launch_copy", "rn_status_string", "rn_last_error",
+    "rn_abi_version",
 )
 ABI_VERSION = 2
 
@@ -100,6 +101,7 @@ _SIGNATURES = {
                             ctypes.c_int),
     "silu_mul_query_config": ([_i64, _i64, _u32, _i32, ctypes.POINTER(LaunchConfig)], ctypes.c_int),
     "rn_launch_empty": ([_vp], ctypes.c_int),
+    "rn_launch_copy": ([_vp, _vp, _i64, _vp], ctypes.c_int),
     "rn_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "rn_last_error": ([], ctypes.c_char_p),
     "rn_abi_version": ([], ctypes.c_int32),

@@ -58,7 +58,7 @@ def _jobs():
         cmd = [HIPCC, *HIP_FLAGS, f"-DRN_TU_X={x}", f"-DRN_TU_OUT={out}", f"-DRN_TU_QS={qs}",
                f"-DRN_TU_NAME={name}", "-c", os.path.join(CSRC, "rows_kernel.hip"), "-o", obj]
         jobs.append((obj, cmd))
-    for name in ("heads_kernel", "act_kernel", "empty_kernel"):
+    for name in ("heads_kernel", "act_kernel", "reference_kernels"):
         obj = os.path.join(BUILD_DIR, f"{name}.o")
         jobs.append((obj, [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, f"{name}.hip"), "-o", obj]))
     for src in ("select.cpp", "abi.cpp"):

@@ -351,6 +351,30 @@ rn_status rn_launch_empty(void* stream) {
   return launch(empty_kernel_address(), 1, 64, nullptr, stream);
 }
 
+rn_status rn_launch_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  clear_error();
+  if (bytes < 0 || bytes % 16 != 0) return fail(RN_ERR_INVALID_ARG, "bytes (%lld) must be a multiple of 16 and >= 0", (long long)bytes);
+  if (bytes == 0) return RN_OK;
+  if (src == nullptr || dst == nullptr) return fail(RN_ERR_INVALID_ARG, "src and dst must not be NULL");
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  if (s0 < d0 + static_cast<uintptr_t>(bytes) && d0 < s0 + static_cast<uintptr_t>(bytes))
+    return fail(RN_ERR_INVALID_ARG, "src and dst overlap");
+  if (!aligned(src, 16) || !aligned(dst, 16)) return fail(RN_ERR_MISALIGNED, "src and dst must be 16-byte aligned");
+  constexpr int64_t kTile = static_cast<int64_t>(kCopyThreads) * 16;
+  const int64_t grid = (bytes + kTile - 1) / kTile;
+  if (grid > 0x7FFFFFFF) return fail(RN_ERR_UNSUPPORTED, "copy of %lld bytes is too large", (long long)bytes);
+  struct {
+    const void* src;
+    void* dst;
+    int64_t bytes;
+  } a = {src, dst, bytes};
+  void* argv[] = {&a.src, &a.dst, &a.bytes};
+  hipError_t e = hipLaunchKernel(copy_kernel_address(), dim3(static_cast<unsigned>(grid)), dim3(kCopyThreads), argv, 0,
+                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RN_ERR_HIP, "hipLaunchKernel: %s", hipGetErrorString(e));
+  return RN_OK;
+}
+
 const char* rn_status_string(rn_status status) {
   switch (status) {
     case RN_OK: return "RN_OK: success";

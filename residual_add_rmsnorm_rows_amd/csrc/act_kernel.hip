@@ -7,8 +7,8 @@
 // half and the up projection in its second half (a merged gate/up GEMM
 // output).  silu(g) = g * sigmoid(g), evaluated in float32 as
 // g * (e / (1 + e)) for g < 0 and g / (1 + e) otherwise, with e = exp(-|g|),
-// so that no intermediate overflows (library exp and division for float32
-// outputs, the hardware exp2 and reciprocal for the narrower outputs).
+// for float32 outputs, and through an offset exponent with the hardware exp2
+// and reciprocal for the narrower outputs (see silu_mul_f32).
 //
 // Same machinery as the rows kernel: one workgroup of W wave64s per row, each
 // lane holding NV steps of one 16-byte chunk of the gate and the matching
@@ -27,27 +27,33 @@ namespace {
 constexpr int act_bits(int dt) { return dt == kBF16 ? 16 : dt == kF32 ? 32 : dt == kFP8 ? 8 : 4; }
 constexpr int act_max(int a, int b) { return a > b ? a : b; }
 
-// ACCURATE (float32 outputs): library expf and an IEEE division, a few ulp of
-// float32 overall.  Otherwise (bf16 / fp8 / fp4 outputs, whose rounding step
-// is 2^-8 relative or coarser): the hardware exp2 and reciprocal (v_exp_f32,
-// v_rcp_f32).  v_exp_f32 flushes subnormal results, and e = exp(-|g|) is
-// subnormal for |g| > 87 while g * e * up can still be a normal number, so
-// the exponent is taken 64 higher and e rescaled by an exact 2^-64 multiply:
-// e = 2^(64 - |g| log2(e)) * 2^-64.  The argument's rounding near 64 costs
-// about 2^-18 relative, far below those formats' steps, at about half the
-// instructions of the generic exp2's own range check.
+// silu(g) * u in float32.
+//
+// ACCURATE (float32 outputs): e = exp(-|g|) with the library expf, then
+// g / (1 + e) for g >= 0 and g e / (1 + e) otherwise, through an IEEE
+// division: a few float32 ulps, and no intermediate overflows.
+//
+// Otherwise (bf16 / fp8 / fp4 outputs, whose rounding step is 2^-8 relative
+// or coarser): silu(g) u = g u / (1 + exp(-g)) evaluated as
+//     t = 2^(-g log2(e) - 64) = exp(-g) 2^-64,
+//     silu(g) u = (g u) * rcp(t + 2^-64) * 2^-64,
+// with the hardware exp2 and reciprocal (v_exp_f32, v_rcp_f32).  The 2^-64
+// offset keeps every intermediate a normal float32 for -132 < g (where the
+// plain form's exp(-g) overflows from g < -88, and its result, though tiny,
+// can still be a normal number once multiplied by u); the final power-of-two
+// multiply is exact and rounds only where the result itself is subnormal.
+// The argument's rounding near 64 costs about 2^-17 relative, far below those
+// formats' steps, in 7 instructions per element without compare or select.
 template <bool ACCURATE>
-__device__ __forceinline__ float silu_f32(float g) {
-  float e, r;
+__device__ __forceinline__ float silu_mul_f32(float g, float u) {
   if constexpr (ACCURATE) {
-    e = expf(-__builtin_fabsf(g));  // in (0, 1]
-    r = 1.0f / (1.0f + e);
+    const float e = expf(-__builtin_fabsf(g));  // in (0, 1]
+    const float r = 1.0f / (1.0f + e);
+    return (g * (g >= 0.f ? r : e * r)) * u;
   } else {
-    e = __builtin_amdgcn_exp2f(__builtin_fmaf(__builtin_fabsf(g), -1.4426950408889634f, 64.0f)) *
-        0x1p-64f;
-    r = __builtin_amdgcn_rcpf(1.0f + e);
+    const float t = __builtin_amdgcn_exp2f(__builtin_fmaf(g, -1.4426950408889634f, -64.0f));
+    return ((g * u) * __builtin_amdgcn_rcpf(t + 0x1p-64f)) * 0x1p-64f;
   }
-  return g * (g >= 0.f ? r : e * r);
 }
 
 template <int XD, int OD, int QS, int NV>
@@ -114,7 +120,7 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void silu_mul_kernel(const 
         unpack<XD, U>(uw[s][c], u);
 #pragma unroll
         for (int i = 0; i < U; ++i) {
-          y[s][c][i] = silu_f32<OD == kF32>(g[i]) * u[i];
+          y[s][c][i] = silu_mul_f32<OD == kF32>(g[i], u[i]);
           if constexpr (ROW_MAX) mx = __builtin_fmaxf(mx, __builtin_fabsf(y[s][c][i]));
         }
       }

@@ -127,6 +127,7 @@ rn_status check_head_config(int64_t tokens, int32_t nq, int32_t nk, const HeadKe
 constexpr int kMaxWavesPerRow = 16;
 constexpr int kMaxVecsPerLane = 8;
 constexpr int kHeadBlockThreads = 256;
+constexpr int kCopyThreads = 512;  // reference copy: one 16-byte vector per lane, 8 KiB per workgroup
 
 // Largest workgroup a rows-kernel variant is compiled for: holding 8 vectors
 // per lane needs more than the 128 VGPRs a 1024-thread workgroup leaves each
@@ -158,6 +159,7 @@ const void* pick_row_kernel_f32_fp4_nv(const RowKey& key);
 const void* pick_head_kernel(const HeadKey& key);
 // act_kernel.hip
 const void* pick_act_kernel(const ActKey& key);
-// empty_kernel.hip
+// reference_kernels.hip
 const void* empty_kernel_address();
+const void* copy_kernel_address();
 }  // namespace rn

@@ -159,6 +159,15 @@ def test_silu_mul_rejects_before_any_hip_call(lib):
                                    None) == L.RN_ERR_INVALID_ARG
 
 
+def test_reference_copy_is_checked(lib):
+    assert lib.rn_launch_copy(FAKE, FAKE + 0x10000, 1000, None) == L.RN_ERR_INVALID_ARG  # not a multiple of 16
+    assert lib.rn_launch_copy(FAKE, FAKE + 0x10000, -16, None) == L.RN_ERR_INVALID_ARG
+    assert lib.rn_launch_copy(None, FAKE, 1024, None) == L.RN_ERR_INVALID_ARG
+    assert lib.rn_launch_copy(FAKE, FAKE + 512, 1024, None) == L.RN_ERR_INVALID_ARG  # overlap
+    assert lib.rn_launch_copy(FAKE + 8, FAKE + 0x10000, 1024, None) == L.RN_ERR_MISALIGNED
+    assert lib.rn_launch_copy(None, None, 0, None) == L.RN_OK
+
+
 def test_rows_zero_is_a_noop(lib):
     assert _fwd(lib, rows=0, x=None, res=None, w=None, out=None, res_out=None) == L.RN_OK
     assert lib.rn_last_error() == b""

@@ -278,6 +278,17 @@ def test_nvfp4_tensor_scale_extremes(factor):
         assert np.mean(sc < 0x08) > 0.5 and np.any(sc == 0)  # subnormal and zero block scales
 
 
+@pytest.mark.parametrize("nbytes", [16, 8192, 3 * 8192 + 48, 1 << 22])
+def test_reference_copy(nbytes):
+    _announce(f"reference copy {nbytes} bytes")
+    src = torch.randint(0, 256, (nbytes + 64,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros(nbytes + 64, dtype=torch.uint8, device="cuda")
+    L.check(L.lib().rn_launch_copy(src.data_ptr(), dst.data_ptr(), nbytes, torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes], src[:nbytes])
+    assert int(dst[nbytes:].count_nonzero()) == 0  # nothing written past the end
+
+
 def test_edge_cases():
     base = WL.WORKLOADS["decode_8x1024"]
     # rows == 0: no launch, empty outputs
