@@ -520,3 +520,21 @@ def test_silu_mul_full_size_sampled(out, scheme):
     r = run_act(wl, xn, scheme, tensor_scale=ts)
     rep = judge_act(wl, xn, r, scheme, rows, tensor_scale=ts)
     assert rep["ok"], rep
+
+
+def test_silu_mul_edge_cases():
+    """rows == 0, the smallest and largest d, ragged d (not a multiple of 64 lanes)."""
+    _announce("silu_mul rows=0")
+    x = torch.empty((0, 2048), dtype=torch.bfloat16, device="cuda")
+    r = R.silu_mul(x)
+    assert r.out.shape == (0, 1024)
+    for xd, rows, d in (("bf16", 3, 8), ("bf16", 2, 32768), ("f32", 2, 16384), ("bf16", 5, 1000), ("f32", 4, 12)):
+        wl = WL.ActWorkload(name="acte", rows=rows, d=d, x_dtype=xd, out_dtype="bf16", x_dist=WL.Dist(0, 2, 0.01, 20.0))
+        _announce(f"silu_mul edge x={xd} rows={rows} d={d}")
+        xn = WL.generate_act(wl, seed=19)
+        rep = judge_act(wl, xn, run_act(wl, xn, "row"), "row")
+        assert rep["ok"], (xd, rows, d, rep)
+    # unsupported sizes are refused before any launch
+    with pytest.raises(R.RNError):
+        R.silu_mul(torch.zeros((2, 2 * 1000), dtype=torch.bfloat16, device="cuda"),
+                   out_dtype=torch.float8_e4m3fn, scale_scheme="mx32")
