@@ -394,6 +394,48 @@ def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
                       f"one thread), {dt:.1f} s"}
 
 
+def _oracle_worker(args):
+    """One process of the parallel CPU baseline: the oracle on its own 64-row
+    batch of the workload, repeated for `budget_s` seconds."""
+    name, first_row, budget_s = args
+    import workloads as WL
+    from oracle import rownorm as O
+
+    wl = WL.WORKLOADS[name]
+    chunk = 64
+    inputs = WL.generate_rownorm(wl, seed=0, row_range=(first_row, first_row + chunk))
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        x = O.decode(inputs["x"], wl.x_dtype)
+        res = None if inputs["residual"] is None else O.decode(inputs["residual"], wl.res_dtype)
+        ref = O.rmsnorm_rows(x, O.decode(inputs["weight"], wl.w_dtype), wl.eps, 1.0 if wl.weight_plus_one else 0.0,
+                             residual=res, res_dtype=wl.res_dtype)
+        if res is not None:
+            O.encode(ref["h"], wl.res_dtype)
+        O.encode(ref["y"], wl.out_dtype)
+        done += chunk
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline_parallel(wl, budget_s: float = 8.0, max_procs: int = 8) -> dict:
+    """The same oracle in one process per host core (at most `max_procs`), each on
+    its own rows; the rate is the sum of the processes' rates."""
+    from concurrent.futures import ProcessPoolExecutor
+    import multiprocessing as mp
+
+    n = max(1, min(max_procs, os.cpu_count() or 1))
+    with ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn")) as ex:
+        parts = list(ex.map(_oracle_worker, [(wl.name, 64 * i, budget_s) for i in range(n)]))
+    rate = sum(rownorm_bytes(wl, rows=r) / t for r, t in parts)
+    rows = sum(r for r, _ in parts)
+    return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": n, "kind": "oracle",
+            "sample": f"{rows} rows x {wl.hidden} in {n} processes (each its own 64-row batch, float64 numpy, "
+                      f"one thread each), {budget_s:.0f} s"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -416,9 +458,17 @@ def main() -> int:
         print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
 
+    import workloads as WL
+
+    # The parallel CPU baseline starts its worker processes before this process
+    # touches the GPU (no process is started from one that has initialised it).
+    cpu_parallel = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle), one process per host core (at most 8)")
+        cpu_parallel = cpu_baseline_parallel(WL.WORKLOADS[MAIN])
+
     import torch
 
-    import workloads as WL
     from residual_add_rmsnorm_rows_amd import _lib as L
     import residual_add_rmsnorm_rows_amd as R
 
@@ -542,6 +592,8 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(wl)
+        if cpu_parallel is not None:
+            result["cpu_baseline_parallel"] = cpu_parallel
     print(json.dumps(result), flush=True)
     return 0
 
