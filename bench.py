@@ -234,6 +234,30 @@ def copy_ceiling(nbytes: int, sets: int, steps: int, warmup: int) -> dict:
             "GBps": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+def native_decode_latency(name: str, calls: int = 2000) -> dict:
+    """Eager decode latency through the C ABI from native code (the library's
+    rn_decode_latency driver, a child process): rmsnorm_fwd against
+    rn_launch_empty, back to back on one stream, no Python in the loop."""
+    import subprocess
+
+    import workloads as WL
+    from residual_add_rmsnorm_rows_amd import build as B
+
+    wl = WL.WORKLOADS[name]
+    if not os.path.exists(B.DECODE_LATENCY_PATH):
+        return {"error": "rn_decode_latency is not built"}
+    try:
+        p = subprocess.run([B.DECODE_LATENCY_PATH, str(wl.rows), str(wl.hidden), str(int(wl.weight_plus_one)),
+                            str(calls)], capture_output=True, text=True, timeout=120)
+    except subprocess.TimeoutExpired:
+        return {"error": "timed out"}
+    if p.returncode != 0:
+        return {"error": (p.stderr or p.stdout).strip()[-300:]}
+    r = json.loads(p.stdout.strip().splitlines()[-1])
+    return {"us_per_call": r["us_per_call"], "empty_us_per_call": r["empty_us_per_call"], "ratio": r["ratio"],
+            "calls": r["calls"]}
+
+
 def decode_metrics(name: str) -> dict:
     import workloads as WL
     from residual_add_rmsnorm_rows_amd import _lib as L
@@ -466,6 +490,12 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle), one process per host core (at most 8)")
         cpu_parallel = cpu_baseline_parallel(WL.WORKLOADS[MAIN])
+    # likewise the native decode-latency driver (its own GPU process, run to completion first)
+    native = {}
+    if not args.no_secondary and not args.no_decode:
+        for name in ("decode_8x1024", "decode_256x4096"):
+            log(f"native decode latency {name}")
+            native[name] = native_decode_latency(name)
 
     import torch
 
@@ -558,6 +588,8 @@ def main() -> int:
         for name in () if args.no_decode else ("decode_8x1024", "decode_256x4096"):
             log(f"decode {name}")
             sec[name] = decode_metrics(name)
+            if name in native:
+                sec[name]["c_abi_eager"] = native[name]
         log("qknorm_4096x32x128")
         sec["qknorm_4096x32x128"] = qknorm_metrics(args.steps * 4, args.warmup)
         log("prefill_fp8_8192x7168")

@@ -3,7 +3,8 @@
 Kernel translation units are compiled with hipcc (device code for gfx950
 only); the host-only selector and C ABI are compiled with g++ against the HIP
 runtime headers; everything is linked into one shared library next to this
-file.  Compilation runs in parallel, one process per translation unit.
+file.  Compilation runs in parallel, one process per translation unit.  A small native driver,
+``rn_decode_latency``, is linked against the library for decode timings.
 
 Usage: ``python -m residual_add_rmsnorm_rows_amd.build`` (or ``build()``).
 """
@@ -23,6 +24,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "librmsnorm_rows.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+DECODE_LATENCY_PATH = os.path.join(PKG_DIR, "rn_decode_latency")
 
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
@@ -100,6 +102,17 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
         print(out, file=sys.stderr)
         raise RuntimeError("link failed")
     os.replace(tmp, LIB_PATH)
+    # native decode-latency driver, linked against the library just built
+    exe_tmp = DECODE_LATENCY_PATH + ".tmp"
+    drv = ["g++", *HOST_FLAGS, os.path.join(CSRC, "decode_latency.cpp"), "-o", exe_tmp,
+           f"-L{os.path.dirname(LIB_PATH)}", "-lrmsnorm_rows", "-Wl,-rpath,$ORIGIN", f"-L{ROCM}/lib", "-lamdhip64",
+           f"-Wl,-rpath,{ROCM}/lib"]
+    rc, out = _run(drv)
+    if rc != 0:
+        print(" ".join(drv), file=sys.stderr)
+        print(out, file=sys.stderr)
+        raise RuntimeError("decode-latency driver failed to build")
+    os.replace(exe_tmp, DECODE_LATENCY_PATH)
     return LIB_PATH
 
 
