@@ -254,8 +254,8 @@ def native_decode_latency(name: str, calls: int = 2000) -> dict:
     if p.returncode != 0:
         return {"error": (p.stderr or p.stdout).strip()[-300:]}
     r = json.loads(p.stdout.strip().splitlines()[-1])
-    return {"us_per_call": r["us_per_call"], "empty_us_per_call": r["empty_us_per_call"], "ratio": r["ratio"],
-            "calls": r["calls"]}
+    return {k: r[k] for k in ("us_per_call", "empty_us_per_call", "ratio", "calls", "host_enqueue_us",
+                              "empty_host_enqueue_us", "select_and_check_ns")}
 
 
 def decode_metrics(name: str) -> dict:

@@ -9,6 +9,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <chrono>
+
 #include "rmsnorm_rows.h"
 
 namespace {
@@ -18,16 +20,30 @@ bool ok(hipError_t e, const char* what) {
   return e == hipSuccess;
 }
 
+// Host-only cost of the selector and argument checks (no HIP call).
+double query_ns(int64_t rows, int64_t hidden, uint32_t flags, int calls) {
+  rn_launch_config cfg;
+  const auto t0 = std::chrono::steady_clock::now();
+  for (int i = 0; i < calls; ++i) rmsnorm_query_config(rows, hidden, flags, 1, 256, &cfg);
+  const auto t1 = std::chrono::steady_clock::now();
+  return std::chrono::duration<double, std::nano>(t1 - t0).count() / calls;
+}
+
+// Average device time per call of `call` over `calls` back-to-back calls (HIP
+// events), and in *host_us the host time to enqueue them.
 template <class F>
-double us_per_call(F&& call, int calls, hipStream_t s) {
+double us_per_call(F&& call, int calls, hipStream_t s, double* host_us) {
   for (int i = 0; i < 100; ++i)
     if (!call()) return -1.0;
   hipEvent_t a, b;
   if (!ok(hipEventCreate(&a), "hipEventCreate") || !ok(hipEventCreate(&b), "hipEventCreate")) return -1.0;
   if (!ok(hipStreamSynchronize(s), "hipStreamSynchronize")) return -1.0;
   ok(hipEventRecord(a, s), "hipEventRecord");
+  const auto t0 = std::chrono::steady_clock::now();
   for (int i = 0; i < calls; ++i)
     if (!call()) return -1.0;
+  const auto t1 = std::chrono::steady_clock::now();
+  *host_us = std::chrono::duration<double, std::micro>(t1 - t0).count() / calls;
   ok(hipEventRecord(b, s), "hipEventRecord");
   if (!ok(hipEventSynchronize(b), "hipEventSynchronize")) return -1.0;
   float ms = 0.f;
@@ -74,15 +90,18 @@ int main(int argc, char** argv) {
     last = rn_launch_empty(s);
     return last == RN_OK;
   };
-  const double t_norm = us_per_call(norm, calls, s);
-  const double t_empty = us_per_call(empty, calls, s);
+  double h_norm = 0, h_empty = 0;
+  const double t_norm = us_per_call(norm, calls, s, &h_norm);
+  const double t_empty = us_per_call(empty, calls, s, &h_empty);
+  const double q_ns = query_ns(rows, hidden, flags, calls);
   if (t_norm < 0 || t_empty < 0) {
     fprintf(stderr, "call failed: %s %s\n", rn_status_string(last), rn_last_error());
     return 1;
   }
   printf("{\"rows\": %lld, \"hidden\": %lld, \"plus_one\": %d, \"calls\": %d, \"us_per_call\": %.3f, "
-         "\"empty_us_per_call\": %.3f, \"ratio\": %.3f}\n",
-         (long long)rows, (long long)hidden, plus_one, calls, t_norm, t_empty, t_norm / t_empty);
+         "\"empty_us_per_call\": %.3f, \"ratio\": %.3f, \"host_enqueue_us\": %.3f, "
+         "\"empty_host_enqueue_us\": %.3f, \"select_and_check_ns\": %.1f}\n",
+         (long long)rows, (long long)hidden, plus_one, calls, t_norm, t_empty, t_norm / t_empty, h_norm, h_empty, q_ns);
   hipStreamDestroy(s);
   hipFree(x);
   hipFree(res);
