@@ -20,6 +20,8 @@
 //     16/32-bit output, one extra partly idle wave often measured 0.5-2%
 //     faster than the exact fit; with fp8 output or no residual the same
 //     extra wave measured up to 25% slower, so the exact fit is the default);
+//     SwiGLU rows have a table of their own (kTunedAct), where extra waves or
+//     vectors often won by 1-6%;
 //   * grid = rows (a workgroup per row; MI355X's dispatcher refills CUs as
 //     workgroups finish, so no persistent loop is needed).
 #include <math.h>
@@ -186,25 +188,36 @@ static const Tuned kTuned[] = {
     {kF32, kF32, false, 16384, 16, 4},
 };
 
-// Launch shape for rows of `hidden` elements; `use_table` consults kTuned
-// (measured for the fused add + RMSNorm with a bf16 weight).
-static rn_status select_rows_shape(int64_t rows, int64_t hidden, const RowKey& key, int num_cus,
-                                   bool use_table, rn_launch_config* cfg) {
+// SwiGLU (bf16 x): fastest (waves, vectors per lane) measured on MI355X,
+// scored like kTuned (geometric mean at 1.2 GB and 0.4 GB per call, five
+// interleaved repetitions), entered where it beat the exact fit by more than
+// half a percent.  Output class: 0 bf16 / f32, 1 fp8 (measured with MX
+// scales), 2 fp4 (measured with NVFP4 scales).
+struct TunedAct {
+  int out_class;
+  int d;
+  int waves, nv;
+};
+static const TunedAct kTunedAct[] = {
+    {0, 4096, 9, 1},   {0, 8192, 12, 2},  {0, 11008, 14, 2}, {0, 13824, 13, 4},
+    {0, 14336, 13, 4}, {0, 18944, 14, 4}, {0, 28672, 16, 4},
+    {1, 13824, 9, 4},  {1, 14336, 9, 4},  {1, 28672, 8, 8},
+    {2, 8192, 8, 2},   {2, 11008, 6, 4},  {2, 13824, 4, 8},  {2, 14336, 4, 8},
+    {2, 28672, 16, 4},
+};
+
+// Launch shape for rows of `hidden` elements: the tabulated (waves, nv) when
+// given (tw > 0) and valid for a prefill-sized call, else the exact fit.
+static rn_status select_rows_shape(int64_t rows, int64_t hidden, const RowKey& key, int num_cus, int tw,
+                                   int tnv, rn_launch_config* cfg) {
   if (num_cus < 1) return fail(RN_ERR_INVALID_ARG, "num_cus must be >= 1");
   const int vec = 16 / (key.x == kBF16 ? 2 : 4);
   const int64_t nvec = hidden / vec;
   const int choices[4] = {1, 2, 4, 8};
   int waves = 0, nv = 0;
-  if (rows > num_cus && use_table) {
-    for (const Tuned& t : kTuned) {
-      if (t.x == key.x && t.res == key.res && t.fp8 == (key.out == kFP8 || key.out == kFP4) &&
-          t.hidden == hidden &&
-          rows_variant_ok(t.waves, t.nv, nvec)) {
-        waves = t.waves;
-        nv = t.nv;
-        break;
-      }
-    }
+  if (rows > num_cus && tw > 0 && rows_variant_ok(tw, tnv, nvec)) {
+    waves = tw;
+    nv = tnv;
   }
   // decode (rows <= CUs, latency bound) and untabulated prefill shapes: the
   // fewest vectors per lane, then the fewest waves that cover the row
@@ -224,7 +237,17 @@ static rn_status select_rows_shape(int64_t rows, int64_t hidden, const RowKey& k
 
 rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int num_cus,
                             rn_launch_config* cfg) {
-  return select_rows_shape(rows, hidden, key, num_cus, key.w == kBF16, cfg);
+  int tw = 0, tnv = 0;
+  if (key.w == kBF16) {  // the table was measured with a bf16 weight
+    for (const Tuned& t : kTuned) {
+      if (t.x == key.x && t.res == key.res && t.fp8 == (key.out == kFP8 || key.out == kFP4) && t.hidden == hidden) {
+        tw = t.waves;
+        tnv = t.nv;
+        break;
+      }
+    }
+  }
+  return select_rows_shape(rows, hidden, key, num_cus, tw, tnv, cfg);
 }
 
 rn_status check_row_config(int64_t rows, int64_t hidden, const RowKey& key,
@@ -268,7 +291,18 @@ rn_status select_act_config(int64_t rows, int64_t d, const ActKey& key, int num_
   rk.qs = key.qs;
   rk.bias = 0;
   rk.nv = 0;
-  return select_rows_shape(rows, d, rk, num_cus, false, cfg);
+  int tw = 0, tnv = 0;
+  if (key.x == kBF16) {
+    const int cls = key.out == kFP8 ? 1 : key.out == kFP4 ? 2 : 0;
+    for (const TunedAct& t : kTunedAct) {
+      if (t.out_class == cls && t.d == d) {
+        tw = t.waves;
+        tnv = t.nv;
+        break;
+      }
+    }
+  }
+  return select_rows_shape(rows, d, rk, num_cus, tw, tnv, cfg);
 }
 
 rn_status check_head_shape(int64_t tokens, int32_t nq, int32_t nk, int32_t head_dim,

@@ -237,6 +237,13 @@ def test_selector_shapes_of_the_workloads():
     assert (c["waves_per_row"], c["vecs_per_lane"]) == (6, 1)
     c = _cfg_res(4096, 10240, "bf16")
     assert (c["waves_per_row"], c["vecs_per_lane"]) == (10, 2)
+    # SwiGLU: its own measured table at prefill sizes, the exact fit for decode
+    a = R.query_silu_mul_config(8192, 14336)
+    assert (a["waves_per_row"], a["vecs_per_lane"]) == (13, 4)
+    a = R.query_silu_mul_config(8192, 14336, out_dtype="fp4_e2m1", scale_scheme="nv16")
+    assert (a["waves_per_row"], a["vecs_per_lane"]) == (4, 8) and a["block_threads"] == 256
+    a = R.query_silu_mul_config(16, 14336)
+    assert (a["waves_per_row"], a["vecs_per_lane"]) == (14, 2)
 
 
 def test_head_mapping_covers_each_row_once():
