@@ -48,24 +48,22 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_digest() -> str:
-    """sha256 over the library's kernel and ABI sources (which counter summaries refer to)."""
+def library_digest() -> str:
+    """sha256 of the built library (what the counter summaries were measured on).
+
+    The build is byte-for-byte reproducible, so this changes exactly when the
+    compiled code does (kernels, selector or ABI), not on comment-only edits."""
+    from residual_add_rmsnorm_rows_amd import _lib as L
+
     h = hashlib.sha256()
-    paths = []
-    for d in (os.path.join(ROOT, "residual_add_rmsnorm_rows_amd", "csrc"), os.path.join(ROOT, "include")):
-        for name in sorted(os.listdir(d)):
-            if name.endswith((".hip", ".h", ".cpp")):
-                paths.append(os.path.join(d, name))
-    for p in paths:
-        h.update(os.path.basename(p).encode())
-        with open(p, "rb") as f:
-            h.update(f.read())
+    with open(L.LIB_PATH, "rb") as f:
+        h.update(f.read())
     return h.hexdigest()
 
 
 def read_traffic(workload: str):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
+    was taken on the library as built now; else None."""
     path = os.path.join(PROFILE_DIR, f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -75,7 +73,7 @@ def read_traffic(workload: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    if fields.get("source_sha256") != source_digest():
+    if fields.get("library_sha256") != library_digest():
         return None
     try:
         return int(float(fields["traffic_bytes_per_launch"]))
@@ -546,7 +544,7 @@ def main() -> int:
         "config": {"workload": f"{MAIN}: {wl.description}", "rows": wl.rows, "hidden": wl.hidden,
                    "x": wl.x_dtype, "residual": wl.res_dtype, "weight": wl.w_dtype, "out": wl.out_dtype,
                    "eps": wl.eps, "launch": cfg, "algorithmic_bytes_per_step": nbytes,
-                   "source_sha256": source_digest()},
+                   "library_sha256": library_digest()},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic},
         "launch_us": {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9), "launches": len(per)},

@@ -31,13 +31,15 @@
 // of a workgroup, so the next row's writes cannot race the current reads).
 // With W == 1 there is no LDS traffic and no barrier (the decode shape).
 //
-// Quantized outputs (fp8 e4m3fn, fp4 e2m1) carry scales at one of three
-// granularities ("Blackwell support" names MXFP8/MXFP4 and FP8 block-wise
-// scaling; the formats follow the OCP FP8 and MX specifications):
+// Quantized outputs (fp8 e4m3fn, fp4 e2m1) carry scales at one of four
+// granularities ("Blackwell support" names MXFP8/MXFP4/NVFP4 and FP8
+// block-wise scaling; the formats follow the OCP FP8 and MX specifications):
 //   per row      scale = amax / 448, codes = e4m3fn(y * 448 / amax);
 //   per 128      the same per group of 128 consecutive elements;
 //   MX per 32    E8M0 scale 2^e with e = floor(log2 amax) - emax (8 for e4m3,
-//                2 for e2m1), codes = encode(y * 2^-e), saturating.
+//                2 for e2m1), codes = encode(y * 2^-e), saturating;
+//   NVFP4 / 16   E4M3FN scale s_b = e4m3fn(amax / (6 s_t)) with the caller's
+//                float32 tensor scale s_t, codes = e2m1(y / (s_b s_t)).
 //
 // This file is compiled once per (x dtype, out dtype, scale scheme), selected
 // by RN_TU_X / RN_TU_OUT / RN_TU_QS / RN_TU_NAME, so the variants build in
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowA
     }
     const float inv = rsqrtf(ss / static_cast<float>(a.hidden) + a.eps);
 
-    // 4. Scale and store.  Scale groups (per 128 or per 32 elements) are GL
+    // 4. Scale and store.  Scale groups (per 128, 32 or 16 elements) are GL
     //    neighbouring lanes of one chunk: their max is a DPP group reduction,
     //    and the group's first lane stores its scale (and amax).
     float amax = 0.f, qmul = 0.f;

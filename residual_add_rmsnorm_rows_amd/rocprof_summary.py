@@ -101,7 +101,7 @@ def traffic(fetch_csv: str, write_csv: str, kernel: str, bench_out: str, command
         f"# command (FETCH_SIZE; the WRITE_SIZE run differs only in the counter): {command}",
         f"kernel: {names[0]}",
         f"workload: {workload}",
-        f"source_sha256: {bench['config']['source_sha256']}",
+        f"library_sha256: {bench['config']['library_sha256']}",
         f"dispatches_fetch: {len(fetch_k)}",
         f"dispatches_write: {len(write_k)}",
         f"fetch_size_kib_per_dispatch: {statistics.mean(fetch_k):.1f}",
