@@ -122,7 +122,7 @@ def qknorm_bytes(wl) -> int:
 class RowCall:
     """Device buffers of one fused add+RMSNorm workload and a raw C-ABI call over them."""
 
-    def __init__(self, wl, inputs, sets: int = 1, scale_scheme: str = "row"):
+    def __init__(self, wl, inputs, sets: int = 1, scale_scheme: str = "row", config=None):
         import torch
         from residual_add_rmsnorm_rows_amd import _lib as L
         from tests.gpu_util import TORCH_DTYPES, to_dev
@@ -147,11 +147,22 @@ class RowCall:
                                   scale_scheme)
         self.ts = (torch.tensor([NV_TENSOR_SCALE[wl.name]], dtype=torch.float32, device="cuda")
                    if scale_scheme == "nv16" else None)
+        self.config = config  # an explicit rn_launch_config, or None for the selector's
         self.i = 0
 
     def __call__(self, stream: int) -> None:
         xs, rs, out, ro, sc = self.sets[self.i]
         self.i = (self.i + 1) % len(self.sets)
+        if self.config is not None:
+            st = self.L.rmsnorm_fwd_config(xs.data_ptr(), None if rs is None else rs.data_ptr(), self.w.data_ptr(),
+                                           out.data_ptr(), None if ro is None else ro.data_ptr(),
+                                           None if sc is None else sc.data_ptr(), None,
+                                           None if self.ts is None else self.ts.data_ptr(), self.wl.rows,
+                                           self.wl.hidden, self.wl.eps, self.flags, ctypes.byref(self.config), stream)
+            if st != 0:
+                from residual_add_rmsnorm_rows_amd._lib import check
+                check(st)
+            return
         st = self.L.rmsnorm_fwd_ex(xs.data_ptr(), None if rs is None else rs.data_ptr(), self.w.data_ptr(),
                                    out.data_ptr(), None if ro is None else ro.data_ptr(),
                                    None if sc is None else sc.data_ptr(), None,
@@ -258,6 +269,7 @@ def native_decode_latency(name: str, calls: int = 2000) -> dict:
 
 def decode_metrics(name: str) -> dict:
     import workloads as WL
+    import residual_add_rmsnorm_rows_amd as R
     from residual_add_rmsnorm_rows_amd import _lib as L
 
     wl = WL.WORKLOADS[name]
@@ -271,12 +283,25 @@ def decode_metrics(name: str) -> dict:
     eager_empty = time_stream_loop(empty, 2000, 100) * 1000.0
     graph = time_graph_loop(call)
     graph_empty = time_graph_loop(empty)
+    # the one-wave-per-row decode shape (the whole row in one wave64's
+    # registers, no LDS, no barrier), timed the same way for comparison
+    vec = 8 if wl.x_dtype == "bf16" else 4
+    cfg = L.LaunchConfig()
+    cfg.kernel, cfg.waves_per_row, cfg.grid = L.RN_KERNEL_ROWS, 1, wl.rows
+    cfg.vecs_per_lane = next(nv for nv in (1, 2, 4, 8) if 64 * nv * vec >= wl.hidden)
+    one = RowCall(wl, WL.generate_rownorm(wl, seed=0), config=cfg)
+    graph_one = time_graph_loop(one)
+    sel = R.query_config(wl.rows, wl.hidden, x_dtype=wl.x_dtype, res_dtype=wl.res_dtype, w_dtype=wl.w_dtype,
+                         out_dtype=wl.out_dtype, weight_plus_one=wl.weight_plus_one, num_cus=0)
     return {
         "workload": wl.description, "rows": wl.rows, "hidden": wl.hidden,
+        "launch": {"waves_per_row": sel["waves_per_row"], "vecs_per_lane": sel["vecs_per_lane"]},
         "us_per_call_eager": round(eager, 3), "empty_us_per_call_eager": round(eager_empty, 3),
         "ratio_eager": round(eager / eager_empty, 3),
         "us_per_call_graph": round(graph, 3), "empty_us_per_call_graph": round(graph_empty, 3),
         "ratio_graph": round(graph / graph_empty, 3),
+        "one_wave_per_row": {"vecs_per_lane": cfg.vecs_per_lane, "us_per_call_graph": round(graph_one, 3),
+                             "ratio_graph": round(graph_one / graph_empty, 3)},
         "algorithmic_bytes": rownorm_bytes(wl),
     }
 

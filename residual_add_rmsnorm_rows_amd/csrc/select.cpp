@@ -8,11 +8,15 @@
 // decode variant with one warp per block when there are fewer warps than SMs;
 // this is the MI355X version of that idea, tuned by measurement):
 //   * vec = 16 bytes of x per lane (8 bf16 or 4 f32): global_load_dwordx4;
-//   * decode shape (rows <= compute units): the data is small and the call is
-//     latency bound, so a row is spread over as many waves as give each lane a
-//     single vector (up to 16 waves; longer rows take 2, 4 or 8 vectors per
-//     lane).  Measured on MI355X for 256 x 4096 bf16: 8 waves x 1 vector per
-//     lane take 2.7 us per call against 4.5 us for one wave x 8 vectors;
+//   * decode shape of the norm kernels (rows <= compute units): the call is
+//     latency bound.  A row
+//     of at most 128 lane vectors stays in one wave (one or two vectors per
+//     lane: no LDS and no barrier); a longer row is spread over at most 8
+//     waves with the fewest vectors per lane that cover it.  Measured on
+//     MI355X (graph launches, 1-256 rows): 1024 wide, 1 wave x 2 vectors beat
+//     2 x 1 by 3-5%; 4096 wide, 8 x 1 took 2.7 us per call against 3.1 us for
+//     one wave x 8 vectors; 8192 wide, 8 x 2 beat 16 x 1 by 5-8%.  (SwiGLU
+//     decode keeps the exact fit: see select_act_config);
 //   * prefill shape: for the dtype classes and hidden sizes that were
 //     measured on MI355X (2048..16384 wide rows), the fastest variant of an
 //     interleaved sweep is taken from a table (kTuned below); otherwise the
@@ -207,9 +211,11 @@ static const TunedAct kTunedAct[] = {
 };
 
 // Launch shape for rows of `hidden` elements: the tabulated (waves, nv) when
-// given (tw > 0) and valid for a prefill-sized call, else the exact fit.
+// given (tw > 0) and valid for a prefill-sized call; for a decode-sized call
+// with `compact_decode`, the decode rule above; else the exact fit with the
+// fewest vectors per lane.
 static rn_status select_rows_shape(int64_t rows, int64_t hidden, const RowKey& key, int num_cus, int tw,
-                                   int tnv, rn_launch_config* cfg) {
+                                   int tnv, bool compact_decode, rn_launch_config* cfg) {
   if (num_cus < 1) return fail(RN_ERR_INVALID_ARG, "num_cus must be >= 1");
   const int vec = 16 / (key.x == kBF16 ? 2 : 4);
   const int64_t nvec = hidden / vec;
@@ -219,8 +225,20 @@ static rn_status select_rows_shape(int64_t rows, int64_t hidden, const RowKey& k
     waves = tw;
     nv = tnv;
   }
-  // decode (rows <= CUs, latency bound) and untabulated prefill shapes: the
-  // fewest vectors per lane, then the fewest waves that cover the row
+  // decode (rows <= CUs, latency bound): one wave for rows of at most 128
+  // vectors, else at most 8 waves with the fewest vectors per lane
+  if (!nv && rows <= num_cus && compact_decode) {
+    for (int f : choices) {
+      const int64_t w = nvec <= 128 ? 1 : (nvec + 64 * f - 1) / (64 * f) < 8 ? (nvec + 64 * f - 1) / (64 * f) : 8;
+      if (rows_variant_ok(static_cast<int>(w), f, nvec)) {
+        waves = static_cast<int>(w);
+        nv = f;
+        break;
+      }
+    }
+  }
+  // untabulated prefill shapes: the fewest vectors per lane, then the fewest
+  // waves that cover the row
   for (int f : choices) {
     if (nv) break;
     int64_t w = (nvec + 64 * f - 1) / (64 * f);
@@ -247,7 +265,7 @@ rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int
       }
     }
   }
-  return select_rows_shape(rows, hidden, key, num_cus, tw, tnv, cfg);
+  return select_rows_shape(rows, hidden, key, num_cus, tw, tnv, true, cfg);
 }
 
 rn_status check_row_config(int64_t rows, int64_t hidden, const RowKey& key,
@@ -302,7 +320,10 @@ rn_status select_act_config(int64_t rows, int64_t d, const ActKey& key, int num_
       }
     }
   }
-  return select_rows_shape(rows, d, rk, num_cus, tw, tnv, cfg);
+  // SwiGLU decode keeps the exact fit: its rows load two tensors, and for
+  // 11008 / 14336 wide rows at 1-64 tokens 11-16 waves x 2 vectors measured
+  // 6-16% faster than the rows kernel's 8-wave cap
+  return select_rows_shape(rows, d, rk, num_cus, tw, tnv, false, cfg);
 }
 
 rn_status check_head_shape(int64_t tokens, int32_t nq, int32_t nk, int32_t head_dim,

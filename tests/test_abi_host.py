@@ -223,10 +223,15 @@ def test_selector_covers_every_row(x):
 
 
 def test_selector_shapes_of_the_workloads():
-    # decode: latency bound, one vector per lane spread over as many waves as needed
+    # decode: latency bound; one wave for rows of at most 128 vectors, else at
+    # most 8 waves with the fewest vectors per lane
     c1, c2 = _cfg(8, 1024), _cfg(256, 4096)
-    assert (c1["waves_per_row"], c1["vecs_per_lane"]) == (2, 1)
+    assert (c1["waves_per_row"], c1["vecs_per_lane"]) == (1, 2)
     assert (c2["waves_per_row"], c2["vecs_per_lane"]) == (8, 1)
+    c = _cfg(8, 8192)
+    assert (c["waves_per_row"], c["vecs_per_lane"]) == (8, 2)
+    c = _cfg(8, 32768)
+    assert (c["waves_per_row"], c["vecs_per_lane"]) == (8, 8)
     # prefill: the measured table (bf16 x with an f32 or bf16 residual stream)
     c3 = _cfg_res(16384, 8192, "f32")
     assert (c3["waves_per_row"], c3["vecs_per_lane"]) == (16, 1)

@@ -151,6 +151,27 @@ def _variants(hidden, vec):
                 yield W, NV
 
 
+@pytest.mark.parametrize("name", ["decode_8x1024", "decode_256x4096"])
+def test_decode_one_wave_per_row(name):
+    """The one-wave64-per-row decode shape (whole row in one wave's registers,
+    no LDS, no barrier) on the decode workloads, next to the selector's shape."""
+    wl = WL.WORKLOADS[name]
+    inputs = WL.generate_rownorm(wl, seed=0)
+    vec = 8
+    nv = next(n for n in (1, 2, 4, 8) if 64 * n * vec >= wl.hidden)
+    cfg = L.LaunchConfig()
+    cfg.kernel, cfg.waves_per_row, cfg.vecs_per_lane, cfg.grid = L.RN_KERNEL_ROWS, 1, nv, wl.rows
+    _announce(f"{name} one wave per row, {nv} vectors per lane")
+    r1 = run_rownorm(wl, inputs, config=cfg)
+    rep = judge(wl, inputs, r1)
+    assert rep["ok"], rep
+    r2 = run_rownorm(wl, inputs)
+    # both shapes sum in float32 in different orders: equal within the same bar, and
+    # the updated residual (no reduction involved) bit-identical
+    assert np.array_equal(to_host(r1.residual_out), to_host(r2.residual_out))
+    assert judge(wl, inputs, r2)["ok"]
+
+
 @pytest.mark.parametrize("hidden,x,out", [(8192, "bf16", "bf16"), (7168, "bf16", "fp8_e4m3fn"),
                                           (1000, "bf16", "bf16"), (1000, "f32", "f32"), (64, "bf16", "bf16"),
                                           (8, "bf16", "fp8_e4m3fn"), (3072, "f32", "bf16")])
