@@ -17,13 +17,21 @@
  * residual add): h = round_res(x + residual) is written to residual_out and the
  * norm is taken over that rounded h.  It can also quantize y to OCP fp8 E4M3FN
  * with one dynamic scale per row: scale = amax / 448, amax = max_i |y_i|,
- * code_i = round_nearest_even(y_i / scale) saturated to +-448.  Neither the
- * residual add nor the fp8 output is on the pages; both follow the plain
- * reading stated for each entry point below.
+ * code_i = round_nearest_even(y_i / scale) saturated to +-448, or with the
+ * block-scaled schemes of RN_SCALE_* below (fp8 per 128 elements; MX per 32,
+ * fp8 or fp4 E2M1; NVFP4 per 16).  Neither the residual add nor the quantized
+ * outputs' formulas are on the pages; both follow the plain reading stated
+ * for each entry point below.
  *
  * qknorm_fwd applies the same RMSNorm to every (token, head) row of Q and K
  * over head_dim, with one weight vector per tensor shared by all heads, as in
  * the "QK Norm" section's kernel (heads of Q first, then heads of K, per token).
+ *
+ * silu_mul_fwd is the SwiGLU activation over rows of a merged gate/up
+ * projection, with the same output types as rmsnorm_fwd.
+ *
+ * rn_launch_empty and rn_launch_copy are measurement references (bare launch
+ * latency; streaming-copy bandwidth) launched through the same path.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
