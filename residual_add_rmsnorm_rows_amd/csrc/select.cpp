@@ -26,6 +26,8 @@
 //     extra wave measured up to 25% slower, so the exact fit is the default);
 //     SwiGLU rows have a table of their own (kTunedAct), where extra waves or
 //     vectors often won by 1-6%;
+//   * mid-size shape (CUs < rows <= 16 x CUs): a table per rows-per-CU bucket
+//     (kTunedMid), falling back to the prefill table;
 //   * grid = rows (a workgroup per row; MI355X's dispatcher refills CUs as
 //     workgroups finish, so no persistent loop is needed).
 #include <math.h>
@@ -192,6 +194,53 @@ static const Tuned kTuned[] = {
     {kF32, kF32, false, 16384, 16, 4},
 };
 
+// Mid-size calls (more rows than compute units, at most 16 per CU: chunked
+// prefill, large decode batches): fastest (waves, vectors per lane) measured
+// on MI355X, scored by the geometric mean of a cache-warm call (one buffer
+// set, reused) and a cold one (buffers rotated past the 256 MB Infinity
+// Cache), three interleaved repetitions, at 2, 4, 8 and 16 rows per CU;
+// entered where it beat the streaming-prefill choice by at least 3%.  Fewer
+// waves holding more vectors per lane win here: with at most 16 rows per CU
+// the whole grid is resident at once, and each lane keeps more loads in
+// flight.  Key as kTuned, plus cu_mult: the entry serves rows in
+// ((cu_mult / 2) * CUs, cu_mult * CUs].
+struct TunedMid {
+  int x, res;
+  bool fp8;
+  int hidden;
+  int cu_mult;
+  int waves, nv;
+};
+static const TunedMid kTunedMid[] = {
+    {kBF16, kBF16, false, 2048, 2, 2, 2}, {kBF16, kBF16, false, 2048, 4, 2, 2}, {kBF16, kBF16, false, 2048, 8, 1, 4},
+    {kBF16, kBF16, false, 4096, 2, 5, 2}, {kBF16, kBF16, false, 4096, 4, 1, 8}, {kBF16, kBF16, false, 4096, 8, 1, 8},
+    {kBF16, kBF16, false, 5120, 2, 5, 2}, {kBF16, kBF16, false, 5120, 4, 2, 8}, {kBF16, kBF16, false, 5120, 8, 8, 2},
+    {kBF16, kBF16, false, 7168, 2, 7, 2}, {kBF16, kBF16, false, 7168, 4, 2, 8}, {kBF16, kBF16, false, 8192, 2, 8, 2},
+    {kBF16, kBF16, false, 8192, 4, 2, 8}, {kBF16, kBF16, false, 8192, 8, 2, 8}, {kBF16, kBF16, false, 12288, 2, 3, 8},
+    {kBF16, kBF16, false, 12288, 4, 3, 8}, {kBF16, kBF16, false, 16384, 2, 4, 8}, {kBF16, kBF16, false, 16384, 4, 4, 8},
+    {kBF16, kF32, false, 2048, 2, 1, 4}, {kBF16, kF32, false, 2048, 4, 1, 4}, {kBF16, kF32, false, 2048, 8, 1, 4},
+    {kBF16, kF32, false, 2048, 16, 1, 4}, {kBF16, kF32, false, 4096, 2, 1, 8}, {kBF16, kF32, false, 4096, 4, 1, 8},
+    {kBF16, kF32, false, 4096, 8, 1, 8}, {kBF16, kF32, false, 5120, 2, 2, 8}, {kBF16, kF32, false, 5120, 4, 2, 8},
+    {kBF16, kF32, false, 7168, 2, 2, 8}, {kBF16, kF32, false, 7168, 4, 2, 8}, {kBF16, kF32, false, 8192, 2, 2, 8},
+    {kBF16, kF32, false, 12288, 2, 3, 8}, {kBF16, kBF16, true, 2048, 8, 1, 4}, {kBF16, kBF16, true, 5120, 8, 8, 2},
+    {kBF16, kBF16, true, 16384, 2, 4, 8}, {kBF16, kBF16, true, 16384, 4, 16, 2}, {kBF16, kBF16, true, 16384, 8, 16, 2},
+    {kBF16, kF32, true, 2048, 2, 4, 1}, {kBF16, kF32, true, 2048, 4, 1, 4}, {kBF16, kF32, true, 2048, 8, 1, 4},
+    {kBF16, kF32, true, 2048, 16, 4, 1}, {kBF16, kF32, true, 4096, 4, 2, 4}, {kBF16, kF32, true, 4096, 8, 1, 8},
+    {kBF16, kF32, true, 5120, 2, 3, 4}, {kBF16, kF32, true, 5120, 4, 2, 8}, {kBF16, kF32, true, 7168, 2, 4, 4},
+    {kBF16, kF32, true, 7168, 4, 2, 8}, {kBF16, kF32, true, 8192, 2, 4, 4}, {kBF16, kF32, true, 8192, 4, 2, 8},
+    {kBF16, kF32, true, 12288, 2, 4, 8}, {kBF16, kF32, true, 16384, 2, 4, 8}, {kBF16, kNone, false, 2048, 2, 1, 4},
+    {kBF16, kNone, false, 2048, 4, 1, 4}, {kBF16, kNone, false, 2048, 8, 2, 2}, {kBF16, kNone, false, 2048, 16, 1, 4},
+    {kBF16, kNone, false, 4096, 2, 8, 1}, {kBF16, kNone, false, 4096, 4, 1, 8}, {kBF16, kNone, false, 4096, 8, 1, 8},
+    {kBF16, kNone, false, 5120, 2, 3, 4}, {kBF16, kNone, false, 5120, 4, 5, 2}, {kBF16, kNone, false, 5120, 8, 3, 4},
+    {kBF16, kNone, false, 5120, 16, 5, 2}, {kBF16, kNone, false, 7168, 4, 2, 8}, {kBF16, kNone, false, 8192, 2, 4, 4},
+    {kBF16, kNone, false, 8192, 4, 2, 8}, {kBF16, kNone, false, 8192, 8, 2, 8}, {kBF16, kNone, false, 12288, 2, 3, 8},
+    {kBF16, kNone, false, 12288, 4, 3, 8}, {kBF16, kNone, false, 16384, 2, 4, 8}, {kF32, kF32, false, 2048, 2, 1, 8},
+    {kF32, kF32, false, 2048, 4, 1, 8}, {kF32, kF32, false, 2048, 8, 1, 8}, {kF32, kF32, false, 4096, 2, 2, 8},
+    {kF32, kF32, false, 4096, 4, 2, 8}, {kF32, kF32, false, 4096, 8, 2, 8}, {kF32, kF32, false, 5120, 2, 3, 8},
+    {kF32, kF32, false, 5120, 4, 5, 4}, {kF32, kF32, false, 7168, 2, 4, 8}, {kF32, kF32, false, 7168, 4, 4, 8},
+    {kF32, kF32, false, 8192, 2, 4, 8}, {kF32, kF32, false, 8192, 4, 4, 8},
+};
+
 // SwiGLU (bf16 x): fastest (waves, vectors per lane) measured on MI355X,
 // scored like kTuned (geometric mean at 1.2 GB and 0.4 GB per call, five
 // interleaved repetitions), entered where it beat the exact fit by more than
@@ -256,9 +305,24 @@ static rn_status select_rows_shape(int64_t rows, int64_t hidden, const RowKey& k
 rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int num_cus,
                             rn_launch_config* cfg) {
   int tw = 0, tnv = 0;
-  if (key.w == kBF16) {  // the table was measured with a bf16 weight
+  const bool quant = key.out == kFP8 || key.out == kFP4;
+  if (key.w == kBF16 && num_cus >= 1 && rows > num_cus) {  // the tables were measured with a bf16 weight
+    int bucket = 0;  // rows per CU, rounded up to 2, 4, 8 or 16; 0 above that
+    for (int b = 2; b <= 16; b *= 2) {
+      if (rows <= static_cast<int64_t>(b) * num_cus) {
+        bucket = b;
+        break;
+      }
+    }
+    for (const TunedMid& t : kTunedMid) {
+      if (bucket && t.x == key.x && t.res == key.res && t.fp8 == quant && t.hidden == hidden && t.cu_mult == bucket) {
+        tw = t.waves;
+        tnv = t.nv;
+        break;
+      }
+    }
     for (const Tuned& t : kTuned) {
-      if (t.x == key.x && t.res == key.res && t.fp8 == (key.out == kFP8 || key.out == kFP4) && t.hidden == hidden) {
+      if (tw == 0 && t.x == key.x && t.res == key.res && t.fp8 == quant && t.hidden == hidden) {
         tw = t.waves;
         tnv = t.nv;
         break;

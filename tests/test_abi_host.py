@@ -242,6 +242,11 @@ def test_selector_shapes_of_the_workloads():
     assert (c["waves_per_row"], c["vecs_per_lane"]) == (6, 1)
     c = _cfg_res(4096, 10240, "bf16")
     assert (c["waves_per_row"], c["vecs_per_lane"]) == (10, 2)
+    # mid-size calls: their own table per rows-per-CU bucket
+    c = _cfg_res(1024, 8192, "bf16")
+    assert (c["waves_per_row"], c["vecs_per_lane"]) == (2, 8)
+    c = _cfg_res(4097, 8192, "bf16")  # above 16 rows per CU: the prefill table
+    assert (c["waves_per_row"], c["vecs_per_lane"]) == (16, 1)
     # SwiGLU: its own measured table at prefill sizes, the exact fit for decode
     a = R.query_silu_mul_config(8192, 14336)
     assert (a["waves_per_row"], a["vecs_per_lane"]) == (13, 4)
