@@ -259,6 +259,26 @@ static const TunedAct kTunedAct[] = {
     {2, 28672, 16, 4},
 };
 
+// SwiGLU mid-size calls (CUs < rows <= 16 x CUs), measured and entered as
+// kTunedMid (warm/cold geometric mean, at least 3% over kTunedAct's choice).
+struct TunedActMid {
+  int out_class;
+  int d;
+  int cu_mult;
+  int waves, nv;
+};
+static const TunedActMid kTunedActMid[] = {
+    {0, 4096, 4, 8, 1}, {0, 4096, 8, 1, 8}, {0, 8192, 2, 8, 2}, {0, 8192, 4, 2, 8},
+    {0, 8192, 8, 8, 2}, {0, 11008, 2, 3, 8}, {0, 11008, 4, 6, 4}, {0, 13824, 2, 4, 8},
+    {0, 13824, 4, 16, 2}, {0, 13824, 8, 16, 2}, {0, 14336, 2, 4, 8}, {0, 14336, 4, 16, 2},
+    {0, 14336, 8, 16, 2}, {0, 18944, 2, 12, 4}, {1, 11008, 4, 6, 4}, {1, 13824, 2, 16, 2},
+    {1, 13824, 4, 8, 4}, {1, 13824, 8, 8, 4}, {1, 13824, 16, 8, 4}, {1, 14336, 2, 16, 2},
+    {1, 14336, 4, 8, 4}, {1, 14336, 8, 8, 4}, {1, 18944, 2, 12, 4}, {1, 18944, 4, 12, 4},
+    {2, 8192, 2, 16, 1}, {2, 11008, 2, 12, 2}, {2, 13824, 2, 15, 2}, {2, 13824, 4, 7, 4},
+    {2, 13824, 8, 8, 4}, {2, 13824, 16, 8, 4}, {2, 14336, 2, 16, 2}, {2, 14336, 4, 7, 4},
+    {2, 14336, 8, 8, 4},
+};
+
 // Launch shape for rows of `hidden` elements: the tabulated (waves, nv) when
 // given (tw > 0) and valid for a prefill-sized call; for a decode-sized call
 // with `compact_decode`, the decode rule above; else the exact fit with the
@@ -374,10 +394,24 @@ rn_status select_act_config(int64_t rows, int64_t d, const ActKey& key, int num_
   rk.bias = 0;
   rk.nv = 0;
   int tw = 0, tnv = 0;
-  if (key.x == kBF16) {
+  if (key.x == kBF16 && num_cus >= 1 && rows > num_cus) {
     const int cls = key.out == kFP8 ? 1 : key.out == kFP4 ? 2 : 0;
+    int bucket = 0;  // rows per CU, rounded up to 2, 4, 8 or 16; 0 above that
+    for (int b = 2; b <= 16; b *= 2) {
+      if (rows <= static_cast<int64_t>(b) * num_cus) {
+        bucket = b;
+        break;
+      }
+    }
+    for (const TunedActMid& t : kTunedActMid) {
+      if (bucket && t.out_class == cls && t.d == d && t.cu_mult == bucket) {
+        tw = t.waves;
+        tnv = t.nv;
+        break;
+      }
+    }
     for (const TunedAct& t : kTunedAct) {
-      if (t.out_class == cls && t.d == d) {
+      if (tw == 0 && t.out_class == cls && t.d == d) {
         tw = t.waves;
         tnv = t.nv;
         break;
