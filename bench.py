@@ -307,7 +307,7 @@ def decode_metrics(name: str) -> dict:
 
 
 def stream_metrics(name: str, steps: int, warmup: int, sets: int, out_dtype=None,
-                   scale_scheme: str = "row") -> dict:
+                   scale_scheme: str = "row", rows=None) -> dict:
     from dataclasses import replace
 
     import workloads as WL
@@ -315,6 +315,8 @@ def stream_metrics(name: str, steps: int, warmup: int, sets: int, out_dtype=None
     wl = WL.WORKLOADS[name]
     if out_dtype is not None:
         wl = replace(wl, out_dtype=out_dtype)
+    if rows is not None:
+        wl = wl.with_rows(rows)
     call = RowCall(wl, WL.generate_rownorm(wl, seed=0), sets=sets, scale_scheme=scale_scheme)
     ms = time_stream_loop(call, steps, warmup)
     b = rownorm_bytes(wl, scale_scheme=scale_scheme)
@@ -322,6 +324,8 @@ def stream_metrics(name: str, steps: int, warmup: int, sets: int, out_dtype=None
     if wl.out_dtype in QUANT_TEXT:
         desc = (f"prefill fused add+RMSNorm, {wl.rows} x {wl.hidden} {wl.x_dtype} x and residual "
                 f"(1% outliers x20), {QUANT_TEXT[wl.out_dtype]} out with {SCHEME_TEXT[scale_scheme]}")
+    if rows is not None:
+        desc = f"{desc}; {rows} of its rows, one GPU's share when the rows are split over GPUs"
     return {"workload": desc, "out": wl.out_dtype, "scale_scheme": scale_scheme,
             "us_per_call": round(ms * 1000, 3), "algorithmic_bytes": b,
             "GBps": round(b / (ms * 1e-3) / 1e9, 1), "frac_of_peak": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -615,6 +619,8 @@ def main() -> int:
                 sec[name]["c_abi_eager"] = native[name]
         log("qknorm_4096x32x128")
         sec["qknorm_4096x32x128"] = qknorm_metrics(args.steps * 4, args.warmup)
+        log("one GPU's share of the headline step over 8 GPUs (2048 x 8192)")
+        sec["prefill_16384x8192_share_of_8"] = stream_metrics(MAIN, args.steps * 4, args.warmup, sets=3, rows=2048)
         log("prefill_fp8_8192x7168")
         sec["prefill_fp8_8192x7168"] = stream_metrics("prefill_fp8_8192x7168", args.steps, args.warmup, sets=3)
         log("block-scaled outputs on the 8192 x 7168 prefill")
