@@ -14,7 +14,14 @@ Tolerances (the stated target of the work):
     magnitude index (code & 0x7F, negated for negative codes), so +0 and -0
     are the same point and crossing zero costs the steps on either side;
   * bit-exact where one correctly rounded operation fixes the result (the
-    updated residual).
+    updated residual);
+  * rounding discipline (check_rounding), on top of the bounds above: every
+    rounded output (bf16 values, fp8 / fp4 codes) equals the round-to-nearest-
+    even value of the exact result, except where the exact value lies within
+    NEAR_MIDPOINT_REL (relative) of the midpoint between the two neighbours.
+    There the implementation's own float32 evaluation (sum order, rsqrt,
+    hardware exp / reciprocal: a few 1e-6 relative) may land on either side.
+    The one-step bounds alone would also accept a truncating conversion.
 """
 
 from __future__ import annotations
@@ -23,9 +30,16 @@ from typing import Dict
 
 import numpy as np
 
-from .rownorm import BF16, bf16_decode
+from .rownorm import BF16, Format, bf16_decode, round_to_format
 
-__all__ = ["bf16_ulp", "check_bf16", "check_f32", "check_fp8_codes", "check_fp4_codes", "signed_index"]
+__all__ = ["NEAR_MIDPOINT_REL", "bf16_ulp", "check_bf16", "check_f32", "check_fp8_codes", "check_fp4_codes",
+           "check_rounding", "signed_index"]
+
+# Window around a rounding midpoint inside which either neighbour is accepted:
+# 2^-15 relative, about 5x the float32 evaluation error of the kernels' values
+# (float32 sums of up to 32768 squares in any order: ~sqrt(H) * 2^-24; the
+# hardware exp2 / reciprocal forms: ~2^-18).
+NEAR_MIDPOINT_REL = 2.0 ** -15
 
 
 def bf16_ulp(v: np.ndarray) -> np.ndarray:
@@ -37,8 +51,15 @@ def bf16_ulp(v: np.ndarray) -> np.ndarray:
     return np.ldexp(1.0, e - (BF16.precision - 1))
 
 
+# Absolute midpoint window for bf16 values in float32's subnormal range, where
+# the implementation's float32 intermediates carry absolute (not relative)
+# errors of a few 2^-149.
+BF16_SUBNORMAL_WINDOW = 2.0 ** -140
+
+
 def check_bf16(gpu_bits: np.ndarray, exact: np.ndarray) -> Dict[str, float]:
-    """bf16 bits vs exact doubles: pass iff every |gpu - exact| <= ulp(exact)."""
+    """bf16 bits vs exact doubles: pass iff every |gpu - exact| <= ulp(exact) and the
+    rounding discipline holds (``check_rounding``)."""
     g = bf16_decode(gpu_bits)
     y = np.asarray(exact, dtype=np.float64)
     err = np.abs(g - y)
@@ -46,8 +67,10 @@ def check_bf16(gpu_bits: np.ndarray, exact: np.ndarray) -> Dict[str, float]:
     finite = np.isfinite(y)
     ok = np.where(finite, err <= ulp, np.isnan(g) == np.isnan(y))
     ratio = np.where(finite, err / ulp, 0.0)
-    return {"ok": bool(ok.all()), "max_ulp": float(ratio.max(initial=0.0)),
-            "n_bad": int((~ok).sum()), "n": int(ok.size)}
+    rnd = check_rounding(g[finite], y[finite], BF16, abs_tol=BF16_SUBNORMAL_WINDOW)
+    return {"ok": bool(ok.all()) and rnd["ok"], "max_ulp": float(ratio.max(initial=0.0)),
+            "n_bad": int((~ok).sum()), "n_bad_rounding": rnd["n_bad"],
+            "n_near_midpoint_other_side": rnd["n_near_midpoint_other_side"], "n": int(ok.size)}
 
 
 F32_MIN_NORMAL = 2.0 ** -126
@@ -87,3 +110,24 @@ def check_fp4_codes(gpu: np.ndarray, ref: np.ndarray, max_steps: int = 1) -> Dic
     return {"ok": bool((d <= max_steps).all()), "max_steps": int(d.max(initial=0)),
             "frac_exact": float((d == 0).mean()) if d.size else 1.0, "n_bad": int((d > max_steps).sum()),
             "n": int(d.size)}
+
+
+def check_rounding(gpu_values: np.ndarray, exact: np.ndarray, fmt: Format, rel_tol: float = NEAR_MIDPOINT_REL,
+                   abs_tol: float = 0.0) -> Dict[str, float]:
+    """Round-to-nearest-even discipline of rounded outputs.
+
+    ``gpu_values`` are the implementation's outputs decoded to doubles,
+    ``exact`` the exact values they round.  Every output must equal the
+    correctly rounded exact value (``round_to_format``), or be its other
+    neighbour with the exact value within ``max(rel_tol |v|, abs_tol)`` of the
+    midpoint between the two.
+    """
+    g = np.asarray(gpu_values, dtype=np.float64)
+    v = np.asarray(exact, dtype=np.float64)
+    ref = round_to_format(v, fmt)
+    diff = g != ref  # -0.0 == 0.0
+    lo, hi = np.minimum(g, ref), np.maximum(g, ref)
+    near = (v >= lo) & (v <= hi) & (np.abs(v - (lo + hi) / 2) <= np.maximum(rel_tol * np.abs(v), abs_tol))
+    bad = diff & ~near
+    return {"ok": bool(not bad.any()), "n_bad": int(bad.sum()), "n_near_midpoint_other_side": int((diff & near).sum()),
+            "n": int(g.size)}

@@ -96,6 +96,14 @@ def judge_y(y: np.ndarray, out_dtype: str, out: np.ndarray, scale=None, amax=Non
         cr = C.check_fp8_codes(out, own(scale))
         rep["codes"] = cr
         rep["ok"] &= cr["ok"]
+        # rounding discipline of the codes against the exact y / scale (GPU scales)
+        if scale_scheme == "row":
+            s64 = np.broadcast_to(scale.astype(np.float64).reshape(-1, 1), y.shape)
+        else:
+            s64 = np.repeat(scale.astype(np.float64).reshape(y.shape[0], -1), 128, axis=1)
+        v = np.where(s64 > 0, y / np.where(s64 > 0, s64, 1.0), 0.0)
+        rep["codes_rounding"] = C.check_rounding(O.e4m3fn_decode(out), v, O.E4M3FN)
+        rep["ok"] &= rep["codes_rounding"]["ok"]
     elif scale_scheme == "nv16":  # NVFP4: E4M3FN block scale per 16, float32 tensor scale
         q = BQ.nvfp4_quantize(y, tensor_scale)
         sc = np.asarray(scale, dtype=np.uint8)
@@ -116,6 +124,10 @@ def judge_y(y: np.ndarray, out_dtype: str, out: np.ndarray, scale=None, amax=Non
         cr = C.check_fp4_codes(BQ.unpack_fp4(out), codes_ref)
         rep["codes"] = cr
         rep["ok"] &= cr["ok"]
+        d = np.repeat(O.e4m3fn_decode(sc) * float(np.float32(tensor_scale)), 16, axis=1)
+        v = np.where(d > 0, y / np.where(d > 0, d, 1.0), 0.0)
+        rep["codes_rounding"] = C.check_rounding(BQ.e2m1_decode(BQ.unpack_fp4(out)), v, BQ.E2M1)
+        rep["ok"] &= rep["codes_rounding"]["ok"]
     else:  # MX, E8M0 scale per 32 elements
         q = BQ.mx_quantize(y, out_dtype)
         se = np.asarray(scale, dtype=np.uint8).astype(np.int64) - 127
@@ -143,5 +155,9 @@ def judge_y(y: np.ndarray, out_dtype: str, out: np.ndarray, scale=None, amax=Non
             cr = C.check_fp8_codes(out, codes_ref)
         rep["codes"] = cr
         rep["ok"] &= cr["ok"]
+        v = np.ldexp(y, -np.repeat(se, 32, axis=1))
+        got = BQ.e2m1_decode(BQ.unpack_fp4(out)) if out_dtype == "fp4_e2m1" else O.e4m3fn_decode(out)
+        rep["codes_rounding"] = C.check_rounding(got, v, BQ.E2M1 if out_dtype == "fp4_e2m1" else O.E4M3FN)
+        rep["ok"] &= rep["codes_rounding"]["ok"]
     rep["y_ok"] = rep.pop("ok")
     return rep
