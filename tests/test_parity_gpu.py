@@ -559,3 +559,50 @@ def test_silu_mul_edge_cases():
     with pytest.raises(R.RNError):
         R.silu_mul(torch.zeros((2, 2 * 1000), dtype=torch.bfloat16, device="cuda"),
                    out_dtype=torch.float8_e4m3fn, scale_scheme="mx32")
+
+
+def test_concurrent_host_threads():
+    """Entry points called from several host threads at once, each on its own
+    stream (default priority): results equal the single-threaded ones bit for
+    bit, and each thread's last-error message is its own."""
+    import threading
+
+    shapes = [("decode_8x1024", 8), ("decode_256x4096", 256), ("prefill_fp8_8192x7168", 96), ("prefill_16384x8192", 64)]
+    jobs = []
+    for name, rows in shapes:
+        wl = WL.WORKLOADS[name].with_rows(rows)
+        inputs = WL.generate_rownorm(wl, seed=21)
+        ref = run_rownorm(wl, inputs)
+        jobs.append((wl, inputs, to_host(ref.out), to_host(ref.residual_out)))
+    _announce("concurrent host threads x4")
+    errors, msgs = [], {}
+    lib = L.lib()
+
+    def worker(k):
+        wl, inputs, ref_out, ref_res = jobs[k]
+        stream = torch.cuda.Stream()  # default priority
+        try:
+            with torch.cuda.stream(stream):
+                for i in range(20):
+                    r = run_rownorm(wl, inputs)
+                    if not (np.array_equal(to_host(r.out), ref_out) and np.array_equal(to_host(r.residual_out), ref_res)):
+                        errors.append((k, i))
+                        return
+            if k == 0:  # a failing call on this thread only
+                st = lib.rmsnorm_fwd(0x10000, None, 0x10000, 0x20000, None, None, 4, 1001, 1e-6, 0, None)
+                msgs[k] = (st, lib.rn_last_error().decode())
+            else:
+                msgs[k] = (0, lib.rn_last_error().decode())
+        except Exception as e:  # noqa: BLE001 -- reported below
+            errors.append((k, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(len(jobs))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    torch.cuda.synchronize()
+    assert not any(t.is_alive() for t in threads)
+    assert not errors, errors
+    assert msgs[0][0] == L.RN_ERR_UNSUPPORTED and msgs[0][1]
+    assert all(msgs[k][1] == "" for k in range(1, len(jobs))), msgs
