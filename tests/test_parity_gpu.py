@@ -606,3 +606,50 @@ def test_concurrent_host_threads():
     assert not errors, errors
     assert msgs[0][0] == L.RN_ERR_UNSUPPORTED and msgs[0][1]
     assert all(msgs[k][1] == "" for k in range(1, len(jobs))), msgs
+
+
+def test_graph_capture_replays():
+    """The entry points captured in one HIP graph (the library records kernel
+    launches only: no memset, no allocation) and replayed several times, with
+    eager work that changes the inputs between replays: every replay equals the
+    eager result for the inputs it saw."""
+    wl = WL.WORKLOADS["prefill_fp8_8192x7168"].with_rows(64)
+    inputs = WL.generate_rownorm(wl, seed=22)
+    x = to_dev(inputs["x"], "bf16")
+    res = to_dev(inputs["residual"], "bf16")
+    w = to_dev(inputs["weight"], "bf16")
+    out = torch.empty_like(x)
+    ro = torch.empty_like(res)
+    q = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device="cuda")
+    act_in = torch.cat([x, res], dim=1).contiguous()
+    act_out = torch.empty_like(x)
+    _announce("graph capture of rmsnorm / fp8 / silu_mul, 4 replays")
+
+    def step():
+        R.fused_add_rmsnorm(x, res, w, wl.eps, out=out, residual_out=ro)
+        r8 = R.fused_add_rmsnorm(x, res, w, wl.eps, out_dtype=torch.float8_e4m3fn, out=q,
+                                 residual_out=torch.empty_like(res))
+        R.silu_mul(act_in, out=act_out)
+        return r8
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=s):
+        r8g = step()
+    for k in range(4):
+        # eager work between replays: new inputs in the captured buffers
+        x.mul_(-1.0 if k % 2 else 0.5)
+        act_in.copy_(torch.cat([x, res], dim=1))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (to_host(out), to_host(ro), to_host(q), to_host(r8g.scale), to_host(act_out))
+        e = R.fused_add_rmsnorm(x, res, w, wl.eps)
+        e8 = R.fused_add_rmsnorm(x, res, w, wl.eps, out_dtype=torch.float8_e4m3fn)
+        ea = R.silu_mul(act_in)
+        torch.cuda.synchronize()
+        want = (to_host(e.out), to_host(e.residual_out), to_host(e8.out), to_host(e8.scale), to_host(ea.out))
+        for a, b in zip(got, want):
+            assert np.array_equal(a, b), k
