@@ -191,6 +191,23 @@ def time_stream_loop(fn, steps: int, warmup: int) -> float:
     return start.elapsed_time(end) / steps
 
 
+def launch_percentiles(fn, launches: int = 50) -> dict:
+    """p10 / p50 / p90 of single-launch durations (each launch between its own
+    pair of events on the launch stream), in microseconds."""
+    import torch
+
+    stream = torch.cuda.current_stream().cuda_stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    for a, b in evs:
+        a.record()
+        fn(stream)
+        b.record()
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) * 1000.0 for a, b in evs)
+    pick = lambda q: round(per[min(len(per) - 1, int(q * len(per)))], 2)  # noqa: E731
+    return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9), "launches": len(per)}
+
+
 def time_graph_loop(fn, calls: int = 200, replays: int = 10) -> float:
     """Average microseconds per call with `calls` calls captured in one HIP graph."""
     import torch
@@ -319,6 +336,7 @@ def stream_metrics(name: str, steps: int, warmup: int, sets: int, out_dtype=None
         wl = wl.with_rows(rows)
     call = RowCall(wl, WL.generate_rownorm(wl, seed=0), sets=sets, scale_scheme=scale_scheme)
     ms = time_stream_loop(call, steps, warmup)
+    spread = launch_percentiles(call)
     b = rownorm_bytes(wl, scale_scheme=scale_scheme)
     desc = wl.description
     if wl.out_dtype in QUANT_TEXT:
@@ -329,7 +347,7 @@ def stream_metrics(name: str, steps: int, warmup: int, sets: int, out_dtype=None
     return {"workload": desc, "out": wl.out_dtype, "scale_scheme": scale_scheme,
             "us_per_call": round(ms * 1000, 3), "algorithmic_bytes": b,
             "GBps": round(b / (ms * 1e-3) / 1e9, 1), "frac_of_peak": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "buffer_sets": sets}
+            "buffer_sets": sets, "launch_us": spread}
 
 
 def qknorm_metrics(steps: int, warmup: int, sets: int = 8) -> dict:
@@ -357,10 +375,11 @@ def qknorm_metrics(steps: int, warmup: int, sets: int = 8) -> dict:
             L.check(st)
 
     ms = time_stream_loop(call, steps, warmup)
+    spread = launch_percentiles(call)
     b = qknorm_bytes(wl)
     return {"workload": wl.description, "us_per_call": round(ms * 1000, 3), "algorithmic_bytes": b,
             "GBps": round(b / (ms * 1e-3) / 1e9, 1), "frac_of_peak": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "buffer_sets": sets}
+            "buffer_sets": sets, "launch_us": spread}
 
 
 def act_metrics(steps: int, warmup: int, out_dtype: str = "bf16", scale_scheme: str = "row", sets: int = 2) -> dict:
@@ -399,6 +418,7 @@ def act_metrics(steps: int, warmup: int, out_dtype: str = "bf16", scale_scheme: 
             L.check(st)
 
     ms = time_stream_loop(call, steps, warmup)
+    spread = launch_percentiles(call)
     size = {"bf16": 2, "f32": 4, "fp8_e4m3fn": 1, "fp4_e2m1": 0.5}
     b = int(wl.rows * (2 * wl.d * size[wl.x_dtype] + wl.d * size[out_dtype] + sb))
     desc = wl.description
@@ -408,7 +428,7 @@ def act_metrics(steps: int, warmup: int, out_dtype: str = "bf16", scale_scheme: 
     return {"workload": desc, "out": out_dtype, "scale_scheme": scale_scheme,
             "us_per_call": round(ms * 1000, 3), "algorithmic_bytes": b,
             "GBps": round(b / (ms * 1e-3) / 1e9, 1), "frac_of_peak": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "buffer_sets": sets, "warmup": warmup}
+            "buffer_sets": sets, "warmup": warmup, "launch_us": spread}
 
 
 def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
@@ -554,14 +574,7 @@ def main() -> int:
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     # per-launch spread: each launch bracketed by its own events (after the timed region)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a, b in evs:
-        a.record()
-        call(stream)
-        b.record()
-    torch.cuda.synchronize()
-    per = sorted(a.elapsed_time(b) * 1000.0 for a, b in evs)
-    pick = lambda q: round(per[min(len(per) - 1, int(q * len(per)))], 2)  # noqa: E731
+    spread = launch_percentiles(call, args.steps)
     nbytes = rownorm_bytes(wl)
     gbs = nbytes / (ms * 1e-3) / 1e9
     log(f"{MAIN}: {ms * 1000:.1f} us/step, {gbs:.1f} GB/s")
@@ -576,7 +589,7 @@ def main() -> int:
                    "library_sha256": library_digest()},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic},
-        "launch_us": {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9), "launches": len(per)},
+        "launch_us": spread,
     }
     del call
     torch.cuda.empty_cache()
