@@ -83,17 +83,6 @@ struct HeadKey {
   int rpl;             // heads per lane group: 1, 2, 4
 };
 
-// Decoded and validated arguments of an rmsnorm call (host side).
-struct RowCall {
-  RowKey key;
-  rn_launch_config cfg;
-};
-
-struct HeadCall {
-  HeadKey key;
-  rn_launch_config cfg;
-};
-
 // --- selector / validation (select.cpp, host only) -------------------------
 
 // Thread-local message for rn_last_error(); returns `st` for convenience.
