@@ -6,30 +6,29 @@
 // Selector rules (the page's "Prefill & decode specialization" section picks
 // a per-thread vector giving 128-bit loads, then the number of warps, then a
 // decode variant with one warp per block when there are fewer warps than SMs;
-// this is the MI355X version of that idea, tuned by measurement):
-//   * vec = 16 bytes of x per lane (8 bf16 or 4 f32): global_load_dwordx4;
-//   * decode shape of the norm kernels (rows <= compute units): the call is
-//     latency bound.  A row
-//     of at most 128 lane vectors stays in one wave (one or two vectors per
-//     lane: no LDS and no barrier); a longer row is spread over at most 8
+// this is the MI355X version of that idea, tuned by measurement and keyed on
+// the token count as well as the row width and dtypes):
+//   * vec = 16 bytes of x per lane (8 bf16 or 4 f32), one 16-byte buffer load;
+//   * decode (rows <= compute units), norm kernels: the call is latency bound.
+//     A row of at most 128 lane vectors stays in one wave (one or two vectors
+//     per lane: no LDS and no barrier); a longer row is spread over at most 8
 //     waves with the fewest vectors per lane that cover it.  Measured on
 //     MI355X (graph launches, 1-256 rows): 1024 wide, 1 wave x 2 vectors beat
 //     2 x 1 by 3-5%; 4096 wide, 8 x 1 took 2.7 us per call against 3.1 us for
-//     one wave x 8 vectors; 8192 wide, 8 x 2 beat 16 x 1 by 5-8%.  (SwiGLU
-//     decode keeps the exact fit: see select_act_config);
-//   * prefill shape: for the dtype classes and hidden sizes that were
-//     measured on MI355X (2048..16384 wide rows), the fastest variant of an
-//     interleaved sweep is taken from a table (kTuned below); otherwise the
-//     exact fit with the fewest vectors per lane.  (With a residual and a
-//     16/32-bit output, one extra partly idle wave often measured 0.5-2%
-//     faster than the exact fit; with fp8 output or no residual the same
-//     extra wave measured up to 25% slower, so the exact fit is the default);
-//     SwiGLU rows have a table of their own (kTunedAct), where extra waves or
-//     vectors often won by 1-6%;
-//   * mid-size shape (CUs < rows <= 16 x CUs): a table per rows-per-CU bucket
-//     (kTunedMid), falling back to the prefill table;
+//     one wave x 8 vectors; 8192 wide, 8 x 2 beat 16 x 1 by 5-8%.  SwiGLU
+//     decode keeps the exact fit (see select_act_config);
+//   * mid-size (compute units < rows <= 16 x compute units: chunked prefill,
+//     large decode batches): a table per rows-per-CU bucket (kTunedMid,
+//     kTunedActMid), falling back to the prefill tables;
+//   * prefill: for the dtype classes and hidden sizes that were measured
+//     (2048..16384 wide rows), the fastest variant of an interleaved sweep
+//     from a table (kTuned; kTunedAct for SwiGLU); otherwise the exact fit
+//     with the fewest vectors per lane.  (With a residual and a 16/32-bit
+//     output, one extra partly idle wave often measured 0.5-2% faster than
+//     the exact fit; with fp8 output or no residual the same extra wave
+//     measured up to 25% slower, so the exact fit is the default);
 //   * grid = rows (a workgroup per row; MI355X's dispatcher refills CUs as
-//     workgroups finish, so no persistent loop is needed).
+//     workgroups finish, and persistent grids measured 1-7% slower).
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
