@@ -1,5 +1,7 @@
-"""MI355X-native (gfx950) row normalization: fused residual add + RMSNorm,
-per-head QK-norm, and fp8 e4m3fn output with a per-row scale.
+"""MI355X-native (gfx950) row kernels: fused residual add + RMSNorm, per-head
+QK-norm and SwiGLU (SiLU-and-mul), with bf16 / f32 outputs or quantized ones
+(fp8 e4m3fn with a per-row or per-128 scale, MXFP8 / MXFP4 with E8M0 scales per
+32, NVFP4 with E4M3FN scales per 16 and a tensor scale).
 
 Thin torch-facing binding over the C ABI in include/rmsnorm_rows.h: it checks
 tensors, allocates outputs with torch, and passes raw device pointers and the
@@ -299,6 +301,8 @@ def silu_mul(x: torch.Tensor, *, out_dtype: Optional[torch.dtype] = None, scale_
 
 def query_silu_mul_config(rows: int, d: int, *, x_dtype: str = "bf16", out_dtype: str = "bf16",
                           scale_scheme: str = "row", num_cus: int = 256) -> dict:
+    """The launch configuration silu_mul picks (host only with an explicit
+    ``num_cus``; ``num_cus=0`` queries the current device)."""
     cfg = LaunchConfig()
     flags = (_lib.DTYPE_CODES[x_dtype] << _lib.RN_FLAGS_X_SHIFT) | (_lib.DTYPE_CODES[out_dtype] << _lib.RN_FLAGS_OUT_SHIFT)
     flags |= _lib.SCALE_SCHEMES[scale_scheme] << _lib.RN_FLAGS_SCALE_SHIFT
