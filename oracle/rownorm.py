@@ -51,13 +51,28 @@ Pins (all run with ``pytest -m "not gpu"``):
   * ``fp8_quantize_rows``: the format's error bounds and the saturation
     invariant (tests/test_oracle_fp8.py);
   * ``qknorm``: a head-by-head Python loop over the page's (token, head)
-    row order (tests/test_oracle_rmsnorm.py).
+    row order (tests/test_oracle_rmsnorm.py);
+  * ``exact_sum`` / ``rmsnorm_rows_partials``: exact rational brute force
+    (``fractions.Fraction``) on mixed-magnitude and adversarial terms, ties
+    decided by a remainder below double precision, order independence,
+    torch's float32 sum where it is exact, and the one-partial case against
+    ``residual_add`` / ``rmsnorm_rows`` (tests/test_oracle_partials.py).
+
+Partial inputs (``rmsnorm_rows_partials``): x arrives as K partial tensors
+whose sum it is -- the per-rank partials that a tensor-parallel all-reduce
+sums in front of the norm.  The page fuses such a local sum with the
+all-reduce in one decode launch ("CuTeDSL at Perplexity", MoE
+dispatch/combine, single-node tensor-parallel part).  Reading: x is the
+exact sum; with a residual, h = round_res(x + residual) is one rounding of
+the exact sum of all the terms; without one, the norm is taken over the
+exact x.
 """
 
 from __future__ import annotations
 
 from dataclasses import dataclass
-from typing import Dict, Optional, Tuple
+import math
+from typing import Dict, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -76,6 +91,8 @@ __all__ = [
     "encode",
     "residual_add",
     "rmsnorm_rows",
+    "exact_sum",
+    "rmsnorm_rows_partials",
     "fp8_scale_from_amax",
     "fp8_quantize_rows",
     "qknorm",
@@ -273,6 +290,56 @@ def rmsnorm_rows(x: np.ndarray, weight: np.ndarray, eps: float, weight_bias: flo
     wb = np.asarray(weight, dtype=np.float64) + weight_bias
     y = wb[None, :] * h * inv[:, None]
     return {"h": h, "inv": inv, "y": y}
+
+
+def exact_sum(terms: Sequence[np.ndarray]) -> Tuple[np.ndarray, np.ndarray]:
+    """Elementwise exact sum of equally shaped arrays of doubles.
+
+    Returns ``(s, e)``: ``s`` is the exact sum rounded once to double and
+    ``e`` the remainder (exact sum - ``s``) rounded to double, so that
+    ``round_to_format(s, fmt, e)`` rounds the exact sum once to a narrower
+    format (``e`` decides a tie that ``s`` alone would show).  Python's
+    ``math.fsum`` computes both, element by element.  Signed zeros follow
+    IEEE addition: the sum is -0 only when every term is -0.
+    """
+    arrs = [np.asarray(t, dtype=np.float64) for t in terms]
+    if not arrs:
+        raise ValueError("at least one term")
+    shape = arrs[0].shape
+    for a in arrs:
+        if a.shape != shape:
+            raise ValueError("terms must have one shape")
+    cols = np.stack([a.reshape(-1) for a in arrs], axis=1)
+    s = np.empty(cols.shape[0])
+    e = np.empty(cols.shape[0])
+    for i, row in enumerate(cols.tolist()):
+        si = math.fsum(row)
+        s[i] = si
+        e[i] = math.fsum(row + [-si])
+    all_neg_zero = np.all((cols == 0) & np.signbit(cols), axis=1)
+    s[all_neg_zero] = -0.0
+    return s.reshape(shape), e.reshape(shape)
+
+
+def rmsnorm_rows_partials(partials: Sequence[np.ndarray], weight: np.ndarray, eps: float, weight_bias: float,
+                          residual: Optional[np.ndarray] = None, res_dtype: Optional[str] = None
+                          ) -> Dict[str, np.ndarray]:
+    """``rmsnorm_rows`` with x given as the sum of ``partials`` (doubles, shape [rows, H] each).
+
+    With a residual, ``h = round_res(sum_k partials[k] + residual)``: one
+    rounding of the exact sum of all the terms.  Without one, the norm is
+    taken over the exact sum of the partials (as a double: within 2^-53
+    relative of it).  Returns what ``rmsnorm_rows`` returns.
+    """
+    terms = list(partials)
+    if residual is not None:
+        terms.append(residual)
+    s, e = exact_sum(terms)
+    if residual is not None:
+        h = round_to_format(s, FORMATS[res_dtype], e)
+    else:
+        h = s
+    return rmsnorm_rows(h, weight, eps, weight_bias)
 
 
 def fp8_scale_from_amax(amax: np.ndarray) -> np.ndarray:

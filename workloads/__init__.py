@@ -28,6 +28,16 @@ Recipe for one workload (seed ``s``):
 Drawing rows ``[r0, r0 + n)`` alone (``row_range``) reproduces exactly those
 rows of the full tensor, so a large workload can be checked on sampled rows
 without materializing it twice.
+
+Partial-input workloads (``PartialsWorkload``): partial k is drawn like x
+from ``SeedSequence([s, k + 1]).spawn(5)`` (stream x, outlier mask stream of
+x); the residual and the weight come from ``SeedSequence(s)`` as above.
+With ``exact_sum`` every bf16-valued input of the sum (the partials, and a
+bf16 residual) has each |value| below 2^-7 replaced by +0 after the storage
+rounding, and f32 partials are first rounded to bfloat16 values (kept in
+float32 storage).  Every nonzero term then lies in [2^-7, 2^5) for the
+distributions used here (the tests check this), so every float32 prefix sum
+of up to 8 such terms is exact: the sum's rounding order cannot change it.
 """
 
 from __future__ import annotations
@@ -42,7 +52,9 @@ __all__ = [
     "RowNormWorkload",
     "QKNormWorkload",
     "ActWorkload",
+    "PartialsWorkload",
     "generate_act",
+    "generate_partials",
     "WORKLOADS",
     "generate_rownorm",
     "generate_qknorm",
@@ -128,6 +140,30 @@ class ActWorkload:
         return replace(self, rows=rows)
 
 
+@dataclass(frozen=True)
+class PartialsWorkload:
+    """Fused add+RMSNorm whose x is the sum of ``num_partials`` tensors."""
+
+    name: str
+    rows: int
+    hidden: int
+    num_partials: int
+    x_dtype: str               # dtype of every partial
+    res_dtype: Optional[str]
+    w_dtype: str
+    out_dtype: str
+    part_dist: Dist
+    res_dist: Optional[Dist]
+    w_dist: Dist
+    weight_plus_one: bool
+    eps: float
+    exact_sum: bool = True     # the recipe above that makes float32 sums exact
+    description: str = ""
+
+    def with_rows(self, rows: int) -> "PartialsWorkload":
+        return replace(self, rows=rows)
+
+
 N01 = Dist(0.0, 1.0)
 W_N1 = Dist(1.0, 0.1)
 
@@ -168,6 +204,13 @@ WORKLOADS: Dict[str, object] = {
         description="SwiGLU silu(gate) * up, 8192 tokens, merged gate/up projection 2 x 14336 bf16 "
                     "~ N(0,1), bf16 out",
     ),
+    "partials_8x2048x8192": PartialsWorkload(
+        name="partials_8x2048x8192", rows=2048, hidden=8192, num_partials=8,
+        x_dtype="bf16", res_dtype="f32", w_dtype="bf16", out_dtype="bf16",
+        part_dist=Dist(0.0, 0.5), res_dist=Dist(0.0, 4.0), w_dist=W_N1, weight_plus_one=False, eps=1e-6,
+        description="sum of 8 bf16 partials ~ N(0,0.5) (one GPU's 2048-token share of an 8-way "
+                    "tensor-parallel reduce-scatter) + f32 residual ~ N(0,4) + RMSNorm, 8192 wide, bf16 out",
+    ),
 }
 
 
@@ -179,18 +222,21 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
 
 
-def _children(seed: int):
-    return np.random.SeedSequence(seed).spawn(N_STREAMS)
+def _children(seed: int, salt: Optional[int] = None):
+    entropy = seed if salt is None else [seed, salt]
+    return np.random.SeedSequence(entropy).spawn(N_STREAMS)
 
 
 def draw_tensor(seed: int, stream: int, mask_stream: Optional[int], shape: Tuple[int, int],
-                dist: Dist, dtype: str, row_range: Optional[Tuple[int, int]] = None) -> np.ndarray:
-    """Draw one ``[rows, cols]`` tensor (or a row range of it) following the recipe above."""
+                dist: Dist, dtype: str, row_range: Optional[Tuple[int, int]] = None,
+                salt: Optional[int] = None) -> np.ndarray:
+    """Draw one ``[rows, cols]`` tensor (or a row range of it) following the recipe above
+    (``salt``: the second entropy word of a partial's seed sequence)."""
     rows, cols = shape
     r0, r1 = (0, rows) if row_range is None else row_range
     if not (0 <= r0 <= r1 <= rows):
         raise ValueError(f"row range {row_range} outside [0, {rows}]")
-    kids = _children(seed)
+    kids = _children(seed, salt)
     gen = np.random.Generator(np.random.PCG64(kids[stream]))
     n = (r1 - r0) * cols
     if r0:
@@ -262,3 +308,39 @@ def generate_qknorm(wl: QKNormWorkload, seed: int = 0) -> Dict[str, Optional[np.
 def generate_act(wl: ActWorkload, seed: int = 0, row_range: Optional[Tuple[int, int]] = None) -> np.ndarray:
     """Input ``x`` [rows, 2 d] of a SiLU-and-mul workload (stream x, outliers on the x mask stream)."""
     return draw_tensor(seed, STREAM_X, STREAM_MASK_X, (wl.rows, 2 * wl.d), wl.x_dist, wl.x_dtype, row_range)
+
+
+EXACT_SUM_FLUSH = 2.0 ** -7  # |value| below this becomes +0 under the exact-sum recipe
+
+
+def _flush_small_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns with |value| < EXACT_SUM_FLUSH replaced by +0 (exponent field test, no arithmetic)."""
+    biased_exp = (bits >> 7) & 0xFF
+    small = biased_exp < 127 - 7  # |v| < 2^-7
+    out = bits.copy()
+    out[small] = 0
+    return out
+
+
+def generate_partials(wl: PartialsWorkload, seed: int = 0,
+                      row_range: Optional[Tuple[int, int]] = None) -> Dict[str, object]:
+    """Inputs of a partial-input workload: ``partials`` (a list of ``num_partials``
+    [rows, hidden] tensors), ``residual`` (or None) and ``weight`` [hidden]."""
+    shape = (wl.rows, wl.hidden)
+    parts = []
+    for k in range(wl.num_partials):
+        if wl.exact_sum:
+            p = draw_tensor(seed, STREAM_X, STREAM_MASK_X, shape, wl.part_dist, "bf16", row_range, salt=k + 1)
+            p = _flush_small_bf16(p)
+            if wl.x_dtype == "f32":
+                p = (p.astype(np.uint32) << 16).view(np.float32)
+        else:
+            p = draw_tensor(seed, STREAM_X, STREAM_MASK_X, shape, wl.part_dist, wl.x_dtype, row_range, salt=k + 1)
+        parts.append(p)
+    res = None
+    if wl.res_dtype is not None:
+        res = draw_tensor(seed, STREAM_RES, STREAM_MASK_RES, shape, wl.res_dist, wl.res_dtype, row_range)
+        if wl.exact_sum and wl.res_dtype == "bf16":
+            res = _flush_small_bf16(res)
+    w = draw_tensor(seed, STREAM_W, None, (1, wl.hidden), wl.w_dist, wl.w_dtype)[0]
+    return {"partials": parts, "residual": res, "weight": w}
