@@ -16,11 +16,12 @@ The same line carries:
     sample of the same workload on this host;
   * ``secondary``: the other workloads -- decode calls (us/call against an
     empty kernel launched the same way), per-head QK-norm, the fp8-output
-    prefill with per-row scales, and the same prefill with block-scaled
-    outputs (fp8 per-128 scales, MXFP8, MXFP4), and the SiLU-and-mul
-    activation (bf16, MXFP8, MXFP4 out) (GB/s, with rotating buffer sets
-    larger than the 256 MB Infinity Cache so that every call streams from
-    HBM).
+    prefill with per-row scales, the same prefill with block-scaled
+    outputs (fp8 per-128 scales, MXFP8, MXFP4, NVFP4), the sum of 8 partial
+    inputs in front of the add (one GPU's share of a tensor-parallel
+    reduce-scatter), and the SiLU-and-mul activation (bf16, MXFP8, MXFP4,
+    NVFP4 out) (GB/s, with rotating buffer sets larger than the 256 MB
+    Infinity Cache so that every call streams from HBM).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
 """
@@ -382,6 +383,54 @@ def qknorm_metrics(steps: int, warmup: int, sets: int = 8) -> dict:
             "buffer_sets": sets, "launch_us": spread}
 
 
+def partials_bytes(wl) -> int:
+    """Algorithmic bytes: every partial and the residual read once; out and residual_out written once; weight once."""
+    size = {"bf16": 2, "f32": 4}
+    per_row = wl.hidden * (wl.num_partials * size[wl.x_dtype] + size[wl.out_dtype])
+    if wl.res_dtype is not None:
+        per_row += 2 * wl.hidden * size[wl.res_dtype]
+    return wl.rows * per_row + wl.hidden * size[wl.w_dtype]
+
+
+def partials_metrics(name: str, steps: int, warmup: int, sets: int = 2) -> dict:
+    import torch
+
+    import workloads as WL
+    from residual_add_rmsnorm_rows_amd import _lib as L
+    from tests.gpu_util import TORCH_DTYPES, to_dev
+
+    wl = WL.WORKLOADS[name]
+    inp = WL.generate_partials(wl, seed=0)
+    parts0 = [to_dev(p, wl.x_dtype) for p in inp["partials"]]
+    res0 = to_dev(inp["residual"], wl.res_dtype)
+    w = to_dev(inp["weight"], wl.w_dtype)
+    bufs = []
+    for i in range(sets):
+        parts = parts0 if i == 0 else [p.clone() for p in parts0]
+        res = res0 if i == 0 else res0.clone()
+        ptrs = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
+        out = torch.empty(wl.rows, wl.hidden, dtype=TORCH_DTYPES[wl.out_dtype], device="cuda")
+        bufs.append((parts, ptrs, res, torch.empty_like(res), out))
+    lib = L.lib()
+    flags = L.make_flags(wl.x_dtype, wl.res_dtype, wl.w_dtype, wl.out_dtype, wl.weight_plus_one)
+    state = {"i": 0}
+
+    def call(stream):
+        _, ptrs, res, ro, out = bufs[state["i"]]
+        state["i"] = (state["i"] + 1) % sets
+        st = lib.rmsnorm_fwd_partials(ptrs, wl.num_partials, res.data_ptr(), w.data_ptr(), out.data_ptr(),
+                                      ro.data_ptr(), None, None, wl.rows, wl.hidden, wl.eps, flags, stream)
+        if st != 0:
+            L.check(st)
+
+    ms = time_stream_loop(call, steps, warmup)
+    spread = launch_percentiles(call)
+    b = partials_bytes(wl)
+    return {"workload": wl.description, "us_per_call": round(ms * 1000, 3), "algorithmic_bytes": b,
+            "GBps": round(b / (ms * 1e-3) / 1e9, 1), "frac_of_peak": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "buffer_sets": sets, "launch_us": spread}
+
+
 def act_metrics(steps: int, warmup: int, out_dtype: str = "bf16", scale_scheme: str = "row", sets: int = 2) -> dict:
     """SiLU-and-mul on the 8192 x 14336 workload (bytes: x read once, out and scales written once)."""
     import torch
@@ -645,6 +694,8 @@ def main() -> int:
                                                         out_dtype="fp4_e2m1", scale_scheme="mx32")
         sec["prefill_8192x7168_nvfp4"] = stream_metrics("prefill_fp8_8192x7168", args.steps, args.warmup, sets=3,
                                                         out_dtype="fp4_e2m1", scale_scheme="nv16")
+        log("partials_8x2048x8192")
+        sec["partials_8x2048x8192"] = partials_metrics("partials_8x2048x8192", args.steps * 2, args.warmup)
         log("silu_mul_8192x14336")
         # the quantized variants do more arithmetic per byte; the GPU's power
         # management lowers clocks for a few ms after such a load starts, so
@@ -656,7 +707,7 @@ def main() -> int:
         sec["silu_mul_8192x14336_nvfp4"] = act_metrics(args.steps, aw, "fp4_e2m1", "nv16")
         log("copy ceilings at the secondary workloads' sizes")
         for name, sets, steps in (("qknorm_4096x32x128", 8, args.steps * 4), ("prefill_fp8_8192x7168", 3, args.steps),
-                                  ("silu_mul_8192x14336", 2, args.steps)):
+                                  ("partials_8x2048x8192", 2, args.steps * 2), ("silu_mul_8192x14336", 2, args.steps)):
             c = copy_ceiling(sec[name]["algorithmic_bytes"], sets, steps, args.warmup)
             sec[name]["copy_ceiling"] = {**c, "value_over_ceiling": round(sec[name]["GBps"] / c["GBps"], 4)}
         for name, entry in sec.items():

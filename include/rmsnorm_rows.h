@@ -27,6 +27,9 @@
  * over head_dim, with one weight vector per tensor shared by all heads, as in
  * the "QK Norm" section's kernel (heads of Q first, then heads of K, per token).
  *
+ * rmsnorm_fwd_partials is the same fused add + norm with x given as a sum of
+ * up to 8 partial tensors (summed in the kernel, in float32).
+ *
  * silu_mul_fwd is the SwiGLU activation over rows of a merged gate/up
  * projection, with the same output types as rmsnorm_fwd.
  *
@@ -65,7 +68,7 @@
 extern "C" {
 #endif
 
-#define RN_ABI_VERSION 2
+#define RN_ABI_VERSION 3
 
 typedef enum rn_status {
   RN_OK = 0,
@@ -197,6 +200,56 @@ rn_status rmsnorm_fwd_config(const void* x, const void* residual, const void* we
                              uint32_t flags, const rn_launch_config* cfg, void* stream);
 
 /*
+ * Fused sum of partial inputs + residual add + RMSNorm over rows.
+ *
+ * x is not given whole but as num_partials tensors whose elementwise sum it
+ * is: the per-rank partial outputs of a row-parallel (tensor-parallel)
+ * projection, which an all-reduce or reduce-scatter sums in front of the
+ * norm, or the attention and MLP branch outputs of a parallel residual
+ * block.  The "CuTeDSL at Perplexity" page fuses a local summation kernel
+ * with the all-reduce that follows it into one decode launch (MoE
+ * dispatch/combine, single-node tensor-parallel part) and names the fusion
+ * of inter-device communication with normalization as what comes next
+ * (Conclusion).  This entry point is that fusion's arithmetic on one GPU:
+ * the partials are device pointers (local buffers, or peer buffers the
+ * caller has mapped); the library does no communication itself.
+ *
+ *   partials      HOST array of num_partials device pointers, each [rows, hidden] of
+ *                 dtype flags.x, 16-byte aligned, none NULL (when rows > 0)      (read)
+ *   num_partials  1..8
+ *   residual, weight, out, residual_out, out_scale, out_amax, rows, eps: as rmsnorm_fwd_ex;
+ *   hidden        as rmsnorm_fwd, and at most 2048 lane vectors (16384 bf16 / 8192 f32
+ *                 elements) when num_partials > 1
+ *   flags         as rmsnorm_fwd, with out bf16, f32, or fp8 with RN_SCALE_ROW
+ *                 (other scale granularities and fp4 return RN_ERR_UNSUPPORTED)
+ *
+ * Reading (not on the pages): x = ((p_0 + p_1) + p_2) + ... is summed in
+ * float32 in slot order, without rounding to the x dtype, then
+ * h = round_res(x + residual) as in rmsnorm_fwd (float32 add, one rounding to
+ * the residual dtype), or h = x (float32) without a residual, and the norm
+ * and the output are those of rmsnorm_fwd over h.  When every prefix sum of
+ * the partials is a float32 value (as for bf16 partials within 2^12 of one
+ * another in magnitude, or zero) the float32 sum is exact and the result is
+ * that of rmsnorm_fwd on the exact sum; otherwise each float32 addition
+ * rounds once (error at most (num_partials - 1) * 2^-24 * sum_k |p_k|).
+ * num_partials == 1 is rmsnorm_fwd_ex on x = partials[0].
+ * Aliasing: out may equal one of the partials (in place); residual_out may
+ * equal residual; residual_out equal to a partial or to out is rejected; any
+ * other overlap is undefined.
+ */
+rn_status rmsnorm_fwd_partials(const void* const* partials, int32_t num_partials, const void* residual,
+                               const void* weight, void* out, void* residual_out, void* out_scale,
+                               float* out_amax, int64_t rows, int64_t hidden, float eps, uint32_t flags,
+                               void* stream);
+
+/* As rmsnorm_fwd_partials with an explicit launch configuration (the rules of
+ * rmsnorm_fwd_config; vecs_per_lane at most 2 when num_partials > 1). */
+rn_status rmsnorm_fwd_partials_config(const void* const* partials, int32_t num_partials, const void* residual,
+                                      const void* weight, void* out, void* residual_out, void* out_scale,
+                                      float* out_amax, int64_t rows, int64_t hidden, float eps, uint32_t flags,
+                                      const rn_launch_config* cfg, void* stream);
+
+/*
  * Per-head RMSNorm of Q and K ("CuTeDSL at Perplexity", section "QK Norm").
  *
  *   q          [tokens, num_q_heads, head_dim], token stride q_token_stride elements
@@ -263,6 +316,10 @@ rn_status silu_mul_query_config(int64_t rows, int64_t d, uint32_t flags, int32_t
  * read from flags). */
 rn_status rmsnorm_query_config(int64_t rows, int64_t hidden, uint32_t flags, int32_t has_residual,
                                int32_t num_cus, rn_launch_config* cfg);
+
+/* The launch configuration rmsnorm_fwd_partials would use (host only when num_cus > 0). */
+rn_status rmsnorm_partials_query_config(int64_t rows, int64_t hidden, int32_t num_partials, uint32_t flags,
+                                        int32_t has_residual, int32_t num_cus, rn_launch_config* cfg);
 
 /* Host-only: the launch configuration qknorm_fwd would use. */
 rn_status qknorm_query_config(int64_t tokens, int32_t num_q_heads, int32_t num_k_heads,

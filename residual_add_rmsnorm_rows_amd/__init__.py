@@ -1,5 +1,6 @@
-"""MI355X-native (gfx950) row kernels: fused residual add + RMSNorm, per-head
-QK-norm and SwiGLU (SiLU-and-mul), with bf16 / f32 outputs or quantized ones
+"""MI355X-native (gfx950) row kernels: fused residual add + RMSNorm (with x
+given whole or as a sum of up to 8 partials), per-head QK-norm and SwiGLU
+(SiLU-and-mul), with bf16 / f32 outputs or quantized ones
 (fp8 e4m3fn with a per-row or per-128 scale, MXFP8 / MXFP4 with E8M0 scales per
 32, NVFP4 with E4M3FN scales per 16 and a tensor scale).
 
@@ -12,7 +13,7 @@ library's HIP kernels; nothing here computes, and nothing falls back to the CPU.
 from __future__ import annotations
 
 import ctypes
-from typing import NamedTuple, Optional, Tuple
+from typing import NamedTuple, Optional, Sequence, Tuple
 
 import torch
 
@@ -22,11 +23,13 @@ from ._lib import LaunchConfig, RNError, check, lib, make_flags
 __all__ = [
     "NormOutput",
     "fused_add_rmsnorm",
+    "fused_partials_add_rmsnorm",
     "rmsnorm",
     "qk_norm",
     "silu_mul",
     "query_silu_mul_config",
     "query_config",
+    "query_partials_config",
     "query_qknorm_config",
     "RNError",
     "LaunchConfig",
@@ -99,26 +102,12 @@ def _quant_buffers(od: str, scale_scheme: str, rows: int, n: int, device: torch.
     return scale, amax, ts
 
 
-def fused_add_rmsnorm(x: torch.Tensor, residual: Optional[torch.Tensor], weight: torch.Tensor,
-                      eps: float, *, weight_plus_one: bool = False,
-                      out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
-                      residual_out: Optional[torch.Tensor] = None, return_amax: bool = False,
-                      scale_scheme: str = "row", tensor_scale=None,
-                      config: Optional[LaunchConfig] = None) -> NormOutput:
-    """``residual_out = x + residual``; ``out = RMSNorm(residual_out) * (w [+ 1])``.
-
-    ``x`` is [..., H] (bf16 or f32), ``residual`` the same shape (x dtype or
-    f32) or None, ``weight`` [H].  ``out_dtype`` is bf16, f32,
-    ``torch.float8_e4m3fn`` or ``torch.float4_e2m1fn_x2`` (two codes per byte,
-    [..., H/2]).  Quantized outputs carry scales per ``scale_scheme``:
-    ``"row"`` (fp8; float32 [rows]), ``"group128"`` (fp8; float32
-    [rows, H/128]), ``"mx32"`` (fp8 or fp4; E8M0 ``torch.float8_e8m0fnu``
-    [rows, H/32]) or ``"nv16"`` (fp4; E4M3FN ``torch.float8_e4m3fn``
-    [rows, H/16], with the per-tensor float32 ``tensor_scale``: a
-    one-element device tensor, or a number copied to the device).
-    ``out=x`` and ``residual_out=residual`` are allowed (in place).
-    ``config`` forces a launch configuration.
-    """
+def _rows_setup(x: torch.Tensor, residual: Optional[torch.Tensor], weight: torch.Tensor,
+                weight_plus_one: bool, out_dtype: Optional[torch.dtype], out: Optional[torch.Tensor],
+                residual_out: Optional[torch.Tensor], return_amax: bool, scale_scheme: str, tensor_scale):
+    """Checks of a rows call (x stands for the shape and dtype of the input);
+    allocates the outputs that were not given.  Returns (rows, H, out,
+    residual_out, scale, amax, tensor_scale, flags)."""
     device = x.device
     if device.type != "cuda":
         raise ValueError("x must be a device tensor")
@@ -158,13 +147,75 @@ def fused_add_rmsnorm(x: torch.Tensor, residual: Optional[torch.Tensor], weight:
         raise ValueError("residual_out given without residual")
     scale, amax, ts = _quant_buffers(od, scale_scheme, rows, H, device, return_amax, tensor_scale)
     flags = make_flags(xd, rd, wd, od, weight_plus_one, scale_scheme)
+    return rows, H, out, residual_out, scale, amax, ts, flags
+
+
+def fused_add_rmsnorm(x: torch.Tensor, residual: Optional[torch.Tensor], weight: torch.Tensor,
+                      eps: float, *, weight_plus_one: bool = False,
+                      out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                      residual_out: Optional[torch.Tensor] = None, return_amax: bool = False,
+                      scale_scheme: str = "row", tensor_scale=None,
+                      config: Optional[LaunchConfig] = None) -> NormOutput:
+    """``residual_out = x + residual``; ``out = RMSNorm(residual_out) * (w [+ 1])``.
+
+    ``x`` is [..., H] (bf16 or f32), ``residual`` the same shape (x dtype or
+    f32) or None, ``weight`` [H].  ``out_dtype`` is bf16, f32,
+    ``torch.float8_e4m3fn`` or ``torch.float4_e2m1fn_x2`` (two codes per byte,
+    [..., H/2]).  Quantized outputs carry scales per ``scale_scheme``:
+    ``"row"`` (fp8; float32 [rows]), ``"group128"`` (fp8; float32
+    [rows, H/128]), ``"mx32"`` (fp8 or fp4; E8M0 ``torch.float8_e8m0fnu``
+    [rows, H/32]) or ``"nv16"`` (fp4; E4M3FN ``torch.float8_e4m3fn``
+    [rows, H/16], with the per-tensor float32 ``tensor_scale``: a
+    one-element device tensor, or a number copied to the device).
+    ``out=x`` and ``residual_out=residual`` are allowed (in place).
+    ``config`` forces a launch configuration.
+    """
+    rows, H, out, residual_out, scale, amax, ts, flags = _rows_setup(
+        x, residual, weight, weight_plus_one, out_dtype, out, residual_out, return_amax, scale_scheme, tensor_scale)
     L = lib()
     if config is not None:
         st = L.rmsnorm_fwd_config(_p(x), _p(residual), _p(weight), _p(out), _p(residual_out), _p(scale),
-                                  _p(amax), _p(ts), rows, H, eps, flags, ctypes.byref(config), _stream(device))
+                                  _p(amax), _p(ts), rows, H, eps, flags, ctypes.byref(config), _stream(x.device))
     else:
         st = L.rmsnorm_fwd_ex(_p(x), _p(residual), _p(weight), _p(out), _p(residual_out), _p(scale),
-                              _p(amax), _p(ts), rows, H, eps, flags, _stream(device))
+                              _p(amax), _p(ts), rows, H, eps, flags, _stream(x.device))
+    check(st)
+    return NormOutput(out, residual_out, scale, amax)
+
+
+def fused_partials_add_rmsnorm(partials: Sequence[torch.Tensor], residual: Optional[torch.Tensor],
+                               weight: torch.Tensor, eps: float, *, weight_plus_one: bool = False,
+                               out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                               residual_out: Optional[torch.Tensor] = None, return_amax: bool = False,
+                               config: Optional[LaunchConfig] = None) -> NormOutput:
+    """``fused_add_rmsnorm`` with ``x = partials[0] + partials[1] + ...``, summed
+    in the kernel in float32 (slot order) without an intermediate rounding.
+
+    ``partials`` holds 1..8 tensors of one shape and dtype (bf16 or f32): the
+    partial outputs of a row-parallel projection, or the branch outputs of a
+    parallel residual block.  Outputs are bf16, f32, or fp8 e4m3fn with one
+    scale per row.  ``out`` may be one of the partials (in place).
+    """
+    parts = list(partials)
+    if not 1 <= len(parts) <= _lib.MAX_PARTIALS:
+        raise ValueError(f"1..{_lib.MAX_PARTIALS} partials expected, got {len(parts)}")
+    x = parts[0]
+    for i, p in enumerate(parts):
+        _dev_tensor(p, f"partials[{i}]", x.device)
+        if p.shape != x.shape or p.dtype != x.dtype:
+            raise ValueError(f"partials[{i}] has shape {tuple(p.shape)} / {p.dtype}, "
+                             f"partials[0] has {tuple(x.shape)} / {x.dtype}")
+    rows, H, out, residual_out, scale, amax, _, flags = _rows_setup(
+        x, residual, weight, weight_plus_one, out_dtype, out, residual_out, return_amax, "row", None)
+    ptrs = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
+    L = lib()
+    if config is not None:
+        st = L.rmsnorm_fwd_partials_config(ptrs, len(parts), _p(residual), _p(weight), _p(out), _p(residual_out),
+                                           _p(scale), _p(amax), rows, H, eps, flags, ctypes.byref(config),
+                                           _stream(x.device))
+    else:
+        st = L.rmsnorm_fwd_partials(ptrs, len(parts), _p(residual), _p(weight), _p(out), _p(residual_out),
+                                    _p(scale), _p(amax), rows, H, eps, flags, _stream(x.device))
     check(st)
     return NormOutput(out, residual_out, scale, amax)
 
@@ -247,6 +298,17 @@ def query_config(rows: int, hidden: int, *, x_dtype: str = "bf16", res_dtype: Op
     flags = make_flags(x_dtype, res_dtype, w_dtype, out_dtype, weight_plus_one, scale_scheme)
     check(lib().rmsnorm_query_config(rows, hidden, flags, int(res_dtype is not None), num_cus,
                                      ctypes.byref(cfg)))
+    return cfg.as_dict()
+
+
+def query_partials_config(rows: int, hidden: int, num_partials: int, *, x_dtype: str = "bf16",
+                          res_dtype: Optional[str] = None, w_dtype: str = "bf16", out_dtype: str = "bf16",
+                          weight_plus_one: bool = False, num_cus: int = 256) -> dict:
+    """The launch configuration ``fused_partials_add_rmsnorm`` would use."""
+    cfg = LaunchConfig()
+    flags = make_flags(x_dtype, res_dtype, w_dtype, out_dtype, weight_plus_one)
+    check(lib().rmsnorm_partials_query_config(rows, hidden, num_partials, flags, int(res_dtype is not None),
+                                              num_cus, ctypes.byref(cfg)))
     return cfg.as_dict()
 
 

@@ -44,9 +44,10 @@ EXPORTED_SYMBOLS = (
     "rmsnorm_fwd", "rmsnorm_fwd_ex", "rmsnorm_fwd_config", "qknorm_fwd", "qknorm_fwd_config",
     "rmsnorm_query_config", "qknorm_query_config", "silu_mul_fwd", "silu_mul_fwd_config",
     "silu_mul_query_config", "rn_launch_empty", "rn_launch_copy", "rn_status_string", "rn_last_error",
-    "rn_abi_version",
+    "rn_abi_version", "rmsnorm_fwd_partials", "rmsnorm_fwd_partials_config", "rmsnorm_partials_query_config",
 )
-ABI_VERSION = 2
+ABI_VERSION = 3
+MAX_PARTIALS = 8
 
 
 def make_flags(x: str, res: str | None, w: str, out: str, weight_plus_one: bool,
@@ -94,7 +95,13 @@ _SIGNATURES = {
                    ctypes.c_int),
     "qknorm_fwd_config": ([_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i64, _f32, _u32,
                            ctypes.POINTER(LaunchConfig), _vp], ctypes.c_int),
+    "rmsnorm_fwd_partials": ([ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _u32, _vp],
+                             ctypes.c_int),
+    "rmsnorm_fwd_partials_config": ([ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _u32,
+                                    ctypes.POINTER(LaunchConfig), _vp], ctypes.c_int),
     "rmsnorm_query_config": ([_i64, _i64, _u32, _i32, _i32, ctypes.POINTER(LaunchConfig)], ctypes.c_int),
+    "rmsnorm_partials_query_config": ([_i64, _i64, _i32, _u32, _i32, _i32, ctypes.POINTER(LaunchConfig)],
+                                      ctypes.c_int),
     "qknorm_query_config": ([_i64, _i32, _i32, _i32, _u32, _i32, ctypes.POINTER(LaunchConfig)], ctypes.c_int),
     "silu_mul_fwd": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _u32, _vp], ctypes.c_int),
     "silu_mul_fwd_config": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _u32, ctypes.POINTER(LaunchConfig), _vp],

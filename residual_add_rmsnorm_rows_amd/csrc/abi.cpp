@@ -77,18 +77,51 @@ rn_status launch(const void* fn, int64_t grid, int block, void* args, void* stre
   return RN_OK;
 }
 
-rn_status rows_entry(const void* x, const void* residual, const void* weight, void* out,
-                     void* residual_out, void* out_scale, float* out_amax, const float* tensor_scale, int64_t rows,
-                     int64_t hidden, float eps, uint32_t flags, const rn_launch_config* explicit_cfg,
-                     void* stream) {
+// Partial-input form (rmsnorm_fwd_partials*): the sizes and flags checks of
+// the rows kernel, then those of the partials (count, supported outputs).
+rn_status check_parts_key(int32_t num_parts, int64_t hidden, RowKey* key) {
+  if (num_parts < 1 || num_parts > kMaxParts)
+    return fail(RN_ERR_INVALID_ARG, "num_partials must be in 1..%d (got %d)", kMaxParts, num_parts);
+  if (key->qs != kQRow || key->out == kFP4)
+    return fail(RN_ERR_UNSUPPORTED, "partial inputs take bf16, f32 or fp8 (RN_SCALE_ROW) outputs");
+  const int64_t vec = key->x == kBF16 ? 8 : 4;
+  const int64_t cap = static_cast<int64_t>(64) * kMaxWavesPerRow * kMaxPartsVecsPerLane * vec;
+  if (num_parts > 1 && hidden > cap)
+    return fail(RN_ERR_UNSUPPORTED, "hidden (%lld) above the largest row of the partial-input kernels (%lld)",
+                (long long)hidden, (long long)cap);
+  key->kp = num_parts == 1 ? 1 : parts_slots(num_parts);
+  return RN_OK;
+}
+
+// parts_form: x is the sum of parts[0 .. num_parts) (x itself is unused);
+// otherwise the single-input form.
+rn_status rows_entry(bool parts_form, const void* x, const void* const* parts, int32_t num_parts,
+                     const void* residual,
+                     const void* weight, void* out, void* residual_out, void* out_scale, float* out_amax,
+                     const float* tensor_scale, int64_t rows, int64_t hidden, float eps, uint32_t flags,
+                     const rn_launch_config* explicit_cfg, void* stream) {
   clear_error();
   RowKey key;
   rn_status st = check_row_shape(rows, hidden, flags, residual != nullptr, &key);
   if (st != RN_OK) return st;
+  if (parts_form) {
+    st = check_parts_key(num_parts, hidden, &key);
+    if (st != RN_OK) return st;
+  }
   if (!(eps >= 0.0f) || eps == __builtin_inff()) return fail(RN_ERR_INVALID_ARG, "eps must be finite and >= 0");
   st = check_quant_ptrs(key.out, key.qs, out_scale, out_amax, tensor_scale, false);
   if (st != RN_OK) return st;
   if (rows == 0) return RN_OK;
+  if (parts_form) {
+    if (parts == nullptr) return fail(RN_ERR_INVALID_ARG, "partials must not be NULL");
+    for (int32_t k = 0; k < num_parts; ++k) {
+      if (parts[k] == nullptr) return fail(RN_ERR_INVALID_ARG, "partials[%d] is NULL", k);
+      if (!aligned(parts[k], 16)) return fail(RN_ERR_MISALIGNED, "partials[%d] = %p is not 16-byte aligned", k, parts[k]);
+      if (residual_out != nullptr && parts[k] == residual_out)
+        return fail(RN_ERR_INVALID_ARG, "residual_out must not be one of the partials");
+    }
+    x = parts[0];
+  }
   if (x == nullptr || weight == nullptr || out == nullptr)
     return fail(RN_ERR_INVALID_ARG, "x, weight and out must not be NULL");
   if ((residual == nullptr) != (residual_out == nullptr))
@@ -127,6 +160,8 @@ rn_status rows_entry(const void* x, const void* residual, const void* weight, vo
   a.rows = rows;
   a.hidden = static_cast<int32_t>(hidden);
   a.eps = eps;
+  for (int k = 0; k < kMaxParts; ++k) a.parts[k] = parts_form && k < num_parts ? parts[k] : nullptr;
+  a.num_parts = parts_form ? num_parts : 1;
   return launch(fn, cfg.grid, cfg.block_threads, &a, stream);
 }
 
@@ -209,6 +244,7 @@ rn_status act_entry(const void* x, void* out, void* out_scale, float* out_amax, 
   if (explicit_cfg != nullptr) {
     RowKey rk{};
     rk.x = key.x;
+    rk.kp = 1;
     st = check_row_config(rows, d, rk, explicit_cfg, &cfg);
   } else {
     int cus = 0;
@@ -241,15 +277,15 @@ extern "C" {
 rn_status rmsnorm_fwd(const void* x, const void* residual, const void* weight, void* out,
                       void* residual_out, void* out_scale, int64_t rows, int64_t hidden, float eps,
                       uint32_t flags, void* stream) {
-  return rows_entry(x, residual, weight, out, residual_out, out_scale, nullptr, nullptr, rows, hidden, eps,
-                    flags, nullptr, stream);
+  return rows_entry(false, x, nullptr, 0, residual, weight, out, residual_out, out_scale, nullptr, nullptr, rows,
+                    hidden, eps, flags, nullptr, stream);
 }
 
 rn_status rmsnorm_fwd_ex(const void* x, const void* residual, const void* weight, void* out,
                          void* residual_out, void* out_scale, float* out_amax, const float* tensor_scale,
                          int64_t rows, int64_t hidden, float eps, uint32_t flags, void* stream) {
-  return rows_entry(x, residual, weight, out, residual_out, out_scale, out_amax, tensor_scale, rows, hidden,
-                    eps, flags, nullptr, stream);
+  return rows_entry(false, x, nullptr, 0, residual, weight, out, residual_out, out_scale, out_amax, tensor_scale,
+                    rows, hidden, eps, flags, nullptr, stream);
 }
 
 rn_status rmsnorm_fwd_config(const void* x, const void* residual, const void* weight, void* out,
@@ -260,8 +296,28 @@ rn_status rmsnorm_fwd_config(const void* x, const void* residual, const void* we
     clear_error();
     return fail(RN_ERR_INVALID_ARG, "launch config is NULL");
   }
-  return rows_entry(x, residual, weight, out, residual_out, out_scale, out_amax, tensor_scale, rows, hidden,
-                    eps, flags, cfg, stream);
+  return rows_entry(false, x, nullptr, 0, residual, weight, out, residual_out, out_scale, out_amax, tensor_scale,
+                    rows, hidden, eps, flags, cfg, stream);
+}
+
+rn_status rmsnorm_fwd_partials(const void* const* partials, int32_t num_partials, const void* residual,
+                               const void* weight, void* out, void* residual_out, void* out_scale,
+                               float* out_amax, int64_t rows, int64_t hidden, float eps, uint32_t flags,
+                               void* stream) {
+  return rows_entry(true, nullptr, partials, num_partials, residual, weight, out, residual_out, out_scale, out_amax,
+                    nullptr, rows, hidden, eps, flags, nullptr, stream);
+}
+
+rn_status rmsnorm_fwd_partials_config(const void* const* partials, int32_t num_partials, const void* residual,
+                                      const void* weight, void* out, void* residual_out, void* out_scale,
+                                      float* out_amax, int64_t rows, int64_t hidden, float eps, uint32_t flags,
+                                      const rn_launch_config* cfg, void* stream) {
+  if (cfg == nullptr) {
+    clear_error();
+    return fail(RN_ERR_INVALID_ARG, "launch config is NULL");
+  }
+  return rows_entry(true, nullptr, partials, num_partials, residual, weight, out, residual_out, out_scale, out_amax,
+                    nullptr, rows, hidden, eps, flags, cfg, stream);
 }
 
 rn_status qknorm_fwd(const void* q, const void* k, const void* q_weight, const void* k_weight,
@@ -291,6 +347,23 @@ rn_status rmsnorm_query_config(int64_t rows, int64_t hidden, uint32_t flags, int
   if (cfg == nullptr) return fail(RN_ERR_INVALID_ARG, "cfg is NULL");
   RowKey key;
   rn_status st = check_row_shape(rows, hidden, flags, has_residual != 0, &key);
+  if (st != RN_OK) return st;
+  int cus = num_cus;
+  if (cus <= 0) {
+    st = device_cus(&cus);
+    if (st != RN_OK) return st;
+  }
+  return select_row_config(rows > 0 ? rows : 1, hidden, key, cus, cfg);
+}
+
+rn_status rmsnorm_partials_query_config(int64_t rows, int64_t hidden, int32_t num_partials, uint32_t flags,
+                                        int32_t has_residual, int32_t num_cus, rn_launch_config* cfg) {
+  clear_error();
+  if (cfg == nullptr) return fail(RN_ERR_INVALID_ARG, "cfg is NULL");
+  RowKey key;
+  rn_status st = check_row_shape(rows, hidden, flags, has_residual != 0, &key);
+  if (st != RN_OK) return st;
+  st = check_parts_key(num_partials, hidden, &key);
   if (st != RN_OK) return st;
   int cus = num_cus;
   if (cus <= 0) {

@@ -21,6 +21,9 @@ enum QScheme : int {
   kQNv16 = 3,      // NVFP4: one E4M3FN scale per 16 elements and a float32 tensor scale (fp4 e2m1)
 };
 
+// Partial inputs a rows-kernel launch can sum in front of the residual add.
+constexpr int kMaxParts = 8;
+
 // Kernel arguments of the rows kernel, passed by value as the only argument.
 struct RowArgs {
   const void* x;
@@ -34,6 +37,10 @@ struct RowArgs {
   int64_t rows;
   int32_t hidden;        // elements per row
   float eps;
+  // Kernels built for partial inputs (KP > 1) read x as the sum of
+  // parts[0 .. num_parts) instead of x; the other slots are ignored.
+  const void* parts[kMaxParts];
+  int32_t num_parts;
 };
 
 // Kernel arguments of the per-head kernel.
@@ -69,6 +76,7 @@ struct RowKey {
   int qs;              // QScheme (kQRow unless the output is quantized)
   int bias;            // 0 or 1
   int nv;              // vectors per lane: 1, 2, 4, 8
+  int kp;              // partial-input slots: 1 = x itself; 2, 4 or 8 = a sum of up to that many
 };
 
 struct ActKey {
@@ -92,9 +100,12 @@ void clear_error();
 // Checks flags/sizes (not pointers) of an rmsnorm call and fills key.{x,res,w,out,bias}.
 rn_status check_row_shape(int64_t rows, int64_t hidden, uint32_t flags, bool has_residual,
                           RowKey* key);
-// Selector: launch configuration for rows x hidden on num_cus compute units.
+// Selector: launch configuration for rows x hidden on num_cus compute units
+// (key.kp > 1: the kernels that sum partial inputs, see kMaxPartsVecsPerLane).
 rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int num_cus,
                             rn_launch_config* cfg);
+// Partial-input slots of the smallest kernel that sums num_parts inputs (2, 4 or 8).
+int parts_slots(int num_parts);
 // Checks an explicit configuration and fills the derived fields.
 rn_status check_row_config(int64_t rows, int64_t hidden, const RowKey& key,
                            const rn_launch_config* in, rn_launch_config* out);
@@ -122,6 +133,10 @@ constexpr int kCopyThreads = 512;  // reference copy: one 16-byte vector per lan
 // per lane needs more than the 128 VGPRs a 1024-thread workgroup leaves each
 // lane, so that variant is built for at most 8 waves (256 VGPRs per lane).
 constexpr int max_threads_for_nv(int nv) { return nv >= 8 ? 512 : 1024; }
+
+// Kernels that sum partial inputs keep every slot's loads in flight, so they
+// are built for at most 2 vectors per lane (rows of up to 2048 lane vectors).
+constexpr int kMaxPartsVecsPerLane = 2;
 
 }  // namespace rn
 

@@ -4,6 +4,8 @@
 // "QK Norm" section of "CuTeDSL at Perplexity", extended with a residual add
 // and an fp8 output whose readings are stated in include/rmsnorm_rows.h):
 //   h   = round_res(x + residual)         (or h = x without a residual)
+//         with x = ((p_0 + p_1) + p_2) + ...  in float32 for the variants that
+//         sum K partial inputs (KP slots, K <= KP) in front of the add
 //   inv = rsqrt(sum(h^2) / H + eps)       (float32 accumulation)
 //   y   = (w + b) * (h * inv)             -> out (bf16 / f32), or
 //   fp8: p = (w + b) * h, amax = max|p| * inv, y = p * inv,
@@ -70,8 +72,15 @@ constexpr int storage_bits(int dt) {
 
 constexpr int max_of(int a, int b) { return a > b ? a : b; }
 
-template <int XD, int RD, int WD, int OD, int QS, int BIAS, int NV>
-__global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowArgs a) {
+// The 8-slot partial-input variant at one vector per lane fits 8 waves per
+// SIMD in VGPRs but, left alone, takes more SGPRs than 8 waves allow (eight
+// buffer resources next to the kernel arguments); asking for 8 waves moves
+// the excess into VGPR lanes, which keeps two 16-wave workgroups per CU.
+constexpr int min_waves_per_eu(int nv, int kp) { return kp == 8 && nv == 1 ? 8 : 1; }
+
+template <int XD, int RD, int WD, int OD, int QS, int BIAS, int NV, int KP>
+__global__ __launch_bounds__(max_threads_for_nv(NV)) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(NV, KP))))
+void rows_kernel(const RowArgs a) {
   constexpr int XB = storage_bits(XD) / 8;
   constexpr int VEC = 16 / XB;
   constexpr bool HAS_RES = RD != kNone;
@@ -93,6 +102,7 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowA
   static_assert(QS == kQRow || QUANT, "scale groups only for quantized outputs");
   static_assert(OD != kFP4 || QS == kQMx32 || QS == kQNv16, "fp4 output is MX- or NVFP4-scaled");
   static_assert(QS != kQNv16 || OD == kFP4, "NVFP4 scales are for fp4 output");
+  static_assert(KP == 1 || (KP <= kMaxParts && NV <= kMaxPartsVecsPerLane), "partial-input slots");
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -119,22 +129,45 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowA
 
   for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
     const int64_t row_elem = row * a.hidden;
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(xp + row_elem * XB, static_cast<uint32_t>(a.hidden) * XB);
+    // x, or partial-input slot k; a slot past num_parts gets an empty
+    // resource (its loads return zeros without touching memory)
+    auto x_rsrc = [&](int k) -> __amdgpu_buffer_rsrc_t {
+      if constexpr (KP == 1) {
+        return make_rsrc(xp + row_elem * XB, static_cast<uint32_t>(a.hidden) * XB);
+      } else {
+        const bool used = k < a.num_parts;
+        const char* pk = static_cast<const char*>(a.parts[used ? k : 0]);
+        return make_rsrc(pk + row_elem * XB, used ? static_cast<uint32_t>(a.hidden) * XB : 0u);
+      }
+    };
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(rp + row_elem * RB, static_cast<uint32_t>(a.hidden) * RB);
     const __amdgpu_buffer_rsrc_t orr =
         make_rsrc(op + row_elem * OBITS / 8, static_cast<uint32_t>(a.hidden) * OBITS / 8);
     const __amdgpu_buffer_rsrc_t ror = make_rsrc(rop + row_elem * RB, static_cast<uint32_t>(a.hidden) * RB);
 
-    // 1. Issue every load of this lane's share of the row.
-    uint32_t xw[NV][SUB][XW];
+    // 1. Issue every load of this lane's share of the row.  Partial inputs
+    //    go slot by slot, so that one slot's resource is live at a time.
+    uint32_t xw[NV][SUB][KP][XW];
     uint32_t rw[NV][SUB][HAS_RES ? RW : 1];
     uint32_t ww[NV][SUB][WW];
+    if constexpr (KP > 1) {
+#pragma unroll
+      for (int k = 0; k < KP; ++k) {
+        const __amdgpu_buffer_rsrc_t pr = x_rsrc(k);
+#pragma unroll
+        for (int s = 0; s < NV; ++s) {
+#pragma unroll
+          for (int c = 0; c < SUB; ++c) buffer_load_words<XW * 4, true>(pr, elem_of(s, c) * XB, xw[s][c][k]);
+        }
+      }
+    }
+    const __amdgpu_buffer_rsrc_t xr = x_rsrc(0);
 #pragma unroll
     for (int s = 0; s < NV; ++s) {
 #pragma unroll
       for (int c = 0; c < SUB; ++c) {
         const uint32_t e = elem_of(s, c);
-        buffer_load_words<XW * 4, true>(xr, e * XB, xw[s][c]);
+        if constexpr (KP == 1) buffer_load_words<XW * 4, true>(xr, e * XB, xw[s][c][0]);
         if constexpr (HAS_RES) buffer_load_words<RW * 4, true>(rr, e * RB, rw[s][c]);
         buffer_load_words<WW * 4, false>(wr, e * WB, ww[s][c]);
       }
@@ -152,7 +185,18 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowA
 #pragma unroll
       for (int c = 0; c < SUB; ++c) {
         float xf[U];
-        unpack<XD, U>(xw[s][c], xf);
+        unpack<XD, U>(xw[s][c][0], xf);
+        // partial inputs: added in slot order; the unused slots are skipped
+        // (adding their zeros would turn a -0 sum into +0)
+#pragma unroll
+        for (int k = 1; k < KP; ++k) {
+          if (k < a.num_parts) {
+            float pf[U];
+            unpack<XD, U>(xw[s][c][k], pf);
+#pragma unroll
+            for (int i = 0; i < U; ++i) xf[i] += pf[i];
+          }
+        }
         if constexpr (HAS_RES) {
           float rf[U], sum[U];
           unpack<RD, U>(rw[s][c], rf);
@@ -250,23 +294,41 @@ __global__ __launch_bounds__(max_threads_for_nv(NV)) void rows_kernel(const RowA
   }
 }
 
-template <int XD, int RD, int WD, int OD, int QS, int BIAS>
-const void* pick_nv(int nv) {
-  switch (nv) {
-    case 1: return reinterpret_cast<const void*>(&rows_kernel<XD, RD, WD, OD, QS, BIAS, 1>);
-    case 2: return reinterpret_cast<const void*>(&rows_kernel<XD, RD, WD, OD, QS, BIAS, 2>);
-    case 4: return reinterpret_cast<const void*>(&rows_kernel<XD, RD, WD, OD, QS, BIAS, 4>);
-    case 8: return reinterpret_cast<const void*>(&rows_kernel<XD, RD, WD, OD, QS, BIAS, 8>);
+template <int XD, int RD, int WD, int OD, int QS, int BIAS, int NV>
+const void* pick_kp(int kp) {
+  switch (kp) {
+    case 2: return reinterpret_cast<const void*>(&rows_kernel<XD, RD, WD, OD, QS, BIAS, NV, 2>);
+    case 4: return reinterpret_cast<const void*>(&rows_kernel<XD, RD, WD, OD, QS, BIAS, NV, 4>);
+    case 8: return reinterpret_cast<const void*>(&rows_kernel<XD, RD, WD, OD, QS, BIAS, NV, 8>);
     default: return nullptr;
   }
+}
+
+template <int XD, int RD, int WD, int OD, int QS, int BIAS>
+const void* pick_nv(int nv, int kp) {
+  if (kp == 1) {
+    switch (nv) {
+      case 1: return reinterpret_cast<const void*>(&rows_kernel<XD, RD, WD, OD, QS, BIAS, 1, 1>);
+      case 2: return reinterpret_cast<const void*>(&rows_kernel<XD, RD, WD, OD, QS, BIAS, 2, 1>);
+      case 4: return reinterpret_cast<const void*>(&rows_kernel<XD, RD, WD, OD, QS, BIAS, 4, 1>);
+      case 8: return reinterpret_cast<const void*>(&rows_kernel<XD, RD, WD, OD, QS, BIAS, 8, 1>);
+      default: return nullptr;
+    }
+  }
+  // partial inputs: bf16 / f32 outputs and fp8 with one scale per row
+  if constexpr (QS == kQRow) {
+    if (nv == 1) return pick_kp<XD, RD, WD, OD, QS, BIAS, 1>(kp);
+    if (nv == 2) return pick_kp<XD, RD, WD, OD, QS, BIAS, 2>(kp);
+  }
+  return nullptr;
 }
 
 template <int XD, int RD, int OD, int QS>
 const void* pick_weight(const RowKey& k) {
   if (k.w == kBF16)
-    return k.bias ? pick_nv<XD, RD, kBF16, OD, QS, 1>(k.nv) : pick_nv<XD, RD, kBF16, OD, QS, 0>(k.nv);
+    return k.bias ? pick_nv<XD, RD, kBF16, OD, QS, 1>(k.nv, k.kp) : pick_nv<XD, RD, kBF16, OD, QS, 0>(k.nv, k.kp);
   if (k.w == kF32)
-    return k.bias ? pick_nv<XD, RD, kF32, OD, QS, 1>(k.nv) : pick_nv<XD, RD, kF32, OD, QS, 0>(k.nv);
+    return k.bias ? pick_nv<XD, RD, kF32, OD, QS, 1>(k.nv, k.kp) : pick_nv<XD, RD, kF32, OD, QS, 0>(k.nv, k.kp);
   return nullptr;
 }
 
@@ -274,7 +336,8 @@ const void* pick_weight(const RowKey& k) {
 
 // Built combinations for this (x, out, scale scheme): residual none, f32, or
 // the x dtype; weight bf16 or f32; both weight forms; 1, 2, 4 or 8 vectors
-// per lane.
+// per lane; with one scale per row (or none), also the partial-input
+// variants: 2, 4 or 8 slots at 1 or 2 vectors per lane.
 const void* RN_CAT(pick_row_kernel_, RN_TU_NAME)(const RowKey& k) {
   if (k.x != RN_TU_X || k.out != RN_TU_OUT || k.qs != RN_TU_QS) return nullptr;
   switch (k.res) {

@@ -120,8 +120,11 @@ rn_status check_row_shape(int64_t rows, int64_t hidden, uint32_t flags, bool has
   key->qs = qs;
   key->bias = (flags & RN_FLAG_WEIGHT_PLUS_ONE) ? 1 : 0;
   key->nv = 0;
+  key->kp = 1;
   return RN_OK;
 }
+
+int parts_slots(int num_parts) { return num_parts <= 2 ? 2 : num_parts <= 4 ? 4 : 8; }
 
 static void fill_rows_cfg(int vec, int waves, int nv, int64_t rows, int64_t grid,
                           rn_launch_config* cfg) {
@@ -137,14 +140,29 @@ static void fill_rows_cfg(int vec, int waves, int nv, int64_t rows, int64_t grid
   if (cfg->grid < 1) cfg->grid = 1;
 }
 
-static bool rows_variant_ok(int waves, int nv, int64_t nvec) {
+static bool rows_variant_ok(int waves, int nv, int64_t nvec, int kp) {
   if (waves < 1 || waves > kMaxWavesPerRow) return false;
   if (nv != 1 && nv != 2 && nv != 4 && nv != 8) return false;
+  if (kp > 1 && nv > kMaxPartsVecsPerLane) return false;
   if (64 * waves > max_threads_for_nv(nv)) return false;
   return (int64_t)64 * waves * nv >= nvec;
 }
 
 static const int64_t kMaxGrid = 0x7FFFFFFF;
+
+// Partial-input kernels (bf16 partials, f32 residual, bf16 out), measured on
+// MI355X at about 0.6 GB of traffic per call over every variant within two
+// waves of the exact fit at 1 and 2 vectors per lane (three interleaved
+// repetitions): the entries where the exact fit with the fewest vectors per
+// lane lost 2% or more.  Key: partial-input slots (2, 4, 8), hidden size.
+struct TunedParts {
+  int kp;
+  int hidden;
+  int waves, nv;
+};
+static const TunedParts kTunedParts[] = {
+    {2, 7168, 16, 1}, {4, 4096, 4, 2}, {4, 7168, 8, 2}, {4, 8192, 8, 2}, {8, 7168, 8, 2},
+};
 
 // Fastest (waves, vectors per lane) measured on MI355X for prefill-sized row
 // counts with a bf16 weight: each entry won an interleaved sweep of the
@@ -289,7 +307,7 @@ static rn_status select_rows_shape(int64_t rows, int64_t hidden, const RowKey& k
   const int64_t nvec = hidden / vec;
   const int choices[4] = {1, 2, 4, 8};
   int waves = 0, nv = 0;
-  if (rows > num_cus && tw > 0 && rows_variant_ok(tw, tnv, nvec)) {
+  if (rows > num_cus && tw > 0 && rows_variant_ok(tw, tnv, nvec, key.kp)) {
     waves = tw;
     nv = tnv;
   }
@@ -298,7 +316,7 @@ static rn_status select_rows_shape(int64_t rows, int64_t hidden, const RowKey& k
   if (!nv && rows <= num_cus && compact_decode) {
     for (int f : choices) {
       const int64_t w = nvec <= 128 ? 1 : (nvec + 64 * f - 1) / (64 * f) < 8 ? (nvec + 64 * f - 1) / (64 * f) : 8;
-      if (rows_variant_ok(static_cast<int>(w), f, nvec)) {
+      if (rows_variant_ok(static_cast<int>(w), f, nvec, key.kp)) {
         waves = static_cast<int>(w);
         nv = f;
         break;
@@ -311,7 +329,7 @@ static rn_status select_rows_shape(int64_t rows, int64_t hidden, const RowKey& k
     if (nv) break;
     int64_t w = (nvec + 64 * f - 1) / (64 * f);
     if (w < 1) w = 1;
-    if (w <= kMaxWavesPerRow && rows_variant_ok(static_cast<int>(w), f, nvec)) {
+    if (w <= kMaxWavesPerRow && rows_variant_ok(static_cast<int>(w), f, nvec, key.kp)) {
       waves = static_cast<int>(w);
       nv = f;
     }
@@ -325,7 +343,8 @@ rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int
                             rn_launch_config* cfg) {
   int tw = 0, tnv = 0;
   const bool quant = key.out == kFP8 || key.out == kFP4;
-  if (key.w == kBF16 && num_cus >= 1 && rows > num_cus) {  // the tables were measured with a bf16 weight
+  // the tables were measured with a bf16 weight and a single x input
+  if (key.w == kBF16 && key.kp == 1 && num_cus >= 1 && rows > num_cus) {
     int bucket = 0;  // rows per CU, rounded up to 2, 4, 8 or 16; 0 above that
     for (int b = 2; b <= 16; b *= 2) {
       if (rows <= static_cast<int64_t>(b) * num_cus) {
@@ -348,6 +367,15 @@ rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int
       }
     }
   }
+  if (key.kp > 1 && key.x == kBF16 && num_cus >= 1 && rows > num_cus) {
+    for (const TunedParts& t : kTunedParts) {
+      if (t.kp == key.kp && t.hidden == hidden) {
+        tw = t.waves;
+        tnv = t.nv;
+        break;
+      }
+    }
+  }
   return select_rows_shape(rows, hidden, key, num_cus, tw, tnv, true, cfg);
 }
 
@@ -357,7 +385,7 @@ rn_status check_row_config(int64_t rows, int64_t hidden, const RowKey& key,
   if (in->kernel != RN_KERNEL_ROWS) return fail(RN_ERR_INVALID_ARG, "config kernel must be RN_KERNEL_ROWS");
   const int vec = 16 / (key.x == kBF16 ? 2 : 4);
   const int64_t nvec = hidden / vec;
-  if (!rows_variant_ok(in->waves_per_row, in->vecs_per_lane, nvec))
+  if (!rows_variant_ok(in->waves_per_row, in->vecs_per_lane, nvec, key.kp))
     return fail(RN_ERR_INVALID_ARG, "config waves_per_row=%d vecs_per_lane=%d does not cover %lld "
                 "lane vectors or is not built", in->waves_per_row, in->vecs_per_lane, (long long)nvec);
   if (in->grid < 1 || in->grid > kMaxGrid || (rows > 0 && in->grid > rows))
@@ -392,6 +420,7 @@ rn_status select_act_config(int64_t rows, int64_t d, const ActKey& key, int num_
   rk.qs = key.qs;
   rk.bias = 0;
   rk.nv = 0;
+  rk.kp = 1;
   int tw = 0, tnv = 0;
   if (key.x == kBF16 && num_cus >= 1 && rows > num_cus) {
     const int cls = key.out == kFP8 ? 1 : key.out == kFP4 ? 2 : 0;

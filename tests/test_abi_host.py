@@ -321,3 +321,88 @@ def test_explicit_config_is_checked(lib):
     st = lib.rmsnorm_fwd_config(FAKE, FAKE, FAKE, FAKE + 0x1000, FAKE + 0x2000, None, None, None, 4, 1024, 1e-6, BF,
                                 ctypes.byref(cfg), None)
     assert st == L.RN_ERR_INVALID_ARG
+
+
+# --- partial inputs ---------------------------------------------------------
+
+def _parts_ptrs(*ptrs):
+    return (ctypes.c_void_p * max(len(ptrs), 1))(*ptrs)
+
+
+P0, P1, P2 = FAKE + 0x10000, FAKE + 0x20000, FAKE + 0x30000
+
+
+def _pfwd(lib, parts=(P0, P1), n=None, res=FAKE, w=FAKE, out=FAKE + 0x1000, res_out=FAKE + 0x2000, scale=None,
+          amax=None, rows=4, hidden=1024, eps=1e-6, flags=BF):
+    arr = None if parts is None else _parts_ptrs(*parts)
+    return lib.rmsnorm_fwd_partials(arr, len(parts or ()) if n is None else n, res, w, out, res_out, scale, amax,
+                                    rows, hidden, eps, flags, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=0), L.RN_ERR_INVALID_ARG),
+    (dict(n=9, parts=(P0,) * 9), L.RN_ERR_INVALID_ARG),
+    (dict(n=-1), L.RN_ERR_INVALID_ARG),
+    (dict(parts=None, n=2), L.RN_ERR_INVALID_ARG),
+    (dict(parts=(P0, None)), L.RN_ERR_INVALID_ARG),
+    (dict(parts=(P0, P1 + 8)), L.RN_ERR_MISALIGNED),
+    (dict(parts=(P0, FAKE + 0x2000)), L.RN_ERR_INVALID_ARG),  # residual_out is a partial
+    (dict(res_out=FAKE + 0x1000), L.RN_ERR_INVALID_ARG),  # out == residual_out
+    (dict(res=None), L.RN_ERR_INVALID_ARG),
+    (dict(w=None), L.RN_ERR_INVALID_ARG),
+    (dict(hidden=16384 + 8), L.RN_ERR_UNSUPPORTED),  # above 2048 lane vectors with more than one partial
+    (dict(flags=_qflags("fp8_e4m3fn", "group128"), scale=FAKE + 0x3000), L.RN_ERR_UNSUPPORTED),
+    (dict(flags=_qflags("fp4_e2m1", "mx32"), scale=FAKE + 0x3000), L.RN_ERR_UNSUPPORTED),
+    (dict(flags=L.make_flags("bf16", "bf16", "bf16", "fp8_e4m3fn", False)), L.RN_ERR_INVALID_ARG),  # no scale
+    (dict(eps=float("nan")), L.RN_ERR_INVALID_ARG),
+])
+def test_partials_reject_before_any_hip_call(lib, kw, status):
+    assert _pfwd(lib, **kw) == status
+    assert lib.rn_last_error().decode() != ""
+
+
+def test_partials_rows_zero_is_a_noop(lib):
+    assert lib.rmsnorm_fwd_partials(None, 3, None, None, None, None, None, None, 0, 1024, 1e-6, L.make_flags(
+        "bf16", None, "bf16", "bf16", False), None) == L.RN_OK
+    # the count is still checked
+    assert lib.rmsnorm_fwd_partials(None, 0, None, None, None, None, None, None, 0, 1024, 1e-6, BF, None) \
+        == L.RN_ERR_INVALID_ARG
+
+
+def test_partials_selector():
+    # at most 2 vectors per lane for more than one partial; the single-input
+    # tables do not apply to them
+    for x, vec, hmax in (("bf16", 8, 16384), ("f32", 4, 8192)):
+        for n in (2, 3, 4, 5, 8):
+            for hidden in list(range(vec, 4096 + 1, vec * 13)) + [7168, 8192, hmax]:
+                if hidden > hmax:
+                    continue
+                for rows in (1, 64, 256, 257, 2048, 16384):
+                    c = R.query_partials_config(rows, hidden, n, x_dtype=x, res_dtype="f32",
+                                                out_dtype="bf16", w_dtype="bf16")
+                    W, NV = c["waves_per_row"], c["vecs_per_lane"]
+                    assert NV in (1, 2) and 1 <= W <= 16 and 64 * W * NV * vec >= hidden, (x, n, hidden, rows, c)
+                    assert c["grid"] == rows
+    c = R.query_partials_config(2048, 8192, 8, res_dtype="f32")
+    assert (c["waves_per_row"], c["vecs_per_lane"]) == (16, 1)
+    c = R.query_partials_config(3840, 8192, 4, res_dtype="f32")  # measured: 8 x 2 beats 16 x 1 by 7%
+    assert (c["waves_per_row"], c["vecs_per_lane"]) == (8, 2)
+    c = R.query_partials_config(3072, 7168, 7, res_dtype="f32")  # 8 slots: 8 x 2 beats 14 x 1 by 6%
+    assert (c["waves_per_row"], c["vecs_per_lane"]) == (8, 2)
+    c = R.query_partials_config(32, 8192, 8, res_dtype="f32")  # decode: at most 8 waves
+    assert (c["waves_per_row"], c["vecs_per_lane"]) == (8, 2)
+    # one partial is the single-input kernel and its tables
+    assert R.query_partials_config(8192, 7168, 1, res_dtype="bf16", out_dtype="fp8_e4m3fn") == \
+        R.query_config(8192, 7168, res_dtype="bf16", out_dtype="fp8_e4m3fn")
+
+
+def test_partials_explicit_config_is_checked(lib):
+    cfg = L.LaunchConfig()
+    cfg.kernel, cfg.waves_per_row, cfg.vecs_per_lane, cfg.grid = 0, 2, 4, 4  # 4 vectors per lane: not built
+    arr = _parts_ptrs(P0, P1, P2)
+    st = lib.rmsnorm_fwd_partials_config(arr, 3, FAKE, FAKE, FAKE + 0x1000, FAKE + 0x2000, None, None, 4, 1024,
+                                         1e-6, BF, ctypes.byref(cfg), None)
+    assert st == L.RN_ERR_INVALID_ARG
+    st = lib.rmsnorm_fwd_partials_config(arr, 3, FAKE, FAKE, FAKE + 0x1000, FAKE + 0x2000, None, None, 4, 1024,
+                                         1e-6, BF, None, None)
+    assert st == L.RN_ERR_INVALID_ARG

@@ -1,0 +1,190 @@
+"""GPU parity of the partial-input entry point (rmsnorm_fwd_partials) against the oracle.
+
+Inputs come from ``workloads.generate_partials``.  Under its exact-sum recipe
+every float32 prefix sum of the partials is exact, so the kernel's sum order
+cannot show and the single-input rules apply (updated residual bit-exact,
+outputs to ``oracle.compare``'s tolerances).  General float32 partials are
+judged against the error bound of a float32 sum (``tests.gpu_util.partials_bounds``).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import residual_add_rmsnorm_rows_amd as R
+import workloads as WL
+from oracle import rownorm as O
+from residual_add_rmsnorm_rows_amd import _lib as L
+from tests.gpu_util import TORCH_DTYPES, judge_partials_rows, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _wl(rows, hidden, k, x="bf16", res="f32", w="bf16", out="bf16", bias=False, exact=True, eps=1e-6,
+        part_std=0.5):
+    return WL.PartialsWorkload(
+        name="t", rows=rows, hidden=hidden, num_partials=k, x_dtype=x, res_dtype=res, w_dtype=w, out_dtype=out,
+        part_dist=WL.Dist(0.0, part_std), res_dist=None if res is None else WL.Dist(0.0, 4.0 if res == "f32" else 1.0),
+        w_dist=WL.Dist(0.0, 0.02) if bias else WL.Dist(1.0, 0.1), weight_plus_one=bias, eps=eps, exact_sum=exact)
+
+
+def run_partials(wl, inputs, config=None, out_into_part=None):
+    parts = [to_dev(p, wl.x_dtype) for p in inputs["partials"]]
+    res = None if inputs["residual"] is None else to_dev(inputs["residual"], wl.res_dtype)
+    w = to_dev(inputs["weight"], wl.w_dtype)
+    kw = {}
+    if out_into_part is not None:
+        kw["out"] = parts[out_into_part]
+    r = R.fused_partials_add_rmsnorm(parts, res, w, wl.eps, weight_plus_one=wl.weight_plus_one,
+                                     out_dtype=TORCH_DTYPES[wl.out_dtype], return_amax=wl.out_dtype == "fp8_e4m3fn",
+                                     config=config, **kw)
+    torch.cuda.synchronize()
+    return r
+
+
+def oracle_ref(wl, inputs):
+    parts = [O.decode(p, wl.x_dtype) for p in inputs["partials"]]
+    res = None if inputs["residual"] is None else O.decode(inputs["residual"], wl.res_dtype)
+    return O.rmsnorm_rows_partials(parts, O.decode(inputs["weight"], wl.w_dtype), wl.eps,
+                                   1.0 if wl.weight_plus_one else 0.0, residual=res, res_dtype=wl.res_dtype)
+
+
+def judge(wl, inputs, r, rows=None, ref=None):
+    sel = slice(None) if rows is None else rows
+    sub = {"partials": [p[sel] for p in inputs["partials"]],
+           "residual": None if inputs["residual"] is None else inputs["residual"][sel], "weight": inputs["weight"]}
+    out = to_host(r.out)[sel]
+    res_out = None if r.residual_out is None else to_host(r.residual_out)[sel]
+    scale = None if r.scale is None else to_host(r.scale)[sel]
+    amax = None if r.amax is None else to_host(r.amax)[sel]
+    return judge_partials_rows(sub, wl.x_dtype, wl.res_dtype, wl.w_dtype, wl.out_dtype, wl.eps, wl.weight_plus_one,
+                               out, res_out, scale, amax, exact_sum=wl.exact_sum, ref=ref)
+
+
+def test_workload_small():
+    wl = WL.WORKLOADS["partials_8x2048x8192"].with_rows(300)
+    _announce(f"partials workload 300 rows cfg={R.query_partials_config(300, 8192, 8, res_dtype='f32')}")
+    inp = WL.generate_partials(wl, seed=1)
+    rep = judge(wl, inp, run_partials(wl, inp))
+    assert rep["ok"], rep
+
+
+def test_workload_full_size_sampled():
+    """2048 x 8192 with 8 partials in the selector's launch configuration; the
+    oracle checks sampled rows, including the first and the last."""
+    wl = WL.WORKLOADS["partials_8x2048x8192"]
+    _announce(f"partials full size cfg={R.query_partials_config(wl.rows, wl.hidden, 8, res_dtype='f32')}")
+    inp = WL.generate_partials(wl, seed=0)
+    r = run_partials(wl, inp)
+    rows = np.array([0, 1, 517, 1024, 2046, 2047])
+    rep = judge(wl, inp, r, rows=rows)
+    assert rep["ok"], rep
+
+
+CASES = [  # (x, res, w, out, bias)
+    ("bf16", "f32", "bf16", "bf16", False), ("bf16", "bf16", "bf16", "bf16", True),
+    ("bf16", None, "bf16", "bf16", False), ("bf16", "f32", "f32", "f32", False),
+    ("bf16", "bf16", "bf16", "fp8_e4m3fn", False), ("bf16", None, "f32", "fp8_e4m3fn", True),
+    ("f32", "f32", "f32", "f32", False), ("f32", None, "bf16", "bf16", True), ("f32", "f32", "bf16", "fp8_e4m3fn", False),
+]
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("x,res,w,out,bias", CASES)
+@pytest.mark.parametrize("rows,hidden", [(37, 1000), (5, 4096)])
+def test_dtype_combinations(x, res, w, out, bias, k, rows, hidden):
+    wl = _wl(rows, hidden, k, x, res, w, out, bias)
+    _announce(f"partials k={k} {x}/{res}/{w}->{out} bias={bias} {rows}x{hidden}")
+    inp = WL.generate_partials(wl, seed=7 + k)
+    rep = judge(wl, inp, run_partials(wl, inp))
+    assert rep["ok"], rep
+
+
+def _variants(hidden, vec):
+    nvec = -(-hidden // vec)
+    for W in range(1, 17):
+        for NV in (1, 2):
+            if 64 * W * NV >= nvec and (NV == 1 or 64 * W < nvec or W == 1):
+                yield W, NV
+
+
+@pytest.mark.parametrize("k", [2, 4, 8])
+@pytest.mark.parametrize("x,out", [("bf16", "bf16"), ("bf16", "fp8_e4m3fn"), ("f32", "f32")])
+def test_every_launch_variant(k, x, out):
+    hidden = 3000 if x == "bf16" else 1500
+    wl = _wl(41, hidden, k, x, "f32", "bf16", out)
+    inp = WL.generate_partials(wl, seed=3)
+    ref = oracle_ref(wl, inp)
+    for i, (W, NV) in enumerate(_variants(hidden, 8 if x == "bf16" else 4)):
+        for grid in (41, 13) if i % 4 == 0 else (41,):
+            cfg = L.LaunchConfig()
+            cfg.kernel, cfg.waves_per_row, cfg.vecs_per_lane, cfg.grid = 0, W, NV, grid
+            _announce(f"partials variant k={k} {x}->{out} W={W} NV={NV} grid={grid}")
+            rep = judge(wl, inp, run_partials(wl, inp, config=cfg), ref=ref)
+            assert rep["ok"], (W, NV, grid, rep)
+
+
+@pytest.mark.parametrize("x,k,res,out", [("f32", 8, "f32", "f32"), ("f32", 8, "f32", "bf16"), ("f32", 3, None, "f32"),
+                                         ("bf16", 5, "bf16", "bf16"), ("bf16", 8, "f32", "bf16")])
+def test_inexact_float32_sums_within_bound(x, k, res, out):
+    """General partials (no exact-sum recipe): each float32 addition may round."""
+    wl = _wl(64, 2048, k, x, res, "bf16", out, exact=False, part_std=1.0)
+    _announce(f"partials inexact {x} k={k} res={res} out={out}")
+    inp = WL.generate_partials(wl, seed=11)
+    rep = judge(wl, inp, run_partials(wl, inp))
+    assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("rows", [1, 32, 256])
+def test_decode_shapes(rows):
+    wl = WL.WORKLOADS["partials_8x2048x8192"].with_rows(rows)
+    _announce(f"partials decode rows={rows} cfg={R.query_partials_config(rows, 8192, 8, res_dtype='f32')}")
+    inp = WL.generate_partials(wl, seed=rows)
+    rep = judge(wl, inp, run_partials(wl, inp))
+    assert rep["ok"], rep
+
+
+def test_out_in_place_over_a_partial():
+    wl = _wl(33, 2048, 4, "bf16", "bf16", "bf16", "bf16")
+    _announce("partials in place")
+    inp = WL.generate_partials(wl, seed=5)
+    r = run_partials(wl, inp, out_into_part=2)
+    rep = judge(wl, inp, r)
+    assert rep["ok"], rep
+
+
+def test_single_partial_and_zero_partials_match_the_single_input_kernel():
+    """[x] and [x, 0, 0] give the bits of fused_add_rmsnorm(x)."""
+    wl = _wl(20, 4096, 1, "bf16", "f32", "bf16", "fp8_e4m3fn")
+    _announce("partials vs single input")
+    inp = WL.generate_partials(wl, seed=2)
+    x = to_dev(inp["partials"][0], "bf16")
+    res = to_dev(inp["residual"], "f32")
+    w = to_dev(inp["weight"], "bf16")
+    ref = R.fused_add_rmsnorm(x, res, w, wl.eps, out_dtype=torch.float8_e4m3fn)
+    z = torch.zeros_like(x)
+    for parts in ([x], [x, z, z]):
+        got = R.fused_partials_add_rmsnorm(parts, res, w, wl.eps, out_dtype=torch.float8_e4m3fn)
+        torch.cuda.synchronize()
+        assert torch.equal(got.out.view(torch.uint8), ref.out.view(torch.uint8))
+        assert torch.equal(got.residual_out, ref.residual_out)
+        assert torch.equal(got.scale, ref.scale)
+
+
+def test_zero_rows_and_all_zero_partials():
+    wl = _wl(6, 1024, 3, "bf16", None, "bf16", "fp8_e4m3fn")
+    inp = WL.generate_partials(wl, seed=9)
+    for p in inp["partials"]:
+        p[2] = 0
+    _announce("partials zero row")
+    r = run_partials(wl, inp)
+    rep = judge(wl, inp, r)
+    assert rep["ok"], rep
+    assert float(r.scale[2]) == 0.0 and not to_host(r.out)[2].any()
+    empty = [torch.empty(0, 1024, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    e = R.fused_partials_add_rmsnorm(empty, None, to_dev(inp["weight"], "bf16"), 1e-6)
+    assert e.out.shape == (0, 1024)
