@@ -35,7 +35,7 @@ def _rows(path: str) -> List[Dict[str, str]]:
         return list(csv.DictReader(f))
 
 
-def stats(csv_path: str, command: str, notes=()) -> str:
+def stats(csv_path: str, command: str, notes=(), trace_path: str = "") -> str:
     rows = _rows(csv_path)
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     lines = [
@@ -47,6 +47,22 @@ def stats(csv_path: str, command: str, notes=()) -> str:
     for r in rows:
         lines.append(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.3f} {float(r['MinNs']) / 1e3:10.3f} "
                      f"{float(r['MaxNs']) / 1e3:10.3f} {float(r['TotalDurationNs']) / 1e6:10.3f}  {r['Name']}")
+    if trace_path:
+        # kernels dispatched with several grid sizes (workloads sharing a
+        # compiled kernel): the same figures per grid size, from the trace
+        per = {}
+        for r in _rows(trace_path):
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            per.setdefault(r["Kernel_Name"], {}).setdefault(grid, []).append(dur)
+        split = [(name, g, d) for name, grids in per.items() if len(grids) > 1 for g, d in grids.items()]
+        if split:
+            lines.append("# per grid size (threads), for kernels launched with more than one; from the kernel trace")
+            lines.append("# columns: calls  avg_us  min_us  max_us  total_ms  grid  kernel")
+            split.sort(key=lambda t: -sum(t[2]))
+            for name, g, d in split:
+                lines.append(f"{len(d):7d} {statistics.mean(d):10.3f} {min(d):10.3f} {max(d):10.3f} "
+                             f"{sum(d) / 1e3:10.3f} {g:>10d}  {name}")
     return "\n".join(lines) + "\n"
 
 
@@ -74,12 +90,15 @@ def _last_json(path: str) -> dict:
     return json.loads(lines[-1])
 
 
-def traffic(fetch_csv: str, write_csv: str, kernel: str, bench_out: str, command: str, entry: str = "") -> str:
+def traffic(fetch_csv: str, write_csv: str, kernel: str, bench_out: str, command: str, entry: str = "",
+            grid_size: int = 0) -> str:
     fr, wr = _rows(fetch_csv), _rows(write_csv)
     names = sorted({r["Kernel_Name"] for r in fr + wr if kernel in r["Kernel_Name"]})
     if len(names) != 1:
         raise SystemExit(f"kernel substring {kernel!r} matches {names}")
-    main = lambda r: r["Kernel_Name"] == names[0]  # noqa: E731
+
+    def main(r):  # the kernel's dispatches; with grid_size, only those of that grid (threads)
+        return r["Kernel_Name"] == names[0] and (not grid_size or int(r["Grid_Size"]) == grid_size)
     fetch_k = _counter(fr, "FETCH_SIZE", main)
     write_k = _counter(wr, "WRITE_SIZE", main)
     cf = _counter(fr, "FETCH_SIZE", _copy_rows(fr, "FETCH_SIZE"))
@@ -99,7 +118,7 @@ def traffic(fetch_csv: str, write_csv: str, kernel: str, bench_out: str, command
         "# HBM traffic per launch from rocprofv3 counters (FETCH_SIZE and WRITE_SIZE runs),",
         "# each scaled by the same counter's reading for a 1 GiB device copy in the same run.",
         f"# command (FETCH_SIZE; the WRITE_SIZE run differs only in the counter): {command}",
-        f"kernel: {names[0]}",
+        f"kernel: {names[0]}" + (f" (dispatches with grid size {grid_size} threads)" if grid_size else ""),
         f"workload: {workload}",
         f"library_sha256: {bench['config']['library_sha256']}",
         f"dispatches_fetch: {len(fetch_k)}",
@@ -128,6 +147,7 @@ def main(argv=None) -> int:
     s.add_argument("--command", required=True)
     s.add_argument("--out", required=True)
     s.add_argument("--note", action="append", default=[])
+    s.add_argument("--trace", default="", help="run_kernel_trace.csv: also split kernels by grid size")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -136,9 +156,11 @@ def main(argv=None) -> int:
     t.add_argument("--command", required=True)
     t.add_argument("--out", required=True)
     t.add_argument("--entry", default="", help="secondary workload of the benchmark line (default: the main one)")
+    t.add_argument("--grid-size", type=int, default=0,
+                   help="only the dispatches with this grid size in threads (when workloads share a kernel)")
     a = ap.parse_args(argv)
-    text = stats(a.csv, a.command, a.note) if a.what == "stats" else traffic(a.fetch, a.write, a.kernel, a.bench_out,
-                                                                        a.command, a.entry)
+    text = stats(a.csv, a.command, a.note, a.trace) if a.what == "stats" else traffic(a.fetch, a.write, a.kernel, a.bench_out,
+                                                                        a.command, a.entry, a.grid_size)
     with open(a.out, "w") as f:
         f.write(text)
     print(text)
