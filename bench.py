@@ -392,43 +392,84 @@ def partials_bytes(wl) -> int:
     return wl.rows * per_row + wl.hidden * size[wl.w_dtype]
 
 
-def partials_metrics(name: str, steps: int, warmup: int, sets: int = 2) -> dict:
-    import torch
+class PartialsCall:
+    """Device buffers of one partial-input workload and a raw C-ABI call over them."""
 
+    def __init__(self, wl, sets: int = 1):
+        import torch
+
+        import workloads as WL
+        from residual_add_rmsnorm_rows_amd import _lib as L
+        from tests.gpu_util import TORCH_DTYPES, to_dev
+
+        self.wl = wl
+        inp = WL.generate_partials(wl, seed=0)
+        parts0 = [to_dev(p, wl.x_dtype) for p in inp["partials"]]
+        res0 = to_dev(inp["residual"], wl.res_dtype)
+        self.w = to_dev(inp["weight"], wl.w_dtype)
+        self.sets = []
+        for i in range(sets):
+            parts = parts0 if i == 0 else [p.clone() for p in parts0]
+            res = res0 if i == 0 else res0.clone()
+            ptrs = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
+            out = torch.empty(wl.rows, wl.hidden, dtype=TORCH_DTYPES[wl.out_dtype], device="cuda")
+            self.sets.append((parts, ptrs, res, torch.empty_like(res), out))
+        self.L = L.lib()
+        self.flags = L.make_flags(wl.x_dtype, wl.res_dtype, wl.w_dtype, wl.out_dtype, wl.weight_plus_one)
+        self.i = 0
+
+    def __call__(self, stream: int) -> None:
+        _, ptrs, res, ro, out = self.sets[self.i]
+        self.i = (self.i + 1) % len(self.sets)
+        wl = self.wl
+        st = self.L.rmsnorm_fwd_partials(ptrs, wl.num_partials, res.data_ptr(), self.w.data_ptr(), out.data_ptr(),
+                                         ro.data_ptr(), None, None, wl.rows, wl.hidden, wl.eps, self.flags, stream)
+        if st != 0:
+            from residual_add_rmsnorm_rows_amd._lib import check
+            check(st)
+
+
+def partials_metrics(name: str, steps: int, warmup: int, sets: int = 2) -> dict:
     import workloads as WL
-    from residual_add_rmsnorm_rows_amd import _lib as L
-    from tests.gpu_util import TORCH_DTYPES, to_dev
 
     wl = WL.WORKLOADS[name]
-    inp = WL.generate_partials(wl, seed=0)
-    parts0 = [to_dev(p, wl.x_dtype) for p in inp["partials"]]
-    res0 = to_dev(inp["residual"], wl.res_dtype)
-    w = to_dev(inp["weight"], wl.w_dtype)
-    bufs = []
-    for i in range(sets):
-        parts = parts0 if i == 0 else [p.clone() for p in parts0]
-        res = res0 if i == 0 else res0.clone()
-        ptrs = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
-        out = torch.empty(wl.rows, wl.hidden, dtype=TORCH_DTYPES[wl.out_dtype], device="cuda")
-        bufs.append((parts, ptrs, res, torch.empty_like(res), out))
-    lib = L.lib()
-    flags = L.make_flags(wl.x_dtype, wl.res_dtype, wl.w_dtype, wl.out_dtype, wl.weight_plus_one)
-    state = {"i": 0}
-
-    def call(stream):
-        _, ptrs, res, ro, out = bufs[state["i"]]
-        state["i"] = (state["i"] + 1) % sets
-        st = lib.rmsnorm_fwd_partials(ptrs, wl.num_partials, res.data_ptr(), w.data_ptr(), out.data_ptr(),
-                                      ro.data_ptr(), None, None, wl.rows, wl.hidden, wl.eps, flags, stream)
-        if st != 0:
-            L.check(st)
-
+    call = PartialsCall(wl, sets)
     ms = time_stream_loop(call, steps, warmup)
     spread = launch_percentiles(call)
     b = partials_bytes(wl)
     return {"workload": wl.description, "us_per_call": round(ms * 1000, 3), "algorithmic_bytes": b,
             "GBps": round(b / (ms * 1e-3) / 1e9, 1), "frac_of_peak": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "buffer_sets": sets, "launch_us": spread}
+
+
+def partials_decode_metrics(name: str) -> dict:
+    """Latency of a decode-sized partial-input call against an empty launch (graph and eager)."""
+    import workloads as WL
+    import residual_add_rmsnorm_rows_amd as R
+    from residual_add_rmsnorm_rows_amd import _lib as L
+
+    wl = WL.WORKLOADS[name]
+    call = PartialsCall(wl)
+    lib = L.lib()
+
+    def empty(stream):
+        lib.rn_launch_empty(stream)
+
+    eager = time_stream_loop(call, 2000, 100) * 1000.0
+    eager_empty = time_stream_loop(empty, 2000, 100) * 1000.0
+    graph = time_graph_loop(call)
+    graph_empty = time_graph_loop(empty)
+    sel = R.query_partials_config(wl.rows, wl.hidden, wl.num_partials, x_dtype=wl.x_dtype, res_dtype=wl.res_dtype,
+                                  w_dtype=wl.w_dtype, out_dtype=wl.out_dtype, num_cus=0)
+    return {
+        "workload": wl.description, "rows": wl.rows, "hidden": wl.hidden, "num_partials": wl.num_partials,
+        "launch": {"waves_per_row": sel["waves_per_row"], "vecs_per_lane": sel["vecs_per_lane"]},
+        "us_per_call_eager": round(eager, 3), "empty_us_per_call_eager": round(eager_empty, 3),
+        "ratio_eager": round(eager / eager_empty, 3),
+        "us_per_call_graph": round(graph, 3), "empty_us_per_call_graph": round(graph_empty, 3),
+        "ratio_graph": round(graph / graph_empty, 3),
+        "algorithmic_bytes": partials_bytes(wl),
+    }
 
 
 def act_metrics(steps: int, warmup: int, out_dtype: str = "bf16", scale_scheme: str = "row", sets: int = 2) -> dict:
@@ -696,6 +737,9 @@ def main() -> int:
                                                         out_dtype="fp4_e2m1", scale_scheme="nv16")
         log("partials_8x2048x8192")
         sec["partials_8x2048x8192"] = partials_metrics("partials_8x2048x8192", args.steps * 2, args.warmup)
+        if not args.no_decode:
+            log("partials_decode_8x64x8192")
+            sec["partials_decode_8x64x8192"] = partials_decode_metrics("partials_decode_8x64x8192")
         log("silu_mul_8192x14336")
         # the quantized variants do more arithmetic per byte; the GPU's power
         # management lowers clocks for a few ms after such a load starts, so

@@ -376,6 +376,17 @@ rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int
       }
     }
   }
+  // Partial inputs, decode with more than half the CUs busy: 2 vectors per
+  // lane and the fewest waves (measured 2-14% faster than the decode rule's
+  // shape at 256 rows x 4096 / 8192 wide, 2-8 partials; slower at 64 rows).
+  if (key.kp > 1 && num_cus >= 1 && rows <= num_cus && 2 * rows > num_cus) {
+    const int vec = 16 / (key.x == kBF16 ? 2 : 4);
+    const int64_t w = (hidden / vec + 127) / 128;
+    if (w >= 1 && w <= kMaxWavesPerRow) {
+      fill_rows_cfg(vec, static_cast<int>(w), 2, rows, rows, cfg);
+      return RN_OK;
+    }
+  }
   return select_rows_shape(rows, hidden, key, num_cus, tw, tnv, true, cfg);
 }
 

@@ -389,6 +389,8 @@ def test_partials_selector():
     assert (c["waves_per_row"], c["vecs_per_lane"]) == (8, 2)
     c = R.query_partials_config(3072, 7168, 7, res_dtype="f32")  # 8 slots: 8 x 2 beats 14 x 1 by 6%
     assert (c["waves_per_row"], c["vecs_per_lane"]) == (8, 2)
+    c = R.query_partials_config(256, 4096, 4, res_dtype="f32")  # decode, chip more than half busy: 2 vectors
+    assert (c["waves_per_row"], c["vecs_per_lane"]) == (4, 2)
     c = R.query_partials_config(32, 8192, 8, res_dtype="f32")  # decode: at most 8 waves
     assert (c["waves_per_row"], c["vecs_per_lane"]) == (8, 2)
     # one partial is the single-input kernel and its tables

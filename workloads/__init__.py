@@ -211,6 +211,13 @@ WORKLOADS: Dict[str, object] = {
         description="sum of 8 bf16 partials ~ N(0,0.5) (one GPU's 2048-token share of an 8-way "
                     "tensor-parallel reduce-scatter) + f32 residual ~ N(0,4) + RMSNorm, 8192 wide, bf16 out",
     ),
+    "partials_decode_8x64x8192": PartialsWorkload(
+        name="partials_decode_8x64x8192", rows=64, hidden=8192, num_partials=8,
+        x_dtype="bf16", res_dtype="f32", w_dtype="bf16", out_dtype="bf16",
+        part_dist=Dist(0.0, 0.5), res_dist=Dist(0.0, 4.0), w_dist=W_N1, weight_plus_one=False, eps=1e-6,
+        description="decode: 8 bf16 partials of a 64-token batch summed (the local arithmetic of a one-shot "
+                    "all-reduce over 8 GPUs) + f32 residual + RMSNorm, 8192 wide, bf16 out",
+    ),
 }
 
 
