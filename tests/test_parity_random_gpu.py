@@ -172,3 +172,61 @@ def test_random_silu_mul(case):
     rep = judge_y(y, out, to_host(r.out), None if r.scale is None else to_host(r.scale),
                   None if r.amax is None else to_host(r.amax), scheme, ts)
     assert rep["y_ok"], rep
+
+
+def _partials_cases(n=32, seed=77):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        x = ["bf16", "f32"][rng.integers(2)]
+        res = [None, x, "f32"][rng.integers(3)]
+        w = ["bf16", "f32"][rng.integers(2)]
+        out = ["bf16", "f32", "fp8_e4m3fn"][rng.integers(3)]
+        vec = 8 if x == "bf16" else 4
+        k = int(rng.integers(1, 9))
+        hmax = (16384 if x == "bf16" else 8192) if k > 1 else 4096
+        hidden = vec * int(rng.integers(1, min(hmax, 6144) // vec + 1))
+        rows = int(rng.integers(1, 40))
+        exact = bool(rng.random() < 0.75) or out == "fp8_e4m3fn"
+        cases.append((i, x, res, w, out, bool(rng.integers(2)), k, hidden, rows, exact, int(rng.integers(1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _partials_cases(), ids=lambda c: f"p{c[0]}")
+def test_random_partials(case):
+    """Random partial-input calls; exact-sum inputs judged like single-input rows,
+    general ones against the float32 summation bound (bf16 / f32 outputs)."""
+    from tests.gpu_util import judge_partials_rows
+
+    i, x, res, w, out, b, k, hidden, rows, exact, seed = case
+    rng = np.random.default_rng(seed)
+    wl = WL.PartialsWorkload(name="rand", rows=rows, hidden=hidden, num_partials=k, x_dtype=x, res_dtype=res,
+                             w_dtype=w, out_dtype=out, part_dist=WL.Dist(0, float(rng.uniform(0.2, 2.0))),
+                             res_dist=None if res is None else WL.Dist(0, 3), w_dist=WL.Dist(0.0 if b else 1.0, 0.2),
+                             weight_plus_one=b, eps=float(np.float32(10.0 ** rng.uniform(-7, -3))), exact_sum=exact)
+    cfg = None
+    if rng.random() < 0.6:
+        vec = 8 if x == "bf16" else 4
+        nvec = -(-hidden // vec)
+        max_nv = 2 if k > 1 else 8
+        opts = [(W, NV) for W in range(1, 17) for NV in (1, 2, 4, 8)
+                if NV <= max_nv and 64 * W <= (512 if NV == 8 else 1024) and 64 * W * NV >= nvec
+                and 64 * W * NV <= 4 * nvec + 64]
+        W_, NV_ = opts[rng.integers(len(opts))]
+        cfg = L.LaunchConfig()
+        cfg.kernel, cfg.waves_per_row, cfg.vecs_per_lane = L.RN_KERNEL_ROWS, W_, NV_
+        cfg.grid = int(rng.integers(1, rows + 1))
+    cfg_txt = None if cfg is None else (cfg.waves_per_row, cfg.vecs_per_lane, cfg.grid)
+    _announce(f"random partials #{i}: k={k} x={x} res={res} w={w} out={out} plus_one={b} rows={rows} H={hidden} "
+              f"exact={exact} cfg={cfg_txt}")
+    inputs = WL.generate_partials(wl, seed=seed)
+    parts = [to_dev(p, x) for p in inputs["partials"]]
+    RES = None if res is None else to_dev(inputs["residual"], res)
+    r = R.fused_partials_add_rmsnorm(parts, RES, to_dev(inputs["weight"], w), wl.eps, weight_plus_one=b,
+                                     out_dtype=TORCH_DTYPES[out], return_amax=out == "fp8_e4m3fn", config=cfg)
+    torch.cuda.synchronize()
+    rep = judge_partials_rows(inputs, x, res, w, out, wl.eps, b, to_host(r.out),
+                              None if r.residual_out is None else to_host(r.residual_out),
+                              None if r.scale is None else to_host(r.scale), None if r.amax is None else to_host(r.amax),
+                              exact_sum=exact)
+    assert rep["ok"], rep
