@@ -98,6 +98,18 @@ def test_workload_parity_full_size_sampled(name):
     assert rep["ok"], rep
 
 
+def test_share_of_eight_full_size():
+    """The headline's 2048-row share over 8 GPUs (a bench line), all rows, in the
+    selector's launch configuration."""
+    wl = WL.WORKLOADS["prefill_16384x8192"].with_rows(2048)
+    _announce(f"prefill 2048 x 8192 cfg={R.query_config(wl.rows, wl.hidden, res_dtype='f32')}")
+    inputs = WL.generate_rownorm(wl, seed=0)
+    r = run_rownorm(wl, inputs)
+    rows = np.arange(0, wl.rows, 7)
+    rep = judge(wl, inputs, r, rows)
+    assert rep["ok"], rep
+
+
 def test_qknorm_workload_full():
     wl = WL.WORKLOADS["qknorm_4096x32x128"]
     _announce(f"{wl.name} tokens={wl.tokens} heads={wl.num_q_heads} D={wl.head_dim} "
