@@ -635,13 +635,16 @@ def test_graph_capture_replays():
     q = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device="cuda")
     act_in = torch.cat([x, res], dim=1).contiguous()
     act_out = torch.empty_like(x)
-    _announce("graph capture of rmsnorm / fp8 / silu_mul, 4 replays")
+    p_out = torch.empty_like(x)
+    p_ro = torch.empty_like(res)
+    _announce("graph capture of rmsnorm / fp8 / silu_mul / 3 partials, 4 replays")
 
     def step():
         R.fused_add_rmsnorm(x, res, w, wl.eps, out=out, residual_out=ro)
         r8 = R.fused_add_rmsnorm(x, res, w, wl.eps, out_dtype=torch.float8_e4m3fn, out=q,
                                  residual_out=torch.empty_like(res))
         R.silu_mul(act_in, out=act_out)
+        R.fused_partials_add_rmsnorm([x, res, x], res, w, wl.eps, out=p_out, residual_out=p_ro)
         return r8
 
     step()
@@ -657,11 +660,14 @@ def test_graph_capture_replays():
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        got = (to_host(out), to_host(ro), to_host(q), to_host(r8g.scale), to_host(act_out))
+        got = (to_host(out), to_host(ro), to_host(q), to_host(r8g.scale), to_host(act_out), to_host(p_out),
+               to_host(p_ro))
         e = R.fused_add_rmsnorm(x, res, w, wl.eps)
         e8 = R.fused_add_rmsnorm(x, res, w, wl.eps, out_dtype=torch.float8_e4m3fn)
         ea = R.silu_mul(act_in)
+        ep = R.fused_partials_add_rmsnorm([x, res, x], res, w, wl.eps)
         torch.cuda.synchronize()
-        want = (to_host(e.out), to_host(e.residual_out), to_host(e8.out), to_host(e8.scale), to_host(ea.out))
+        want = (to_host(e.out), to_host(e.residual_out), to_host(e8.out), to_host(e8.scale), to_host(ea.out),
+                to_host(ep.out), to_host(ep.residual_out))
         for a, b in zip(got, want):
             assert np.array_equal(a, b), k
