@@ -96,10 +96,9 @@ rn_status check_parts_key(int32_t num_parts, int64_t hidden, RowKey* key) {
 // parts_form: x is the sum of parts[0 .. num_parts) (x itself is unused);
 // otherwise the single-input form.
 rn_status rows_entry(bool parts_form, const void* x, const void* const* parts, int32_t num_parts,
-                     const void* residual,
-                     const void* weight, void* out, void* residual_out, void* out_scale, float* out_amax,
-                     const float* tensor_scale, int64_t rows, int64_t hidden, float eps, uint32_t flags,
-                     const rn_launch_config* explicit_cfg, void* stream) {
+                     const void* residual, const void* weight, void* out, void* residual_out, void* out_scale,
+                     float* out_amax, const float* tensor_scale, int64_t rows, int64_t hidden, float eps,
+                     uint32_t flags, const rn_launch_config* explicit_cfg, void* stream) {
   clear_error();
   RowKey key;
   rn_status st = check_row_shape(rows, hidden, flags, residual != nullptr, &key);
@@ -116,7 +115,8 @@ rn_status rows_entry(bool parts_form, const void* x, const void* const* parts, i
     if (parts == nullptr) return fail(RN_ERR_INVALID_ARG, "partials must not be NULL");
     for (int32_t k = 0; k < num_parts; ++k) {
       if (parts[k] == nullptr) return fail(RN_ERR_INVALID_ARG, "partials[%d] is NULL", k);
-      if (!aligned(parts[k], 16)) return fail(RN_ERR_MISALIGNED, "partials[%d] = %p is not 16-byte aligned", k, parts[k]);
+      if (!aligned(parts[k], 16))
+        return fail(RN_ERR_MISALIGNED, "partials[%d] = %p is not 16-byte aligned", k, parts[k]);
       if (residual_out != nullptr && parts[k] == residual_out)
         return fail(RN_ERR_INVALID_ARG, "residual_out must not be one of the partials");
     }
