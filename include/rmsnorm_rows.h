@@ -297,6 +297,15 @@ rn_status qknorm_fwd_config(const void* q, const void* k, const void* q_weight, 
  *   rows >= 0; d >= 1, a multiple of the 16-byte vector of x and at most 32768 (bf16) /
  *   16384 (f32); flags: bits 0-1 x dtype, bits 6-7 out dtype, bits 9-10 scale granularity
  *   (as for rmsnorm_fwd); other bits must be zero.  out may not overlap x.
+ *
+ * Range: the results hold the outputs' tolerances while |gate * up| is below
+ * float32's largest value (about 3.4e38).  Past it, bf16 / fp8 / fp4 outputs
+ * of a negative gate become -inf or NaN even where silu(gate) * up is finite,
+ * because the product gate * up is formed first.  For f32 outputs,
+ * exp(-|gate|) is a float32 subnormal beyond |gate| = 87.3 and carries fewer
+ * bits.  The relative error then grows, which shows only where the result is
+ * still a normal number (|up| above about 1e36).  Activations are many orders
+ * of magnitude inside these limits.
  */
 rn_status silu_mul_fwd(const void* x, void* out, void* out_scale, float* out_amax, const float* tensor_scale,
                        int64_t rows, int64_t d, uint32_t flags, void* stream);
