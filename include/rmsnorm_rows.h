@@ -174,6 +174,10 @@ typedef struct rn_launch_config {
  * scale 0 and all-zero codes.
  * Aliasing: out may equal x (in place) and residual_out may equal residual;
  * any other overlap is undefined, and out == residual_out is rejected.
+ * Range: the sum of squares accumulates in float32, as in the page's
+ * listing.  So the tolerances hold while h^2 stays a float32 value
+ * (|h| below about 1.8e19), and while the mean square does not underflow
+ * where eps is 0.  Rows outside that range give zeros or infinities.
  */
 rn_status rmsnorm_fwd(const void* x, const void* residual, const void* weight, void* out,
                       void* residual_out, void* out_scale, int64_t rows, int64_t hidden, float eps,
