@@ -376,10 +376,13 @@ rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int
       }
     }
   }
-  // Partial inputs, decode with more than half the CUs busy: 2 vectors per
-  // lane and the fewest waves (measured 2-14% faster than the decode rule's
-  // shape at 256 rows x 4096 / 8192 wide, 2-8 partials; slower at 64 rows).
-  if (key.kp > 1 && num_cus >= 1 && rows <= num_cus && 2 * rows > num_cus) {
+  // Partial inputs from more than half the CUs busy up to 3 rows per CU, where
+  // the whole grid is resident at once: 2 vectors per lane and the fewest
+  // waves (measured 2-14% faster than the decode rule's shape at 256 rows x
+  // 4096 / 8192 wide, 2-8 partials, and up to 11% faster than the exact fit
+  // at 300-700 rows; at 64 rows the decode rule's shape is as fast).
+  if (key.kp > 1 && num_cus >= 1 && 2 * rows > num_cus && rows <= 3 * static_cast<int64_t>(num_cus) &&
+      tw == 0) {
     const int vec = 16 / (key.x == kBF16 ? 2 : 4);
     const int64_t w = (hidden / vec + 127) / 128;
     if (w >= 1 && w <= kMaxWavesPerRow) {
