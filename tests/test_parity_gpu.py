@@ -586,7 +586,7 @@ def test_concurrent_host_threads():
         inputs = WL.generate_rownorm(wl, seed=21)
         ref = run_rownorm(wl, inputs)
         jobs.append((wl, inputs, to_host(ref.out), to_host(ref.residual_out)))
-    _announce("concurrent host threads x4")
+    _announce("concurrent host threads x5")
     errors, msgs = [], {}
     lib = L.lib()
 
@@ -608,7 +608,31 @@ def test_concurrent_host_threads():
         except Exception as e:  # noqa: BLE001 -- reported below
             errors.append((k, repr(e)))
 
+    # a fifth thread drives the partial-input entry point
+    pwl = WL.WORKLOADS["partials_8x2048x8192"].with_rows(48)
+    pin = WL.generate_partials(pwl, seed=23)
+    pparts = [to_dev(p, "bf16") for p in pin["partials"]]
+    pres, pw = to_dev(pin["residual"], "f32"), to_dev(pin["weight"], "bf16")
+    pref = R.fused_partials_add_rmsnorm(pparts, pres, pw, pwl.eps)
+    torch.cuda.synchronize()
+    pref_out, pref_res = to_host(pref.out), to_host(pref.residual_out)
+
+    def partials_worker():
+        stream = torch.cuda.Stream()
+        try:
+            with torch.cuda.stream(stream):
+                for i in range(20):
+                    r = R.fused_partials_add_rmsnorm(pparts, pres, pw, pwl.eps)
+                    stream.synchronize()
+                    if not (np.array_equal(to_host(r.out), pref_out) and np.array_equal(to_host(r.residual_out),
+                                                                                         pref_res)):
+                        errors.append(("partials", i))
+                        return
+        except Exception as e:  # noqa: BLE001 -- reported below
+            errors.append(("partials", repr(e)))
+
     threads = [threading.Thread(target=worker, args=(k,)) for k in range(len(jobs))]
+    threads.append(threading.Thread(target=partials_worker))
     for t in threads:
         t.start()
     for t in threads:
