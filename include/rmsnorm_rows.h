@@ -235,7 +235,8 @@ rn_status rmsnorm_fwd_config(const void* x, const void* residual, const void* we
  * the partials is a float32 value (as for bf16 partials within 2^12 of one
  * another in magnitude, or zero) the float32 sum is exact and the result is
  * that of rmsnorm_fwd on the exact sum; otherwise each float32 addition
- * rounds once (error at most (num_partials - 1) * 2^-24 * sum_k |p_k|).
+ * rounds once (total error within (num_partials - 1) * 2^-24 * sum_k |p_k|,
+ * to first order).
  * num_partials == 1 is rmsnorm_fwd_ex on x = partials[0].
  * Aliasing: out may equal one of the partials (in place); residual_out may
  * equal residual; residual_out equal to a partial or to out is rejected; any
