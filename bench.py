@@ -45,8 +45,11 @@ MAIN = "prefill_16384x8192"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
+_T0 = time.monotonic()
+
+
 def log(msg: str) -> None:
-    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+    print(f"[bench +{time.monotonic() - _T0:6.1f}s] {msg}", file=sys.stderr, flush=True)
 
 
 def library_digest() -> str:
