@@ -302,12 +302,13 @@ namespace rn {
 // ---------------------------------------------------------------------------
 // Block-scaled quantization of one chunk of U consecutive elements whose
 // scale group spans GL = group / U neighbouring lanes (group = 128 for the
-// per-128 fp8 scheme, 32 for MX).  The values to quantize are v[i] * mul with
-// mul > 0; the group's amax is max|v| over the group times mul (multiplying
-// by a positive number is monotone, so this is the max of the products).
-// Writes the scaled values into y (ready for pack<OD>) and, from the group's
-// first lane, the scale (float32 amax / 448, or E8M0 byte e + 127) at index
-// gidx of the row's scale resource, and the amax when requested.
+// per-128 fp8 scheme, 32 for MX, 16 for NVFP4).  The values to quantize are
+// v[i] * mul with mul > 0; the group's amax is max|v| over the group times mul
+// (multiplying by a positive number is monotone, so this is the max of the
+// products).  Writes the scaled values into y (ready for pack<OD>) and, from
+// the group's first lane, the scale (float32 amax / 448, E8M0 byte e + 127, or
+// NVFP4's E4M3FN block-scale code) at index gidx of the row's scale resource,
+// and the amax when requested.
 // ---------------------------------------------------------------------------
 
 template <int QS>
