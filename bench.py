@@ -524,6 +524,20 @@ def act_metrics(steps: int, warmup: int, out_dtype: str = "bf16", scale_scheme: 
             "buffer_sets": sets, "warmup": warmup, "launch_us": spread}
 
 
+def host_cpu() -> dict:
+    """The host's CPU model (from /proc/cpuinfo) and its logical CPU count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "logical_cpus": os.cpu_count()}
+
+
 def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
     """The oracle as it stands, timed on a bounded sample of the workload's rows."""
     import numpy as np
@@ -552,7 +566,7 @@ def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
             break
     dt = time.perf_counter() - t0
     b = rownorm_bytes(wl, rows=done_rows)
-    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle", "host": host_cpu(),
             "sample": f"{done_rows} rows x {wl.hidden} of the {wl.rows}-row workload "
                       f"({chunk}-row batches, decode + residual add + norm + output rounding, float64 numpy, "
                       f"one thread), {dt:.1f} s"}
@@ -595,7 +609,7 @@ def cpu_baseline_parallel(wl, budget_s: float = 8.0, max_procs: int = 8) -> dict
         parts = list(ex.map(_oracle_worker, [(wl.name, 64 * i, budget_s) for i in range(n)]))
     rate = sum(rownorm_bytes(wl, rows=r) / t for r, t in parts)
     rows = sum(r for r, _ in parts)
-    return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": n, "kind": "oracle",
+    return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": n, "kind": "oracle", "host": host_cpu(),
             "sample": f"{rows} rows x {wl.hidden} in {n} processes (each its own 64-row batch, float64 numpy, "
                       f"one thread each), {budget_s:.0f} s"}
 
