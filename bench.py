@@ -426,7 +426,8 @@ class PartialsCall:
         self.i = (self.i + 1) % len(self.sets)
         wl = self.wl
         st = self.L.rmsnorm_fwd_partials(ptrs, wl.num_partials, res.data_ptr(), self.w.data_ptr(), out.data_ptr(),
-                                         ro.data_ptr(), None, None, wl.rows, wl.hidden, wl.eps, self.flags, stream)
+                                         ro.data_ptr(), None, None, None, wl.rows, wl.hidden, wl.eps, self.flags,
+                                         stream)
         if st != 0:
             from residual_add_rmsnorm_rows_amd._lib import check
             check(st)

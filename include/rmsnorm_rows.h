@@ -221,11 +221,10 @@ rn_status rmsnorm_fwd_config(const void* x, const void* residual, const void* we
  *   partials      HOST array of num_partials device pointers, each [rows, hidden] of
  *                 dtype flags.x, 16-byte aligned, none NULL (when rows > 0)      (read)
  *   num_partials  1..8
- *   residual, weight, out, residual_out, out_scale, out_amax, rows, eps: as rmsnorm_fwd_ex;
+ *   residual, weight, out, residual_out, out_scale, out_amax, tensor_scale, rows, eps,
+ *   flags: as rmsnorm_fwd_ex (every output type and scale granularity);
  *   hidden        as rmsnorm_fwd, and at most 2048 lane vectors (16384 bf16 / 8192 f32
  *                 elements) when num_partials > 1
- *   flags         as rmsnorm_fwd, with out bf16, f32, or fp8 with RN_SCALE_ROW
- *                 (other scale granularities and fp4 return RN_ERR_UNSUPPORTED)
  *
  * Reading (not on the pages): x = ((p_0 + p_1) + p_2) + ... is summed in
  * float32 in slot order, without rounding to the x dtype, then
@@ -244,15 +243,15 @@ rn_status rmsnorm_fwd_config(const void* x, const void* residual, const void* we
  */
 rn_status rmsnorm_fwd_partials(const void* const* partials, int32_t num_partials, const void* residual,
                                const void* weight, void* out, void* residual_out, void* out_scale,
-                               float* out_amax, int64_t rows, int64_t hidden, float eps, uint32_t flags,
-                               void* stream);
+                               float* out_amax, const float* tensor_scale, int64_t rows, int64_t hidden, float eps,
+                               uint32_t flags, void* stream);
 
 /* As rmsnorm_fwd_partials with an explicit launch configuration (the rules of
  * rmsnorm_fwd_config; vecs_per_lane at most 2 when num_partials > 1). */
 rn_status rmsnorm_fwd_partials_config(const void* const* partials, int32_t num_partials, const void* residual,
                                       const void* weight, void* out, void* residual_out, void* out_scale,
-                                      float* out_amax, int64_t rows, int64_t hidden, float eps, uint32_t flags,
-                                      const rn_launch_config* cfg, void* stream);
+                                      float* out_amax, const float* tensor_scale, int64_t rows, int64_t hidden,
+                                      float eps, uint32_t flags, const rn_launch_config* cfg, void* stream);
 
 /*
  * Per-head RMSNorm of Q and K ("CuTeDSL at Perplexity", section "QK Norm").

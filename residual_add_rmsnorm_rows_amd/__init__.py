@@ -187,14 +187,16 @@ def fused_partials_add_rmsnorm(partials: Sequence[torch.Tensor], residual: Optio
                                weight: torch.Tensor, eps: float, *, weight_plus_one: bool = False,
                                out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
                                residual_out: Optional[torch.Tensor] = None, return_amax: bool = False,
+                               scale_scheme: str = "row", tensor_scale=None,
                                config: Optional[LaunchConfig] = None) -> NormOutput:
     """``fused_add_rmsnorm`` with ``x = partials[0] + partials[1] + ...``, summed
     in the kernel in float32 (slot order) without an intermediate rounding.
 
     ``partials`` holds 1..8 tensors of one shape and dtype (bf16 or f32): the
     partial outputs of a row-parallel projection, or the branch outputs of a
-    parallel residual block.  Outputs are bf16, f32, or fp8 e4m3fn with one
-    scale per row.  ``out`` may be one of the partials (in place).
+    parallel residual block.  Outputs, scale schemes and ``tensor_scale`` are
+    those of ``fused_add_rmsnorm``.  ``out`` may be one of the partials (in
+    place).
     """
     parts = list(partials)
     if not 1 <= len(parts) <= _lib.MAX_PARTIALS:
@@ -205,17 +207,17 @@ def fused_partials_add_rmsnorm(partials: Sequence[torch.Tensor], residual: Optio
         if p.shape != x.shape or p.dtype != x.dtype:
             raise ValueError(f"partials[{i}] has shape {tuple(p.shape)} / {p.dtype}, "
                              f"partials[0] has {tuple(x.shape)} / {x.dtype}")
-    rows, H, out, residual_out, scale, amax, _, flags = _rows_setup(
-        x, residual, weight, weight_plus_one, out_dtype, out, residual_out, return_amax, "row", None)
+    rows, H, out, residual_out, scale, amax, ts, flags = _rows_setup(
+        x, residual, weight, weight_plus_one, out_dtype, out, residual_out, return_amax, scale_scheme, tensor_scale)
     ptrs = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
     L = lib()
     if config is not None:
         st = L.rmsnorm_fwd_partials_config(ptrs, len(parts), _p(residual), _p(weight), _p(out), _p(residual_out),
-                                           _p(scale), _p(amax), rows, H, eps, flags, ctypes.byref(config),
+                                           _p(scale), _p(amax), _p(ts), rows, H, eps, flags, ctypes.byref(config),
                                            _stream(x.device))
     else:
         st = L.rmsnorm_fwd_partials(ptrs, len(parts), _p(residual), _p(weight), _p(out), _p(residual_out),
-                                    _p(scale), _p(amax), rows, H, eps, flags, _stream(x.device))
+                                    _p(scale), _p(amax), _p(ts), rows, H, eps, flags, _stream(x.device))
     check(st)
     return NormOutput(out, residual_out, scale, amax)
 
@@ -303,10 +305,10 @@ def query_config(rows: int, hidden: int, *, x_dtype: str = "bf16", res_dtype: Op
 
 def query_partials_config(rows: int, hidden: int, num_partials: int, *, x_dtype: str = "bf16",
                           res_dtype: Optional[str] = None, w_dtype: str = "bf16", out_dtype: str = "bf16",
-                          weight_plus_one: bool = False, num_cus: int = 256) -> dict:
+                          weight_plus_one: bool = False, scale_scheme: str = "row", num_cus: int = 256) -> dict:
     """The launch configuration ``fused_partials_add_rmsnorm`` would use."""
     cfg = LaunchConfig()
-    flags = make_flags(x_dtype, res_dtype, w_dtype, out_dtype, weight_plus_one)
+    flags = make_flags(x_dtype, res_dtype, w_dtype, out_dtype, weight_plus_one, scale_scheme)
     check(lib().rmsnorm_partials_query_config(rows, hidden, num_partials, flags, int(res_dtype is not None),
                                               num_cus, ctypes.byref(cfg)))
     return cfg.as_dict()

@@ -95,10 +95,10 @@ _SIGNATURES = {
                    ctypes.c_int),
     "qknorm_fwd_config": ([_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i64, _f32, _u32,
                            ctypes.POINTER(LaunchConfig), _vp], ctypes.c_int),
-    "rmsnorm_fwd_partials": ([ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _u32, _vp],
-                             ctypes.c_int),
-    "rmsnorm_fwd_partials_config": ([ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _u32,
-                                    ctypes.POINTER(LaunchConfig), _vp], ctypes.c_int),
+    "rmsnorm_fwd_partials": ([ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _u32,
+                              _vp], ctypes.c_int),
+    "rmsnorm_fwd_partials_config": ([ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32,
+                                     _u32, ctypes.POINTER(LaunchConfig), _vp], ctypes.c_int),
     "rmsnorm_query_config": ([_i64, _i64, _u32, _i32, _i32, ctypes.POINTER(LaunchConfig)], ctypes.c_int),
     "rmsnorm_partials_query_config": ([_i64, _i64, _i32, _u32, _i32, _i32, ctypes.POINTER(LaunchConfig)],
                                       ctypes.c_int),

@@ -78,12 +78,10 @@ rn_status launch(const void* fn, int64_t grid, int block, void* args, void* stre
 }
 
 // Partial-input form (rmsnorm_fwd_partials*): the sizes and flags checks of
-// the rows kernel, then those of the partials (count, supported outputs).
+// the rows kernel, then those of the partials (count, row length).
 rn_status check_parts_key(int32_t num_parts, int64_t hidden, RowKey* key) {
   if (num_parts < 1 || num_parts > kMaxParts)
     return fail(RN_ERR_INVALID_ARG, "num_partials must be in 1..%d (got %d)", kMaxParts, num_parts);
-  if (key->qs != kQRow || key->out == kFP4)
-    return fail(RN_ERR_UNSUPPORTED, "partial inputs take bf16, f32 or fp8 (RN_SCALE_ROW) outputs");
   const int64_t vec = key->x == kBF16 ? 8 : 4;
   const int64_t cap = static_cast<int64_t>(64) * kMaxWavesPerRow * kMaxPartsVecsPerLane * vec;
   if (num_parts > 1 && hidden > cap)
@@ -302,22 +300,22 @@ rn_status rmsnorm_fwd_config(const void* x, const void* residual, const void* we
 
 rn_status rmsnorm_fwd_partials(const void* const* partials, int32_t num_partials, const void* residual,
                                const void* weight, void* out, void* residual_out, void* out_scale,
-                               float* out_amax, int64_t rows, int64_t hidden, float eps, uint32_t flags,
-                               void* stream) {
+                               float* out_amax, const float* tensor_scale, int64_t rows, int64_t hidden, float eps,
+                               uint32_t flags, void* stream) {
   return rows_entry(true, nullptr, partials, num_partials, residual, weight, out, residual_out, out_scale, out_amax,
-                    nullptr, rows, hidden, eps, flags, nullptr, stream);
+                    tensor_scale, rows, hidden, eps, flags, nullptr, stream);
 }
 
 rn_status rmsnorm_fwd_partials_config(const void* const* partials, int32_t num_partials, const void* residual,
                                       const void* weight, void* out, void* residual_out, void* out_scale,
-                                      float* out_amax, int64_t rows, int64_t hidden, float eps, uint32_t flags,
-                                      const rn_launch_config* cfg, void* stream) {
+                                      float* out_amax, const float* tensor_scale, int64_t rows, int64_t hidden,
+                                      float eps, uint32_t flags, const rn_launch_config* cfg, void* stream) {
   if (cfg == nullptr) {
     clear_error();
     return fail(RN_ERR_INVALID_ARG, "launch config is NULL");
   }
   return rows_entry(true, nullptr, partials, num_partials, residual, weight, out, residual_out, out_scale, out_amax,
-                    nullptr, rows, hidden, eps, flags, cfg, stream);
+                    tensor_scale, rows, hidden, eps, flags, cfg, stream);
 }
 
 rn_status qknorm_fwd(const void* q, const void* k, const void* q_weight, const void* k_weight,

@@ -76,11 +76,13 @@ constexpr int max_of(int a, int b) { return a > b ? a : b; }
 // SIMD in VGPRs but, left alone, takes more SGPRs than 8 waves allow (eight
 // buffer resources next to the kernel arguments); asking for 8 waves moves
 // the excess into VGPR lanes, which keeps two 16-wave workgroups per CU.
-constexpr int min_waves_per_eu(int nv, int kp) { return kp == 8 && nv == 1 ? 8 : 1; }
+// Not for the block-scaled outputs, whose extra registers would then spill
+// to scratch memory.
+constexpr int min_waves_per_eu(int nv, int kp, int qs) { return kp == 8 && nv == 1 && qs == kQRow ? 8 : 1; }
 
 template <int XD, int RD, int WD, int OD, int QS, int BIAS, int NV, int KP>
-__global__ __launch_bounds__(max_threads_for_nv(NV)) __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(NV, KP))))
-void rows_kernel(const RowArgs a) {
+__global__ __launch_bounds__(max_threads_for_nv(NV))
+__attribute__((amdgpu_waves_per_eu(min_waves_per_eu(NV, KP, QS)))) void rows_kernel(const RowArgs a) {
   constexpr int XB = storage_bits(XD) / 8;
   constexpr int VEC = 16 / XB;
   constexpr bool HAS_RES = RD != kNone;
@@ -315,11 +317,9 @@ const void* pick_nv(int nv, int kp) {
       default: return nullptr;
     }
   }
-  // partial inputs: bf16 / f32 outputs and fp8 with one scale per row
-  if constexpr (QS == kQRow) {
-    if (nv == 1) return pick_kp<XD, RD, WD, OD, QS, BIAS, 1>(kp);
-    if (nv == 2) return pick_kp<XD, RD, WD, OD, QS, BIAS, 2>(kp);
-  }
+  // partial inputs: every output type and scale scheme, 1 or 2 vectors per lane
+  if (nv == 1) return pick_kp<XD, RD, WD, OD, QS, BIAS, 1>(kp);
+  if (nv == 2) return pick_kp<XD, RD, WD, OD, QS, BIAS, 2>(kp);
   return nullptr;
 }
 
@@ -336,8 +336,8 @@ const void* pick_weight(const RowKey& k) {
 
 // Built combinations for this (x, out, scale scheme): residual none, f32, or
 // the x dtype; weight bf16 or f32; both weight forms; 1, 2, 4 or 8 vectors
-// per lane; with one scale per row (or none), also the partial-input
-// variants: 2, 4 or 8 slots at 1 or 2 vectors per lane.
+// per lane; and the partial-input variants: 2, 4 or 8 slots at 1 or 2
+// vectors per lane.
 const void* RN_CAT(pick_row_kernel_, RN_TU_NAME)(const RowKey& k) {
   if (k.x != RN_TU_X || k.out != RN_TU_OUT || k.qs != RN_TU_QS) return nullptr;
   switch (k.res) {

@@ -48,10 +48,12 @@ int main(void) {
   const void* parts[3] = {p, p, (const void*)(uintptr_t)0x30008};
   EXPECT(rmsnorm_partials_query_config(2048, 8192, 8, flags, 1, 256, &cfg) == RN_OK);
   EXPECT(cfg.vecs_per_lane <= 2 && (int64_t)64 * cfg.waves_per_row * cfg.vecs_per_lane * cfg.vec >= 8192);
-  EXPECT(rmsnorm_fwd_partials(parts, 3, p, p, q, (void*)(uintptr_t)0x40000, NULL, NULL, 4, 1024, 1e-6f, flags,
-                              NULL) == RN_ERR_MISALIGNED);
-  EXPECT(rmsnorm_fwd_partials(parts, 9, p, p, q, q, NULL, NULL, 4, 1024, 1e-6f, flags, NULL) == RN_ERR_INVALID_ARG);
-  EXPECT(rmsnorm_fwd_partials(NULL, 2, NULL, NULL, NULL, NULL, NULL, NULL, 0, 1024, 1e-6f, flags, NULL) == RN_OK);
+  EXPECT(rmsnorm_fwd_partials(parts, 3, p, p, q, (void*)(uintptr_t)0x40000, NULL, NULL, NULL, 4, 1024, 1e-6f,
+                              flags, NULL) == RN_ERR_MISALIGNED);
+  EXPECT(rmsnorm_fwd_partials(parts, 9, p, p, q, q, NULL, NULL, NULL, 4, 1024, 1e-6f, flags, NULL) ==
+         RN_ERR_INVALID_ARG);
+  EXPECT(rmsnorm_fwd_partials(NULL, 2, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, 1024, 1e-6f, flags, NULL) ==
+         RN_OK);
 
   if (failures == 0) printf("c abi check: ok\n");
   return failures == 0 ? 0 : 1;

@@ -45,7 +45,7 @@ int main(void) {
     if (st == RN_OK && ((int64_t)64 * cfg.waves_per_row * cfg.vecs_per_lane * cfg.vec < hidden ||
                         (np > 1 && cfg.vecs_per_lane > 2))) { printf("partials cfg bug\n"); return 1; }
     rmsnorm_fwd_partials_config(np > 9 || np < 0 ? NULL : parts, np, NULL, (void*)0x1000, (void*)0x2000, NULL, NULL,
-                                NULL, rows, hidden, 1e-6f, flags, &c, NULL);
+                                NULL, NULL, rows, hidden, 1e-6f, flags, &c, NULL);
   }
   printf("fuzz ok: %ld ok, %ld invalid, %ld unsupported, %ld misaligned, %ld hip\n", counts[0], counts[1], counts[2], counts[3], counts[4]);
   return 0;

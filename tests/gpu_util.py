@@ -165,7 +165,7 @@ def judge_y(y: np.ndarray, out_dtype: str, out: np.ndarray, scale=None, amax=Non
 
 def judge_partials_rows(inputs: dict, x_dtype: str, res_dtype, w_dtype: str, out_dtype: str, eps: float,
                         weight_plus_one: bool, out: np.ndarray, res_out, scale=None, amax=None,
-                        exact_sum: bool = True, ref=None) -> dict:
+                        exact_sum: bool = True, ref=None, scale_scheme: str = "row", tensor_scale=None) -> dict:
     """Compare the outputs of some rows of a partial-input call with the oracle.
 
     ``inputs`` holds the same rows of every partial (``partials``) and of the
@@ -189,7 +189,7 @@ def judge_partials_rows(inputs: dict, x_dtype: str, res_dtype, w_dtype: str, out
             same = np.array_equal(np.asarray(res_out).view(np.uint8), np.asarray(expect).view(np.uint8))
             rep["res_out_bit_exact"] = same
             rep["ok"] &= same
-        rep.update(judge_y(ref["y"], out_dtype, out, scale, amax))
+        rep.update(judge_y(ref["y"], out_dtype, out, scale, amax, scale_scheme, tensor_scale))
         rep["ok"] = rep["ok"] and rep.pop("y_ok")
         return rep
     b = partials_bounds(parts, RES, res_dtype, W, bias, eps, ref)

@@ -333,9 +333,9 @@ P0, P1, P2 = FAKE + 0x10000, FAKE + 0x20000, FAKE + 0x30000
 
 
 def _pfwd(lib, parts=(P0, P1), n=None, res=FAKE, w=FAKE, out=FAKE + 0x1000, res_out=FAKE + 0x2000, scale=None,
-          amax=None, rows=4, hidden=1024, eps=1e-6, flags=BF):
+          amax=None, ts=None, rows=4, hidden=1024, eps=1e-6, flags=BF):
     arr = None if parts is None else _parts_ptrs(*parts)
-    return lib.rmsnorm_fwd_partials(arr, len(parts or ()) if n is None else n, res, w, out, res_out, scale, amax,
+    return lib.rmsnorm_fwd_partials(arr, len(parts or ()) if n is None else n, res, w, out, res_out, scale, amax, ts,
                                     rows, hidden, eps, flags, None)
 
 
@@ -351,8 +351,9 @@ def _pfwd(lib, parts=(P0, P1), n=None, res=FAKE, w=FAKE, out=FAKE + 0x1000, res_
     (dict(res=None), L.RN_ERR_INVALID_ARG),
     (dict(w=None), L.RN_ERR_INVALID_ARG),
     (dict(hidden=16384 + 8), L.RN_ERR_UNSUPPORTED),  # above 2048 lane vectors with more than one partial
-    (dict(flags=_qflags("fp8_e4m3fn", "group128"), scale=FAKE + 0x3000), L.RN_ERR_UNSUPPORTED),
-    (dict(flags=_qflags("fp4_e2m1", "mx32"), scale=FAKE + 0x3000), L.RN_ERR_UNSUPPORTED),
+    (dict(flags=_qflags("fp8_e4m3fn", "group128"), hidden=1000, scale=FAKE + 0x3000), L.RN_ERR_UNSUPPORTED),
+    (dict(flags=_qflags("fp4_e2m1", "nv16"), scale=FAKE + 0x3000), L.RN_ERR_INVALID_ARG),  # NVFP4 without tensor_scale
+    (dict(flags=_qflags("fp4_e2m1", "mx32"), scale=FAKE + 0x3000, ts=FAKE + 0x4000), L.RN_ERR_INVALID_ARG),
     (dict(flags=L.make_flags("bf16", "bf16", "bf16", "fp8_e4m3fn", False)), L.RN_ERR_INVALID_ARG),  # no scale
     (dict(eps=float("nan")), L.RN_ERR_INVALID_ARG),
 ])
@@ -362,10 +363,10 @@ def test_partials_reject_before_any_hip_call(lib, kw, status):
 
 
 def test_partials_rows_zero_is_a_noop(lib):
-    assert lib.rmsnorm_fwd_partials(None, 3, None, None, None, None, None, None, 0, 1024, 1e-6, L.make_flags(
+    assert lib.rmsnorm_fwd_partials(None, 3, None, None, None, None, None, None, None, 0, 1024, 1e-6, L.make_flags(
         "bf16", None, "bf16", "bf16", False), None) == L.RN_OK
     # the count is still checked
-    assert lib.rmsnorm_fwd_partials(None, 0, None, None, None, None, None, None, 0, 1024, 1e-6, BF, None) \
+    assert lib.rmsnorm_fwd_partials(None, 0, None, None, None, None, None, None, None, 0, 1024, 1e-6, BF, None) \
         == L.RN_ERR_INVALID_ARG
 
 
@@ -402,9 +403,9 @@ def test_partials_explicit_config_is_checked(lib):
     cfg = L.LaunchConfig()
     cfg.kernel, cfg.waves_per_row, cfg.vecs_per_lane, cfg.grid = 0, 2, 4, 4  # 4 vectors per lane: not built
     arr = _parts_ptrs(P0, P1, P2)
-    st = lib.rmsnorm_fwd_partials_config(arr, 3, FAKE, FAKE, FAKE + 0x1000, FAKE + 0x2000, None, None, 4, 1024,
-                                         1e-6, BF, ctypes.byref(cfg), None)
+    st = lib.rmsnorm_fwd_partials_config(arr, 3, FAKE, FAKE, FAKE + 0x1000, FAKE + 0x2000, None, None, None, 4,
+                                         1024, 1e-6, BF, ctypes.byref(cfg), None)
     assert st == L.RN_ERR_INVALID_ARG
-    st = lib.rmsnorm_fwd_partials_config(arr, 3, FAKE, FAKE, FAKE + 0x1000, FAKE + 0x2000, None, None, 4, 1024,
-                                         1e-6, BF, None, None)
+    st = lib.rmsnorm_fwd_partials_config(arr, 3, FAKE, FAKE, FAKE + 0x1000, FAKE + 0x2000, None, None, None, 4,
+                                         1024, 1e-6, BF, None, None)
     assert st == L.RN_ERR_INVALID_ARG

@@ -188,3 +188,52 @@ def test_zero_rows_and_all_zero_partials():
     empty = [torch.empty(0, 1024, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
     e = R.fused_partials_add_rmsnorm(empty, None, to_dev(inp["weight"], "bf16"), 1e-6)
     assert e.out.shape == (0, 1024)
+
+
+BLOCK_SCHEMES = [("fp8_e4m3fn", "group128"), ("fp8_e4m3fn", "mx32"), ("fp4_e2m1", "mx32"), ("fp4_e2m1", "nv16")]
+
+
+@pytest.mark.parametrize("k", [2, 3, 8])
+@pytest.mark.parametrize("out,scheme", BLOCK_SCHEMES)
+@pytest.mark.parametrize("x,res,rows,hidden", [("bf16", "f32", 37, 1024), ("bf16", "bf16", 5, 4096),
+                                               ("f32", "f32", 9, 2048)])
+def test_block_scaled_outputs(k, out, scheme, x, res, rows, hidden):
+    """Partial inputs with every block-scaled output (per-128 fp8, MXFP8, MXFP4, NVFP4)."""
+    from tests.gpu_util import nvfp4_tensor_scale
+
+    wl = _wl(rows, hidden, k, x, res, "bf16", out)
+    _announce(f"partials k={k} {x}/{res} -> {out}/{scheme} {rows}x{hidden}")
+    inp = WL.generate_partials(wl, seed=31 + k)
+    ref = oracle_ref(wl, inp)
+    ts = nvfp4_tensor_scale(ref["y"]) if scheme == "nv16" else None
+    parts = [to_dev(p, x) for p in inp["partials"]]
+    r = R.fused_partials_add_rmsnorm(parts, to_dev(inp["residual"], res), to_dev(inp["weight"], "bf16"), wl.eps,
+                                     out_dtype=TORCH_DTYPES[out], scale_scheme=scheme, tensor_scale=ts,
+                                     return_amax=True)
+    torch.cuda.synchronize()
+    rep = judge_partials_rows(inp, x, res, "bf16", out, wl.eps, False, to_host(r.out), to_host(r.residual_out),
+                              to_host(r.scale), to_host(r.amax), ref=ref, scale_scheme=scheme, tensor_scale=ts)
+    assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("out,scheme", BLOCK_SCHEMES)
+def test_block_scaled_every_launch_variant(out, scheme):
+    from tests.gpu_util import nvfp4_tensor_scale
+
+    wl = _wl(21, 2048, 8, "bf16", "f32", "bf16", out)
+    inp = WL.generate_partials(wl, seed=41)
+    ref = oracle_ref(wl, inp)
+    ts = nvfp4_tensor_scale(ref["y"]) if scheme == "nv16" else None
+    parts = [to_dev(p, "bf16") for p in inp["partials"]]
+    res, w = to_dev(inp["residual"], "f32"), to_dev(inp["weight"], "bf16")
+    for W, NV in _variants(2048, 8):
+        cfg = L.LaunchConfig()
+        cfg.kernel, cfg.waves_per_row, cfg.vecs_per_lane, cfg.grid = 0, W, NV, 21
+        _announce(f"partials block variant {out}/{scheme} W={W} NV={NV}")
+        r = R.fused_partials_add_rmsnorm(parts, res, w, wl.eps, out_dtype=TORCH_DTYPES[out], scale_scheme=scheme,
+                                         tensor_scale=ts, return_amax=True, config=cfg)
+        torch.cuda.synchronize()
+        rep = judge_partials_rows(inp, "bf16", "f32", "bf16", out, wl.eps, False, to_host(r.out),
+                                  to_host(r.residual_out), to_host(r.scale), to_host(r.amax), ref=ref,
+                                  scale_scheme=scheme, tensor_scale=ts)
+        assert rep["ok"], (W, NV, rep)

@@ -181,14 +181,16 @@ def _partials_cases(n=32, seed=77):
         x = ["bf16", "f32"][rng.integers(2)]
         res = [None, x, "f32"][rng.integers(3)]
         w = ["bf16", "f32"][rng.integers(2)]
-        out = ["bf16", "f32", "fp8_e4m3fn"][rng.integers(3)]
+        out, scheme = OUTS[rng.integers(len(OUTS))]
         vec = 8 if x == "bf16" else 4
+        g = int(np.lcm(vec, GRANULE[scheme]))
         k = int(rng.integers(1, 9))
         hmax = (16384 if x == "bf16" else 8192) if k > 1 else 4096
-        hidden = vec * int(rng.integers(1, min(hmax, 6144) // vec + 1))
+        hidden = g * int(rng.integers(1, min(hmax, 6144) // g + 1))
         rows = int(rng.integers(1, 40))
-        exact = bool(rng.random() < 0.75) or out == "fp8_e4m3fn"
-        cases.append((i, x, res, w, out, bool(rng.integers(2)), k, hidden, rows, exact, int(rng.integers(1 << 30))))
+        exact = bool(rng.random() < 0.75) or out not in ("bf16", "f32")
+        cases.append((i, x, res, w, out, scheme, bool(rng.integers(2)), k, hidden, rows, exact,
+                      int(rng.integers(1 << 30))))
     return cases
 
 
@@ -198,7 +200,7 @@ def test_random_partials(case):
     general ones against the float32 summation bound (bf16 / f32 outputs)."""
     from tests.gpu_util import judge_partials_rows
 
-    i, x, res, w, out, b, k, hidden, rows, exact, seed = case
+    i, x, res, w, out, scheme, b, k, hidden, rows, exact, seed = case
     rng = np.random.default_rng(seed)
     wl = WL.PartialsWorkload(name="rand", rows=rows, hidden=hidden, num_partials=k, x_dtype=x, res_dtype=res,
                              w_dtype=w, out_dtype=out, part_dist=WL.Dist(0, float(rng.uniform(0.2, 2.0))),
@@ -217,16 +219,25 @@ def test_random_partials(case):
         cfg.kernel, cfg.waves_per_row, cfg.vecs_per_lane = L.RN_KERNEL_ROWS, W_, NV_
         cfg.grid = int(rng.integers(1, rows + 1))
     cfg_txt = None if cfg is None else (cfg.waves_per_row, cfg.vecs_per_lane, cfg.grid)
-    _announce(f"random partials #{i}: k={k} x={x} res={res} w={w} out={out} plus_one={b} rows={rows} H={hidden} "
-              f"exact={exact} cfg={cfg_txt}")
+    _announce(f"random partials #{i}: k={k} x={x} res={res} w={w} out={out}/{scheme} plus_one={b} rows={rows} "
+              f"H={hidden} exact={exact} cfg={cfg_txt}")
     inputs = WL.generate_partials(wl, seed=seed)
+    ts = None
+    if scheme == "nv16":
+        Y = O.rmsnorm_rows_partials([O.decode(p, x) for p in inputs["partials"]], O.decode(inputs["weight"], w), wl.eps,
+                                    1.0 if b else 0.0,
+                                    residual=None if res is None else O.decode(inputs["residual"], res),
+                                    res_dtype=res)["y"]
+        ts = nvfp4_tensor_scale(Y) * float(2.0 ** rng.integers(-3, 4))
     parts = [to_dev(p, x) for p in inputs["partials"]]
     RES = None if res is None else to_dev(inputs["residual"], res)
+    quant = out in ("fp8_e4m3fn", "fp4_e2m1")
     r = R.fused_partials_add_rmsnorm(parts, RES, to_dev(inputs["weight"], w), wl.eps, weight_plus_one=b,
-                                     out_dtype=TORCH_DTYPES[out], return_amax=out == "fp8_e4m3fn", config=cfg)
+                                     out_dtype=TORCH_DTYPES[out], return_amax=quant, scale_scheme=scheme,
+                                     tensor_scale=ts, config=cfg)
     torch.cuda.synchronize()
     rep = judge_partials_rows(inputs, x, res, w, out, wl.eps, b, to_host(r.out),
                               None if r.residual_out is None else to_host(r.residual_out),
                               None if r.scale is None else to_host(r.scale), None if r.amax is None else to_host(r.amax),
-                              exact_sum=exact)
+                              exact_sum=exact, scale_scheme=scheme, tensor_scale=ts)
     assert rep["ok"], rep
