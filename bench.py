@@ -386,19 +386,22 @@ def qknorm_metrics(steps: int, warmup: int, sets: int = 8) -> dict:
             "buffer_sets": sets, "launch_us": spread}
 
 
-def partials_bytes(wl) -> int:
-    """Algorithmic bytes: every partial and the residual read once; out and residual_out written once; weight once."""
-    size = {"bf16": 2, "f32": 4}
+def partials_bytes(wl, scale_scheme: str = "row") -> int:
+    """Algorithmic bytes: every partial and the residual read once; out (and its scales) and residual_out
+    written once; weight once."""
+    size = {"bf16": 2, "f32": 4, "fp8_e4m3fn": 1, "fp4_e2m1": 0.5}
     per_row = wl.hidden * (wl.num_partials * size[wl.x_dtype] + size[wl.out_dtype])
     if wl.res_dtype is not None:
         per_row += 2 * wl.hidden * size[wl.res_dtype]
-    return wl.rows * per_row + wl.hidden * size[wl.w_dtype]
+    if wl.out_dtype in ("fp8_e4m3fn", "fp4_e2m1"):
+        per_row += SCALE_BYTES[scale_scheme](wl.hidden)
+    return int(wl.rows * per_row + wl.hidden * size[wl.w_dtype])
 
 
 class PartialsCall:
     """Device buffers of one partial-input workload and a raw C-ABI call over them."""
 
-    def __init__(self, wl, sets: int = 1):
+    def __init__(self, wl, sets: int = 1, scale_scheme: str = "row", tensor_scale=None):
         import torch
 
         import workloads as WL
@@ -410,40 +413,55 @@ class PartialsCall:
         parts0 = [to_dev(p, wl.x_dtype) for p in inp["partials"]]
         res0 = to_dev(inp["residual"], wl.res_dtype)
         self.w = to_dev(inp["weight"], wl.w_dtype)
+        quant = wl.out_dtype in ("fp8_e4m3fn", "fp4_e2m1")
+        out_cols = wl.hidden // 2 if wl.out_dtype == "fp4_e2m1" else wl.hidden
         self.sets = []
         for i in range(sets):
             parts = parts0 if i == 0 else [p.clone() for p in parts0]
             res = res0 if i == 0 else res0.clone()
             ptrs = (ctypes.c_void_p * len(parts))(*[p.data_ptr() for p in parts])
-            out = torch.empty(wl.rows, wl.hidden, dtype=TORCH_DTYPES[wl.out_dtype], device="cuda")
-            self.sets.append((parts, ptrs, res, torch.empty_like(res), out))
+            out = torch.empty(wl.rows, out_cols, dtype=TORCH_DTYPES[wl.out_dtype], device="cuda")
+            sc = (torch.empty(wl.rows, SCALE_BYTES[scale_scheme](wl.hidden), dtype=torch.uint8, device="cuda")
+                  if quant else None)
+            self.sets.append((parts, ptrs, res, torch.empty_like(res), out, sc))
+        self.ts = (torch.tensor([tensor_scale], dtype=torch.float32, device="cuda")
+                   if scale_scheme == "nv16" else None)
         self.L = L.lib()
-        self.flags = L.make_flags(wl.x_dtype, wl.res_dtype, wl.w_dtype, wl.out_dtype, wl.weight_plus_one)
+        self.flags = L.make_flags(wl.x_dtype, wl.res_dtype, wl.w_dtype, wl.out_dtype, wl.weight_plus_one,
+                                  scale_scheme)
         self.i = 0
 
     def __call__(self, stream: int) -> None:
-        _, ptrs, res, ro, out = self.sets[self.i]
+        _, ptrs, res, ro, out, sc = self.sets[self.i]
         self.i = (self.i + 1) % len(self.sets)
         wl = self.wl
         st = self.L.rmsnorm_fwd_partials(ptrs, wl.num_partials, res.data_ptr(), self.w.data_ptr(), out.data_ptr(),
-                                         ro.data_ptr(), None, None, None, wl.rows, wl.hidden, wl.eps, self.flags,
-                                         stream)
+                                         ro.data_ptr(), None if sc is None else sc.data_ptr(), None,
+                                         None if self.ts is None else self.ts.data_ptr(), wl.rows, wl.hidden, wl.eps,
+                                         self.flags, stream)
         if st != 0:
             from residual_add_rmsnorm_rows_amd._lib import check
             check(st)
 
 
-def partials_metrics(name: str, steps: int, warmup: int, sets: int = 2) -> dict:
+def partials_metrics(name: str, steps: int, warmup: int, sets: int = 2, out_dtype=None,
+                     scale_scheme: str = "row") -> dict:
+    from dataclasses import replace
+
     import workloads as WL
 
     wl = WL.WORKLOADS[name]
-    call = PartialsCall(wl, sets)
+    desc = wl.description
+    if out_dtype is not None:
+        wl = replace(wl, out_dtype=out_dtype)
+        desc = desc.replace("bf16 out", f"{QUANT_TEXT[out_dtype]} out with {SCHEME_TEXT[scale_scheme]}")
+    call = PartialsCall(wl, sets, scale_scheme)
     ms = time_stream_loop(call, steps, warmup)
     spread = launch_percentiles(call)
-    b = partials_bytes(wl)
-    return {"workload": wl.description, "us_per_call": round(ms * 1000, 3), "algorithmic_bytes": b,
-            "GBps": round(b / (ms * 1e-3) / 1e9, 1), "frac_of_peak": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "buffer_sets": sets, "launch_us": spread}
+    b = partials_bytes(wl, scale_scheme)
+    return {"workload": desc, "out": wl.out_dtype, "scale_scheme": scale_scheme, "us_per_call": round(ms * 1000, 3),
+            "algorithmic_bytes": b, "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "buffer_sets": sets, "launch_us": spread}
 
 
 def partials_decode_metrics(name: str) -> dict:
@@ -755,6 +773,8 @@ def main() -> int:
                                                         out_dtype="fp4_e2m1", scale_scheme="nv16")
         log("partials_8x2048x8192")
         sec["partials_8x2048x8192"] = partials_metrics("partials_8x2048x8192", args.steps * 2, args.warmup)
+        sec["partials_8x2048x8192_mxfp4"] = partials_metrics("partials_8x2048x8192", args.steps * 2, args.warmup,
+                                                             out_dtype="fp4_e2m1", scale_scheme="mx32")
         if not args.no_decode:
             log("partials_decode_8x64x8192")
             sec["partials_decode_8x64x8192"] = partials_decode_metrics("partials_decode_8x64x8192")

@@ -30,6 +30,9 @@ def test_algorithmic_bytes_of_the_workloads():
     # 8 partials of 2048 x 8192 bf16, f32 residual in and out, bf16 out, bf16 weight
     p = WL.WORKLOADS["partials_8x2048x8192"]
     assert bench.partials_bytes(p) == 2048 * 8192 * (8 * 2 + 4 + 4 + 2) + 8192 * 2 == 436_224_000
+    # the same with MXFP4 out: half a byte per code and one E8M0 byte per 32 elements
+    assert bench.partials_bytes(replace(p, out_dtype="fp4_e2m1"), "mx32") == \
+        2048 * (8192 * (8 * 2 + 4 + 4) + 8192 // 2 + 8192 // 32) + 8192 * 2
 
 
 def _run(*args):
