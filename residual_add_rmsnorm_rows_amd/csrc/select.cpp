@@ -390,7 +390,16 @@ rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int
       return RN_OK;
     }
   }
-  return select_rows_shape(rows, hidden, key, num_cus, tw, tnv, true, cfg);
+  const rn_status st = select_rows_shape(rows, hidden, key, num_cus, tw, tnv, true, cfg);
+  // Partial inputs with block-scaled outputs (per-128 fp8, MX, NVFP4): their
+  // kernels take too many registers for two workgroups of more than 8 waves
+  // per CU, so a row of one vector per lane over more than 8 waves runs as
+  // half the waves with 2 vectors per lane (bf16 partials, f32 residual,
+  // 2 and 8 partials, 7168 and 8192 wide: 8 x 2 measured 12-17% faster than
+  // 14-16 x 1; at 4096 wide 8 x 1 and 4 x 2 are within 2%).
+  if (st == RN_OK && key.kp > 1 && key.qs != kQRow && cfg->vecs_per_lane == 1 && cfg->waves_per_row > 8)
+    fill_rows_cfg(cfg->vec, (cfg->waves_per_row + 1) / 2, 2, rows, cfg->grid, cfg);
+  return st;
 }
 
 rn_status check_row_config(int64_t rows, int64_t hidden, const RowKey& key,

@@ -394,6 +394,19 @@ def test_partials_selector():
     assert (c["waves_per_row"], c["vecs_per_lane"]) == (4, 2)
     c = R.query_partials_config(32, 8192, 8, res_dtype="f32")  # decode: at most 8 waves
     assert (c["waves_per_row"], c["vecs_per_lane"]) == (8, 2)
+    # block-scaled outputs: more than 8 waves of one vector run as half the
+    # waves with 2 vectors (measured 12-17% faster); per-row fp8 keeps 16 x 1
+    for od, scheme in (("fp8_e4m3fn", "group128"), ("fp8_e4m3fn", "mx32"), ("fp4_e2m1", "mx32"),
+                       ("fp4_e2m1", "nv16")):
+        for n, hidden in ((8, 8192), (2, 8192), (2, 7168)):
+            c = R.query_partials_config(2048, hidden, n, res_dtype="f32", out_dtype=od, scale_scheme=scheme)
+            assert (c["waves_per_row"], c["vecs_per_lane"]) == (8, 2), (od, scheme, n, hidden, c)
+        c = R.query_partials_config(4096, 4096, 8, res_dtype="f32", out_dtype=od, scale_scheme=scheme)
+        assert (c["waves_per_row"], c["vecs_per_lane"]) == (8, 1)
+        c = R.query_partials_config(2048, 12288, 8, res_dtype="f32", out_dtype=od, scale_scheme=scheme)
+        assert (c["waves_per_row"], c["vecs_per_lane"]) == (12, 2)
+    c = R.query_partials_config(2048, 8192, 8, res_dtype="f32", out_dtype="fp8_e4m3fn")
+    assert (c["waves_per_row"], c["vecs_per_lane"]) == (16, 1)
     # one partial is the single-input kernel and its tables
     assert R.query_partials_config(8192, 7168, 1, res_dtype="bf16", out_dtype="fp8_e4m3fn") == \
         R.query_config(8192, 7168, res_dtype="bf16", out_dtype="fp8_e4m3fn")
