@@ -85,6 +85,29 @@ def test_workload_full_size_sampled():
     assert rep["ok"], rep
 
 
+
+def test_block_scaled_full_size_sampled():
+    """2048 x 8192 with 8 partials and MXFP4 output in the selector's launch
+    configuration (8 waves x 2 vectors per lane); the oracle checks sampled
+    rows, including the first and the last."""
+    from dataclasses import replace
+
+    wl = replace(WL.WORKLOADS["partials_8x2048x8192"], out_dtype="fp4_e2m1")
+    cfg = R.query_partials_config(wl.rows, wl.hidden, 8, res_dtype="f32", out_dtype="fp4_e2m1", scale_scheme="mx32")
+    assert (cfg["waves_per_row"], cfg["vecs_per_lane"]) == (8, 2)
+    _announce(f"partials full size MXFP4 cfg={cfg}")
+    inp = WL.generate_partials(wl, seed=0)
+    parts = [to_dev(p, wl.x_dtype) for p in inp["partials"]]
+    r = R.fused_partials_add_rmsnorm(parts, to_dev(inp["residual"], wl.res_dtype), to_dev(inp["weight"], wl.w_dtype),
+                                     wl.eps, out_dtype=TORCH_DTYPES["fp4_e2m1"], scale_scheme="mx32", return_amax=True)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 517, 1024, 2046, 2047])
+    sub = {"partials": [p[rows] for p in inp["partials"]], "residual": inp["residual"][rows], "weight": inp["weight"]}
+    rep = judge_partials_rows(sub, wl.x_dtype, wl.res_dtype, wl.w_dtype, "fp4_e2m1", wl.eps, wl.weight_plus_one,
+                              to_host(r.out)[rows], to_host(r.residual_out)[rows], to_host(r.scale)[rows],
+                              to_host(r.amax)[rows], exact_sum=wl.exact_sum, scale_scheme="mx32")
+    assert rep["ok"], rep
+
 CASES = [  # (x, res, w, out, bias)
     ("bf16", "f32", "bf16", "bf16", False), ("bf16", "bf16", "bf16", "bf16", True),
     ("bf16", None, "bf16", "bf16", False), ("bf16", "f32", "f32", "f32", False),
