@@ -23,10 +23,12 @@
 //   * prefill: for the dtype classes and hidden sizes that were measured
 //     (2048..16384 wide rows), the fastest variant of an interleaved sweep
 //     from a table (kTuned; kTunedAct for SwiGLU); otherwise the exact fit
-//     with the fewest vectors per lane.  (With a residual and a 16/32-bit
-//     output, one extra partly idle wave often measured 0.5-2% faster than
-//     the exact fit; with fp8 output or no residual the same extra wave
-//     measured up to 25% slower, so the exact fit is the default);
+//     with the fewest vectors per lane, except for bf16 rows without a
+//     residual (bf16 output) and quantized outputs with a bf16 residual,
+//     which take 2 vectors per lane past 2 (resp. 8) waves.  (With a residual and a
+//     16/32-bit output, one extra partly idle wave often measured 0.5-2%
+//     faster than the exact fit; with fp8 output or no residual the same
+//     extra wave measured up to 25% slower, so the exact fit is the default);
 //   * grid = rows (a workgroup per row; MI355X's dispatcher refills CUs as
 //     workgroups finish, and persistent grids measured 1-7% slower).
 #include <math.h>
@@ -170,6 +172,10 @@ static const TunedParts kTunedParts[] = {
 // seven for the close calls), scored by the geometric mean of the throughput
 // at 1.2 GB and at 0.4 GB of traffic per call (kernel with nontemporal input
 // loads and output stores).
+// The 4608..6144 wide entries come from a later sweep of six dtype classes
+// at 1536..6144 wide (three repetitions, same score), entered where the
+// winner beat the selector's previous choice by at least 2% (the other
+// winners of that sweep are the rule below select_row_config's tables).
 // Key: x dtype, residual dtype (kNone: no residual), whether the output is
 // quantized (fp8 / fp4), hidden size.
 struct Tuned {
@@ -193,7 +199,8 @@ static const Tuned kTuned[] = {
     {kBF16, kBF16, true, 2048, 4, 1},    {kBF16, kBF16, true, 4096, 8, 1},
     {kBF16, kBF16, true, 5120, 5, 2},    {kBF16, kBF16, true, 7168, 8, 2},
     {kBF16, kBF16, true, 8192, 8, 2},    {kBF16, kBF16, true, 12288, 12, 2},
-    {kBF16, kBF16, true, 16384, 8, 4},
+    {kBF16, kBF16, true, 16384, 8, 4},   {kBF16, kBF16, true, 4608, 5, 2},
+    {kBF16, kBF16, true, 5376, 6, 2},    {kBF16, kBF16, true, 6144, 8, 2},
     // bf16 x, f32 residual stream, fp8/fp4 out
     {kBF16, kF32, true, 2048, 5, 1},     {kBF16, kF32, true, 4096, 8, 1},
     {kBF16, kF32, true, 5120, 8, 2},     {kBF16, kF32, true, 7168, 16, 1},
@@ -365,6 +372,24 @@ rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int
         tnv = t.nv;
         break;
       }
+    }
+  }
+  // Untabulated hidden sizes of two classes whose exact fit at one vector
+  // per lane runs many short waves: bf16 rows without a residual with bf16
+  // output (more than 2 waves) and quantized outputs with a bf16 residual
+  // (more than 8 waves) take 2 vectors per lane and the fewest waves instead.
+  // Swept at 2304-6144 wide: 2-31% faster for no residual, 6-14% for the
+  // quantized outputs past 4096 wide; checked at 19 other shapes and output
+  // schemes (1792-7680 wide, per-row and per-128 fp8, MXFP4, NVFP4): 1.00x
+  // to 1.37x.  Without a residual, f32 output measured 2-3% slower this way
+  // and keeps the exact fit.
+  if (tw == 0 && key.w == kBF16 && key.kp == 1 && key.x == kBF16 && num_cus >= 1 && rows > num_cus) {
+    const int64_t nvec = hidden / 8;
+    const bool no_res = key.res == kNone && key.out == kBF16 && nvec > 2 * 64;
+    const bool quant_bf16_res = key.res == kBF16 && quant && nvec > 8 * 64;
+    if ((no_res || quant_bf16_res) && nvec <= 2 * 64 * kMaxWavesPerRow) {
+      tw = static_cast<int>((nvec + 127) / 128);
+      tnv = 2;
     }
   }
   if (key.kp > 1 && key.x == kBF16 && num_cus >= 1 && rows > num_cus) {

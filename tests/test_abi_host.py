@@ -242,6 +242,19 @@ def test_selector_shapes_of_the_workloads():
     assert (c["waves_per_row"], c["vecs_per_lane"]) == (6, 1)
     c = _cfg_res(4096, 10240, "bf16")
     assert (c["waves_per_row"], c["vecs_per_lane"]) == (10, 2)
+    # ... except bf16 rows without a residual (bf16 out) past 2 waves and
+    # quantized outputs with a bf16 residual past 8 waves: 2 vectors per lane
+    for hidden, shape in ((2304, (3, 2)), (2816, (3, 2)), (6656, (7, 2)), (1024, (2, 1))):
+        c = _cfg(100000, hidden)
+        assert (c["waves_per_row"], c["vecs_per_lane"]) == shape, (hidden, c)
+    c = _cfg(100000, 3328, out="f32")  # f32 out keeps the exact fit
+    assert (c["waves_per_row"], c["vecs_per_lane"]) == (7, 1)
+    for out, scheme in (("fp8_e4m3fn", "row"), ("fp8_e4m3fn", "group128"), ("fp4_e2m1", "mx32"), ("fp4_e2m1", "nv16")):
+        for hidden, shape in ((6656, (7, 2)), (4352, (5, 2)), (3584, (7, 1)), (6144, (8, 2))):
+            c = R.query_config(100000, hidden, res_dtype="bf16", out_dtype=out, scale_scheme=scheme)
+            assert (c["waves_per_row"], c["vecs_per_lane"]) == shape, (out, scheme, hidden, c)
+    c = _cfg_res(100000, 6656, "f32", out="fp8_e4m3fn")  # f32 residual keeps the exact fit
+    assert (c["waves_per_row"], c["vecs_per_lane"]) == (13, 1)
     # mid-size calls: their own table per rows-per-CU bucket
     c = _cfg_res(1024, 8192, "bf16")
     assert (c["waves_per_row"], c["vecs_per_lane"]) == (2, 8)

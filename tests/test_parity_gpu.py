@@ -252,6 +252,30 @@ def test_block_scaled_outputs(scheme, out, x, res, rows, hidden):
         assert np.all(sc[0, 1] == 0)
 
 
+@pytest.mark.parametrize("res,out,scheme,hidden,shape", [
+    (None, "bf16", "row", 2816, (3, 2)), (None, "bf16", "row", 6656, (7, 2)),
+    ("bf16", "fp8_e4m3fn", "row", 6656, (7, 2)), ("bf16", "fp8_e4m3fn", "group128", 4352, (5, 2)),
+    ("bf16", "fp4_e2m1", "mx32", 6656, (7, 2)), ("bf16", "fp4_e2m1", "nv16", 6144, (8, 2)),
+])
+def test_selector_two_vector_rule(res, out, scheme, hidden, shape):
+    """The selector's 2-vectors-per-lane shapes for rows without a residual and
+    for quantized outputs with a bf16 residual (rows whose last wave is partly
+    idle), in the selector's own launch configuration."""
+    rows = 300
+    cfg = R.query_config(rows, hidden, res_dtype=res, out_dtype=out, scale_scheme=scheme, num_cus=0)
+    _announce(f"two-vector rule res={res} out={out}/{scheme} {rows}x{hidden} cfg={cfg}")
+    assert (cfg["waves_per_row"], cfg["vecs_per_lane"]) == shape
+    wl = WL.RowNormWorkload(name="rule", kind="test", rows=rows, hidden=hidden, x_dtype="bf16", res_dtype=res,
+                            w_dtype="bf16", out_dtype=out, x_dist=WL.Dist(0, 1, 0.01, 20.0),
+                            res_dist=None if res is None else WL.Dist(0, 1, 0.01, 20.0),
+                            w_dist=WL.Dist(1, 0.1), weight_plus_one=False, eps=1e-6)
+    inputs = WL.generate_rownorm(wl, seed=14)
+    ts = nvfp4_tensor_scale(oracle_y(wl, inputs)) if scheme == "nv16" else None
+    r = run_rownorm(wl, inputs, scale_scheme=scheme, tensor_scale=ts)
+    rep = judge(wl, inputs, r, scale_scheme=scheme, tensor_scale=ts)
+    assert rep["ok"], rep
+
+
 @pytest.mark.parametrize("scheme,out", [("group128", "fp8_e4m3fn"), ("mx32", "fp4_e2m1"), ("mx32", "fp8_e4m3fn"),
                                         ("nv16", "fp4_e2m1")])
 def test_block_scaled_every_launch_variant(scheme, out):
