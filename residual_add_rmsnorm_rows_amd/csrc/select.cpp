@@ -23,9 +23,9 @@
 //   * prefill: for the dtype classes and hidden sizes that were measured
 //     (2048..16384 wide rows), the fastest variant of an interleaved sweep
 //     from a table (kTuned; kTunedAct for SwiGLU); otherwise the exact fit
-//     with the fewest vectors per lane, except for bf16 rows without a
-//     residual (bf16 output) and quantized outputs with a bf16 residual,
-//     which take 2 vectors per lane past 2 (resp. 8) waves.  (With a residual and a
+//     with the fewest vectors per lane, except for rows without a residual
+//     (2 or 4 vectors per lane, by output width) and quantized outputs with
+//     a residual of the x dtype (2 vectors per lane past 8 waves).  (With a residual and a
 //     16/32-bit output, one extra partly idle wave often measured 0.5-2%
 //     faster than the exact fit; with fp8 output or no residual the same
 //     extra wave measured up to 25% slower, so the exact fit is the default);
@@ -374,22 +374,40 @@ rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int
       }
     }
   }
-  // Untabulated hidden sizes of two classes whose exact fit at one vector
-  // per lane runs many short waves: bf16 rows without a residual with bf16
-  // output (more than 2 waves) and quantized outputs with a bf16 residual
-  // (more than 8 waves) take 2 vectors per lane and the fewest waves instead.
-  // Swept at 2304-6144 wide: 2-31% faster for no residual, 6-14% for the
-  // quantized outputs past 4096 wide; checked at 19 other shapes and output
-  // schemes (1792-7680 wide, per-row and per-128 fp8, MXFP4, NVFP4): 1.00x
-  // to 1.37x.  Without a residual, f32 output measured 2-3% slower this way
-  // and keeps the exact fit.
-  if (tw == 0 && key.w == kBF16 && key.kp == 1 && key.x == kBF16 && num_cus >= 1 && rows > num_cus) {
-    const int64_t nvec = hidden / 8;
-    const bool no_res = key.res == kNone && key.out == kBF16 && nvec > 2 * 64;
-    const bool quant_bf16_res = key.res == kBF16 && quant && nvec > 8 * 64;
-    if ((no_res || quant_bf16_res) && nvec <= 2 * 64 * kMaxWavesPerRow) {
-      tw = static_cast<int>((nvec + 127) / 128);
-      tnv = 2;
+  // Untabulated shapes whose exact fit at one vector per lane runs many
+  // short waves take more vectors per lane and the fewest waves instead; the
+  // fewer bytes one lane vector streams, the more vectors pay:
+  //   * no residual, output narrower than x (fp8 / fp4, or f32 x to bf16):
+  //     4 vectors per lane;
+  //   * no residual, output as wide as x: 2 vectors per lane;
+  //   * a quantized output with a residual of the x dtype, past 8 waves:
+  //     2 vectors per lane.
+  // Swept at 1536-8192 wide: 1.26-1.70x for bf16 rows to fp8 without a
+  // residual, 1.09-1.50x for f32 rows without one, 2-31% for bf16 rows to
+  // bf16 without one, 6-14% (bf16) and 4-14% (f32) for the quantized
+  // outputs; within 2.5% of each size's best shape.  A wider output (bf16 x
+  // to f32 out without a residual) measured 2-3% slower this way and keeps
+  // the exact fit, as do the other classes (within 2% of their best).
+  if (tw == 0 && key.w == kBF16 && key.kp == 1 && num_cus >= 1 && rows > num_cus) {
+    const int64_t nvec = hidden / (key.x == kBF16 ? 8 : 4);
+    const int xb = key.x == kBF16 ? 2 : 4;
+    const int ob = key.out == kBF16 ? 2 : key.out == kF32 ? 4 : 1;
+    int nv_rule = 0;
+    if (key.res == kNone && nvec > 2 * 64) {
+      if (quant || ob < xb) {
+        nv_rule = 4;
+      } else if (ob == xb) {
+        nv_rule = 2;
+      }
+    } else if (key.res == key.x && quant && nvec > 8 * 64) {
+      nv_rule = 2;
+    }
+    if (nv_rule) {
+      const int64_t w = (nvec + 64 * nv_rule - 1) / (64 * nv_rule);
+      if (w <= kMaxWavesPerRow && 64 * w <= max_threads_for_nv(nv_rule)) {
+        tw = static_cast<int>(w);
+        tnv = nv_rule;
+      }
     }
   }
   if (key.kp > 1 && key.x == kBF16 && num_cus >= 1 && rows > num_cus) {

@@ -255,6 +255,17 @@ def test_selector_shapes_of_the_workloads():
             assert (c["waves_per_row"], c["vecs_per_lane"]) == shape, (out, scheme, hidden, c)
     c = _cfg_res(100000, 6656, "f32", out="fp8_e4m3fn")  # f32 residual keeps the exact fit
     assert (c["waves_per_row"], c["vecs_per_lane"]) == (13, 1)
+    # no residual and an output narrower than x: 4 vectors per lane; f32 rows
+    # to f32: 2; quantized f32 rows with an f32 residual: 2 past 8 waves
+    for x, out, scheme, hidden, shape in (("bf16", "fp8_e4m3fn", "row", 5376, (3, 4)),
+                                          ("bf16", "fp4_e2m1", "mx32", 1536, (1, 4)),
+                                          ("f32", "bf16", "row", 6144, (6, 4)), ("f32", "f32", "row", 3072, (6, 2))):
+        c = R.query_config(100000, hidden, x_dtype=x, out_dtype=out, scale_scheme=scheme)
+        assert (c["waves_per_row"], c["vecs_per_lane"]) == shape, (x, out, hidden, c)
+    c = R.query_config(100000, 3584, x_dtype="f32", res_dtype="f32", out_dtype="fp8_e4m3fn")
+    assert (c["waves_per_row"], c["vecs_per_lane"]) == (7, 2)
+    c = R.query_config(100000, 1536, x_dtype="f32", res_dtype="f32", out_dtype="fp8_e4m3fn")
+    assert (c["waves_per_row"], c["vecs_per_lane"]) == (6, 1)  # at most 8 waves: the exact fit
     # mid-size calls: their own table per rows-per-CU bucket
     c = _cfg_res(1024, 8192, "bf16")
     assert (c["waves_per_row"], c["vecs_per_lane"]) == (2, 8)
