@@ -268,8 +268,10 @@ static const TunedMid kTunedMid[] = {
 // SwiGLU (bf16 x): fastest (waves, vectors per lane) measured on MI355X,
 // scored like kTuned (geometric mean at 1.2 GB and 0.4 GB per call, five
 // interleaved repetitions), entered where it beat the exact fit by more than
-// half a percent.  Output class: 0 bf16 / f32, 1 fp8 (measured with MX
-// scales), 2 fp4 (measured with NVFP4 scales).
+// half a percent.  A later sweep of intermediate sizes 4096-27648 (three
+// repetitions) added 5632, 6144, 8960, 9728 and 27648, where the winner beat
+// the exact fit by 2.4-6.2%.  Output class: 0 bf16 / f32, 1 fp8 (measured
+// with MX scales), 2 fp4 (measured with NVFP4 scales).
 struct TunedAct {
   int out_class;
   int d;
@@ -281,6 +283,8 @@ static const TunedAct kTunedAct[] = {
     {1, 13824, 9, 4},  {1, 14336, 9, 4},  {1, 28672, 8, 8},
     {2, 8192, 8, 2},   {2, 11008, 6, 4},  {2, 13824, 4, 8},  {2, 14336, 4, 8},
     {2, 28672, 16, 4},
+    {0, 6144, 13, 1},  {0, 27648, 16, 4}, {2, 5632, 4, 4},   {2, 6144, 6, 2},
+    {2, 8960, 5, 4},   {2, 9728, 6, 4},
 };
 
 // SwiGLU mid-size calls (CUs < rows <= 16 x CUs), measured and entered as

@@ -278,6 +278,10 @@ def test_selector_shapes_of_the_workloads():
     assert (a["waves_per_row"], a["vecs_per_lane"]) == (4, 8) and a["block_threads"] == 256
     a = R.query_silu_mul_config(16, 14336)
     assert (a["waves_per_row"], a["vecs_per_lane"]) == (14, 2)
+    a = R.query_silu_mul_config(8192, 9728, out_dtype="fp4_e2m1", scale_scheme="nv16")
+    assert (a["waves_per_row"], a["vecs_per_lane"]) == (6, 4)
+    a = R.query_silu_mul_config(8192, 6144)
+    assert (a["waves_per_row"], a["vecs_per_lane"]) == (13, 1)
 
 
 def test_head_mapping_covers_each_row_once():
