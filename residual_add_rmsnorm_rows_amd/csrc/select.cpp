@@ -385,14 +385,19 @@ rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int
   //     4 vectors per lane;
   //   * no residual, output as wide as x: 2 vectors per lane;
   //   * a quantized output with a residual of the x dtype, past 8 waves:
-  //     2 vectors per lane.
-  // Swept at 1536-8192 wide: 1.26-1.70x for bf16 rows to fp8 without a
-  // residual, 1.09-1.50x for f32 rows without one, 2-31% for bf16 rows to
-  // bf16 without one, 6-14% (bf16) and 4-14% (f32) for the quantized
-  // outputs; within 2.5% of each size's best shape.  A wider output (bf16 x
-  // to f32 out without a residual) measured 2-3% slower this way and keeps
-  // the exact fit, as do the other classes (within 2% of their best).
-  if (tw == 0 && key.w == kBF16 && key.kp == 1 && num_cus >= 1 && rows > num_cus) {
+  //     2 vectors per lane;
+  //   * with an f32 weight, a bf16 residual and bf16 output, past 8 waves:
+  //     4 vectors per lane.
+  // Swept at 1536-8192 wide with a bf16 weight: 1.26-1.70x for bf16 rows to
+  // fp8 without a residual, 1.09-1.50x for f32 rows without one, 2-31% for
+  // bf16 rows to bf16 without one, 6-14% (bf16) and 4-14% (f32) for the
+  // quantized outputs; within 2.5% of each size's best shape.  With an f32
+  // weight (2048-8192 wide): 1.10-1.58x, 1.02-1.27x and 1.04-1.16x for the
+  // first three bf16 classes past the sizes the rule starts at, and 3-8% for
+  // the last.  A wider output (bf16 x to f32 out without a residual)
+  // measured 2-3% slower this way and keeps the exact fit, as do the other
+  // classes (within 2% of their best).
+  if (tw == 0 && key.kp == 1 && num_cus >= 1 && rows > num_cus) {
     const int64_t nvec = hidden / (key.x == kBF16 ? 8 : 4);
     const int xb = key.x == kBF16 ? 2 : 4;
     const int ob = key.out == kBF16 ? 2 : key.out == kF32 ? 4 : 1;
@@ -405,6 +410,8 @@ rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int
       }
     } else if (key.res == key.x && quant && nvec > 8 * 64) {
       nv_rule = 2;
+    } else if (key.w == kF32 && key.x == kBF16 && key.res == kBF16 && key.out == kBF16 && nvec > 8 * 64) {
+      nv_rule = 4;
     }
     if (nv_rule) {
       const int64_t w = (nvec + 64 * nv_rule - 1) / (64 * nv_rule);

@@ -266,6 +266,13 @@ def test_selector_shapes_of_the_workloads():
     assert (c["waves_per_row"], c["vecs_per_lane"]) == (7, 2)
     c = R.query_config(100000, 1536, x_dtype="f32", res_dtype="f32", out_dtype="fp8_e4m3fn")
     assert (c["waves_per_row"], c["vecs_per_lane"]) == (6, 1)  # at most 8 waves: the exact fit
+    # an f32 weight takes the same rules, plus 4 vectors per lane past 8 waves
+    # with a bf16 residual and bf16 output
+    for res, out, hidden, shape in ((None, "bf16", 7168, (7, 2)), (None, "fp8_e4m3fn", 5120, (3, 4)),
+                                    ("bf16", "fp8_e4m3fn", 7168, (7, 2)), ("bf16", "bf16", 7168, (4, 4)),
+                                    ("bf16", "bf16", 4096, (8, 1)), ("f32", "bf16", 7168, (14, 1))):
+        c = R.query_config(100000, hidden, res_dtype=res, w_dtype="f32", out_dtype=out)
+        assert (c["waves_per_row"], c["vecs_per_lane"]) == shape, (res, out, hidden, c)
     # mid-size calls: their own table per rows-per-CU bucket
     c = _cfg_res(1024, 8192, "bf16")
     assert (c["waves_per_row"], c["vecs_per_lane"]) == (2, 8)

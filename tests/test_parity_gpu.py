@@ -252,25 +252,29 @@ def test_block_scaled_outputs(scheme, out, x, res, rows, hidden):
         assert np.all(sc[0, 1] == 0)
 
 
-@pytest.mark.parametrize("x,res,out,scheme,hidden,shape", [
-    ("bf16", None, "bf16", "row", 2816, (3, 2)), ("bf16", None, "bf16", "row", 6656, (7, 2)),
-    ("bf16", None, "fp8_e4m3fn", "row", 4352, (3, 4)), ("bf16", None, "fp4_e2m1", "mx32", 6656, (4, 4)),
-    ("bf16", None, "fp4_e2m1", "nv16", 2816, (2, 4)), ("f32", None, "bf16", "row", 4352, (5, 4)),
-    ("f32", None, "f32", "row", 2816, (6, 2)), ("f32", "f32", "fp8_e4m3fn", "group128", 3328, (7, 2)),
-    ("bf16", "bf16", "fp8_e4m3fn", "row", 6656, (7, 2)), ("bf16", "bf16", "fp8_e4m3fn", "group128", 4352, (5, 2)),
-    ("bf16", "bf16", "fp4_e2m1", "mx32", 6656, (7, 2)), ("bf16", "bf16", "fp4_e2m1", "nv16", 6144, (8, 2)),
+@pytest.mark.parametrize("x,res,w,out,scheme,hidden,shape", [
+    ("bf16", None, "bf16", "bf16", "row", 2816, (3, 2)), ("bf16", None, "bf16", "bf16", "row", 6656, (7, 2)),
+    ("bf16", None, "bf16", "fp8_e4m3fn", "row", 4352, (3, 4)), ("bf16", None, "bf16", "fp4_e2m1", "mx32", 6656, (4, 4)),
+    ("bf16", None, "bf16", "fp4_e2m1", "nv16", 2816, (2, 4)), ("f32", None, "bf16", "bf16", "row", 4352, (5, 4)),
+    ("f32", None, "bf16", "f32", "row", 2816, (6, 2)), ("f32", "f32", "bf16", "fp8_e4m3fn", "group128", 3328, (7, 2)),
+    ("bf16", "bf16", "bf16", "fp8_e4m3fn", "row", 6656, (7, 2)),
+    ("bf16", "bf16", "bf16", "fp8_e4m3fn", "group128", 4352, (5, 2)),
+    ("bf16", "bf16", "bf16", "fp4_e2m1", "mx32", 6656, (7, 2)), ("bf16", "bf16", "bf16", "fp4_e2m1", "nv16", 6144, (8, 2)),
+    ("bf16", None, "f32", "bf16", "row", 7168, (7, 2)), ("bf16", None, "f32", "fp8_e4m3fn", "row", 5120, (3, 4)),
+    ("bf16", "bf16", "f32", "bf16", "row", 6656, (4, 4)),
 ])
-def test_selector_more_vectors_rule(x, res, out, scheme, hidden, shape):
+def test_selector_more_vectors_rule(x, res, w, out, scheme, hidden, shape):
     """The selector's 2- and 4-vectors-per-lane shapes for rows without a
     residual and for quantized outputs with a residual of the x dtype (rows
     whose last wave is partly idle), in the selector's own launch
     configuration."""
     rows = 300
-    cfg = R.query_config(rows, hidden, x_dtype=x, res_dtype=res, out_dtype=out, scale_scheme=scheme, num_cus=0)
-    _announce(f"more-vectors rule x={x} res={res} out={out}/{scheme} {rows}x{hidden} cfg={cfg}")
+    cfg = R.query_config(rows, hidden, x_dtype=x, res_dtype=res, w_dtype=w, out_dtype=out, scale_scheme=scheme,
+                         num_cus=0)
+    _announce(f"more-vectors rule x={x} res={res} w={w} out={out}/{scheme} {rows}x{hidden} cfg={cfg}")
     assert (cfg["waves_per_row"], cfg["vecs_per_lane"]) == shape
     wl = WL.RowNormWorkload(name="rule", kind="test", rows=rows, hidden=hidden, x_dtype=x, res_dtype=res,
-                            w_dtype="bf16", out_dtype=out, x_dist=WL.Dist(0, 1, 0.01, 20.0),
+                            w_dtype=w, out_dtype=out, x_dist=WL.Dist(0, 1, 0.01, 20.0),
                             res_dist=None if res is None else WL.Dist(0, 1, 0.01, 20.0),
                             w_dist=WL.Dist(1, 0.1), weight_plus_one=False, eps=1e-6)
     inputs = WL.generate_rownorm(wl, seed=14)
