@@ -32,6 +32,9 @@ ARCH = "gfx950"
 
 # Packed fp32 VALU ops are kept out of generated code (-packed-fp32-ops);
 # the host pass of hipcc warns that it does not know the feature, harmlessly.
+# Each HIP translation unit gets a fixed compilation-unit ID (-cuid, below):
+# by default clang derives it from the source file's absolute path, which
+# would make the library's bytes depend on where the tree is checked out.
 HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -57,12 +60,12 @@ def _jobs():
     jobs = []
     for x, out, qs, name in ROW_VARIANTS:
         obj = os.path.join(BUILD_DIR, f"rows_{name}.o")
-        cmd = [HIPCC, *HIP_FLAGS, f"-DRN_TU_X={x}", f"-DRN_TU_OUT={out}", f"-DRN_TU_QS={qs}",
+        cmd = [HIPCC, *HIP_FLAGS, f"-cuid=rows_{name}", f"-DRN_TU_X={x}", f"-DRN_TU_OUT={out}", f"-DRN_TU_QS={qs}",
                f"-DRN_TU_NAME={name}", "-c", os.path.join(CSRC, "rows_kernel.hip"), "-o", obj]
         jobs.append((obj, cmd))
     for name in ("heads_kernel", "act_kernel", "reference_kernels"):
         obj = os.path.join(BUILD_DIR, f"{name}.o")
-        jobs.append((obj, [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, f"{name}.hip"), "-o", obj]))
+        jobs.append((obj, [HIPCC, *HIP_FLAGS, f"-cuid={name}", "-c", os.path.join(CSRC, f"{name}.hip"), "-o", obj]))
     for src in ("select.cpp", "abi.cpp"):
         obj = os.path.join(BUILD_DIR, src.replace(".cpp", ".o"))
         jobs.append((obj, ["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
