@@ -57,16 +57,49 @@ def _row_cases(n=48, seed=2024):
     return cases
 
 
+def _row_cases_prefill(n=24, seed=2026):
+    """Row counts past the compute-unit count, where the selector's prefill
+    tables and its more-vectors rule apply; always the selector's launch."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        x = ["bf16", "f32"][rng.integers(2)]
+        res = [None, x, "f32"][rng.integers(3)]
+        w = ["bf16", "f32"][rng.integers(2)]
+        out, scheme = OUTS[rng.integers(len(OUTS))]
+        vec = 8 if x == "bf16" else 4
+        g = int(np.lcm(vec, GRANULE[scheme]))
+        hmax = 8192 if x == "bf16" else 4096
+        hidden = g * int(rng.integers(1024 // g + 1, hmax // g + 1))
+        rows = int(rng.integers(257, 601))
+        cases.append((i, x, res, w, out, scheme, bool(rng.integers(2)), hidden, rows, int(rng.integers(1 << 30))))
+    return cases
+
+
 @pytest.mark.parametrize("case", _row_cases(), ids=lambda c: f"r{c[0]}")
 def test_random_rows(case):
+    _row_case(case, selector_only=False)
+
+
+@pytest.mark.parametrize("case", _row_cases_prefill(), ids=lambda c: f"rp{c[0]}")
+def test_random_rows_prefill_selector(case):
+    _row_case(case, selector_only=True)
+
+
+def _row_case(case, selector_only):
     i, x, res, w, out, scheme, b, hidden, rows, seed = case
     rng = np.random.default_rng(seed)
     wl = WL.RowNormWorkload(name="rand", kind="test", rows=rows, hidden=hidden, x_dtype=x, res_dtype=res,
                             w_dtype=w, out_dtype=out, x_dist=WL.Dist(0, 1, 0.01, 20.0),
                             res_dist=None if res is None else WL.Dist(0, 3), w_dist=WL.Dist(0.0 if b else 1.0, 0.2),
                             weight_plus_one=b, eps=float(np.float32(10.0 ** rng.uniform(-7, -3))))
-    cfg = _random_config(rng, hidden, 8 if x == "bf16" else 4, rows)
-    cfg_txt = None if cfg is None else (cfg.waves_per_row, cfg.vecs_per_lane, cfg.grid)
+    cfg = None if selector_only else _random_config(rng, hidden, 8 if x == "bf16" else 4, rows)
+    if cfg is None:
+        q = R.query_config(rows, hidden, x_dtype=x, res_dtype=res, w_dtype=w, out_dtype=out, weight_plus_one=b,
+                           scale_scheme=scheme, num_cus=0)
+        cfg_txt = ("selector", q["waves_per_row"], q["vecs_per_lane"], q["grid"])
+    else:
+        cfg_txt = (cfg.waves_per_row, cfg.vecs_per_lane, cfg.grid)
     _announce(f"random rows #{i}: x={x} res={res} w={w} out={out}/{scheme} plus_one={b} rows={rows} H={hidden} "
               f"cfg={cfg_txt}")
     inputs = WL.generate_rownorm(wl, seed=seed)
