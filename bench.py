@@ -10,8 +10,8 @@ on the stream the kernel runs on.
 
 The same line carries:
   * ``roofline``: the kernel against MI355X's 8 TB/s HBM peak, plus the HBM
-    bytes measured by rocprofv3 counters when a counter summary for the
-    current kernel sources is present under profiles/;
+    bytes measured by rocprofv3 counters when profiles/ holds a counter
+    summary taken on this very library build (same sha256), else null;
   * ``cpu_baseline``: the CPU oracle (numpy, float64) timed on a bounded
     sample of the same workload on this host;
   * ``secondary``: the other workloads -- decode calls (us/call against an
@@ -19,7 +19,8 @@ The same line carries:
     prefill with per-row scales, the same prefill with block-scaled
     outputs (fp8 per-128 scales, MXFP8, MXFP4, NVFP4), the sum of 8 partial
     inputs in front of the add (one GPU's share of a tensor-parallel
-    reduce-scatter), and the SiLU-and-mul activation (bf16, MXFP8, MXFP4,
+    reduce-scatter; bf16 and MXFP4 out, and a 64-token decode call), and the
+    SiLU-and-mul activation (bf16, MXFP8, MXFP4,
     NVFP4 out) (GB/s, with rotating buffer sets larger than the 256 MB
     Infinity Cache so that every call streams from HBM).
 
