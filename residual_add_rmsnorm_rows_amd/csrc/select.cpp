@@ -391,7 +391,7 @@ rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int
   // Swept at 1536-8192 wide with a bf16 weight: 1.26-1.70x for bf16 rows to
   // fp8 without a residual, 1.09-1.50x for f32 rows without one, 2-31% for
   // bf16 rows to bf16 without one, 6-14% (bf16) and 4-14% (f32) for the
-  // quantized outputs; within 2.5% of each size's best shape.  With an f32
+  // quantized outputs; within 2.5% of each size's best shape (2.7% once).  With an f32
   // weight (2048-8192 wide): 1.10-1.58x, 1.02-1.27x and 1.04-1.16x for the
   // first three bf16 classes past the sizes the rule starts at, and 3-8% for
   // the last.  A wider output (bf16 x to f32 out without a residual)
