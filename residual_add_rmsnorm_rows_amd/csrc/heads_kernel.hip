@@ -91,8 +91,8 @@ __global__ __launch_bounds__(kHeadBlockThreads) void heads_kernel(const HeadArgs
     float y[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
-      if constexpr (BIAS) wf[i] += 1.0f;
-      y[i] = wf[i] * (x[i] * inv);
+      const float t = x[i] * inv;
+      y[i] = BIAS ? __builtin_fmaf(wf[i], t, t) : wf[i] * t;  // (1 + w) t, one rounding
     }
     uint32_t ow[4];
     pack<TD, VEC>(y, ow);

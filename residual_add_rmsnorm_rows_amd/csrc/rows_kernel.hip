@@ -10,6 +10,8 @@
 //   y   = (w + b) * (h * inv)             -> out (bf16 / f32), or
 //   fp8: p = (w + b) * h, amax = max|p| * inv, y = p * inv,
 //        code = e4m3fn(y * (448 / amax)), scale = amax / 448
+//   (with b = 1, (w + 1) t is evaluated as the fused multiply-add w t + t:
+//   one rounding)
 //
 // Layout of one row across the workgroup: each lane holds NV steps of VEC
 // elements, VEC = 16 bytes of x (8 bf16 or 4 f32).  Step s of lane `lane` in
@@ -219,8 +221,8 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(NV, KP, QS)))) void rows_ker
           unpack<WD, U>(ww[s][c], wf);
 #pragma unroll
           for (int i = 0; i < U; ++i) {
-            if constexpr (BIAS) wf[i] += 1.0f;
-            h[s][c][i] = wf[i] * h[s][c][i];
+            // (1 + w) h as one fused multiply-add w h + h: a single rounding
+            h[s][c][i] = BIAS ? __builtin_fmaf(wf[i], h[s][c][i], h[s][c][i]) : wf[i] * h[s][c][i];
             if constexpr (QS == kQRow) mx = __builtin_fmaxf(mx, __builtin_fabsf(h[s][c][i]));
           }
         }
@@ -278,8 +280,8 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(NV, KP, QS)))) void rows_ker
           unpack<WD, U>(ww[s][c], wf);
 #pragma unroll
           for (int i = 0; i < U; ++i) {
-            if constexpr (BIAS) wf[i] += 1.0f;
-            y[i] = wf[i] * (h[s][c][i] * inv);
+            const float t = h[s][c][i] * inv;
+            y[i] = BIAS ? __builtin_fmaf(wf[i], t, t) : wf[i] * t;  // (1 + w) t, one rounding
           }
         }
         uint32_t ow[OW];
