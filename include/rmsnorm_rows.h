@@ -11,7 +11,8 @@
  * normalized row, one cast back to the storage type.  The page's "Inference at
  * Perplexity" section names the weight bias (plain w, or 1 + w) as a knob of
  * RMS norm; here it is the RN_FLAG_WEIGHT_PLUS_ONE flag and is specialized at
- * compile time.
+ * compile time.  With it, (1 + w) t is evaluated as the float32 fused
+ * multiply-add w t + t (one rounding of the exact product).
  *
  * rmsnorm_fwd adds an optional residual stream in front of the norm (fused
  * residual add): h = round_res(x + residual) is written to residual_out and the
