@@ -29,7 +29,7 @@
  * the "QK Norm" section's kernel (heads of Q first, then heads of K, per token).
  *
  * rmsnorm_fwd_partials is the same fused add + norm with x given as a sum of
- * up to 8 partial tensors (summed in the kernel, in float32).
+ * up to 8 partial tensors (summed exactly in the kernel, rounded once).
  *
  * silu_mul_fwd is the SwiGLU activation over rows of a merged gate/up
  * projection, with the same output types as rmsnorm_fwd.
@@ -227,16 +227,19 @@ rn_status rmsnorm_fwd_config(const void* x, const void* residual, const void* we
  *   hidden        as rmsnorm_fwd, and at most 2048 lane vectors (16384 bf16 / 8192 f32
  *                 elements) when num_partials > 1
  *
- * Reading (not on the pages): x = ((p_0 + p_1) + p_2) + ... is summed in
- * float32 in slot order, without rounding to the x dtype, then
- * h = round_res(x + residual) as in rmsnorm_fwd (float32 add, one rounding to
- * the residual dtype), or h = x (float32) without a residual, and the norm
- * and the output are those of rmsnorm_fwd over h.  When every prefix sum of
- * the partials is a float32 value (as for bf16 partials within 2^12 of one
- * another in magnitude, or zero) the float32 sum is exact and the result is
- * that of rmsnorm_fwd on the exact sum; otherwise each float32 addition
- * rounds once (total error within (num_partials - 1) * 2^-24 * sum_k |p_k|,
- * to first order).
+ * Reading (not on the pages): x is the exact sum of the partials.  With a
+ * residual, h = round_res(p_0 + ... + p_{n-1} + residual) is the exact sum of
+ * all the terms rounded once (to nearest even) to the residual dtype and
+ * written to residual_out; without one, h is the exact sum rounded once to
+ * float32.  The norm and the output are those of rmsnorm_fwd over h, so the
+ * result does not depend on the order of the partials.  The kernel sums with
+ * error-free float32 additions (TwoSum) whose rounding errors it keeps in a
+ * double, then rounds once through round-to-odd; this is the exact sum
+ * whenever the largest running sum is below 2^74 times the last significant
+ * bit of the smallest nonzero term -- for bf16 terms, any terms within 2^63
+ * of one another in magnitude, for float32 terms within 2^47 -- and the
+ * running sums stay below float32's largest value.  Outside that range the
+ * sum can be off in its last bit.
  * num_partials == 1 is rmsnorm_fwd_ex on x = partials[0].
  * Aliasing: out may equal one of the partials (in place); residual_out may
  * equal residual; residual_out equal to a partial or to out is rejected; any

@@ -211,6 +211,17 @@ __device__ __forceinline__ void unpack(const uint32_t (&w)[words_for<DT, VEC>()]
   }
 }
 
+// Element i of a lane vector of dtype DT (bf16 or f32) as a float.
+template <int DT, int N>
+__device__ __forceinline__ float element(const uint32_t (&w)[N], int i) {
+  if constexpr (DT == kBF16) {
+    return (i & 1) ? bf16_hi(w[i / 2]) : bf16_lo(w[i / 2]);
+  } else {
+    static_assert(DT == kF32, "inputs are bf16 or f32");
+    return __uint_as_float(w[i]);
+  }
+}
+
 // Pack floats to a lane vector of dtype DT: bf16/f32 round to nearest even;
 // fp8 e4m3fn and fp4 e2m1 take values already scaled into the format's range
 // (codes in element order from the low byte / low nibble up).
@@ -293,6 +304,83 @@ __device__ __forceinline__ float group_reduce(float v) {
     v = Op::apply(Op::apply(r0, r1), Op::apply(r2, r3));
   }
   return v;
+}
+
+// ---------------------------------------------------------------------------
+// Exact sums of float32 terms (the partial inputs and the residual).
+//
+// The running sum s is a float32 value and every addition goes through
+// Knuth's TwoSum, an error-free transformation: t = fl(s + v) and
+// e = (s + v) - t exactly, in six float32 additions and no branch.  The
+// errors are summed in a double c.  The exact sum is s + c provided that sum
+// of errors is itself exact, which holds whenever the largest running sum is
+// below 2^74 times the last significant bit of the smallest nonzero term:
+// every error is a multiple of that bit and at most 2^-24 of the running sum,
+// so the sums of up to eight of them stay within 53 bits.  For nine terms or
+// fewer with 8 significant bits (bf16 values) that is any set of terms within
+// 2^63 of one another in magnitude; with 24 (float32), within 2^47.  (bf16
+// terms within 2^12 of one another are summed exactly in float32 and c stays
+// zero.)
+//
+// Rounding the exact sum once to a narrower format goes through round-to-odd
+// at an intermediate precision: rounding to odd with at least two more bits
+// than the target and then to nearest even is the same as rounding the exact
+// value to nearest even once (Boldo and Melquiond, "Emulation of FMA and
+// correctly rounded sums: proved algorithms using rounding to odd", IEEE
+// Transactions on Computers, 2008).  Double has 53 bits, float32 24, bfloat16
+// 8, so double -> float32 needs one such step and double -> bfloat16 two.
+// When every error of a wave is zero, s is the exact sum and no step is needed.
+// ---------------------------------------------------------------------------
+
+struct ExactSum {
+  float s;   // running sum, rounded
+  double c;  // exact sum of the rounding errors (within the range above)
+  __device__ __forceinline__ void init(float v) {
+    s = v;
+    c = 0.0;
+  }
+  __device__ __forceinline__ void add(float v) {
+    const float t = s + v;
+    const float bv = t - s;
+    const float e = (s - (t - bv)) + (v - bv);
+    s = t;
+    c += static_cast<double>(e);
+  }
+};
+
+// Step a value one unit in the last place toward the exact value it
+// approximates: away from zero when `away`, else toward zero (bit patterns of
+// one sign are ordered like the magnitudes).
+__device__ __forceinline__ double step_ulp(double t, bool away) {
+  const uint64_t b = static_cast<uint64_t>(__double_as_longlong(t));
+  return __longlong_as_double(static_cast<long long>(away ? b + 1u : b - 1u));
+}
+__device__ __forceinline__ float step_ulp(float f, bool away) {
+  const uint32_t b = __float_as_uint(f);
+  return __uint_as_float(away ? b + 1u : b - 1u);
+}
+
+// The exact sum rounded once to float32: to nearest even (ODD == false), or
+// to odd (ODD == true) for a later nearest-even rounding to bfloat16.
+template <bool ODD>
+__device__ __forceinline__ float round_exact_sum(const ExactSum& a) {
+  if (__builtin_amdgcn_ballot_w64(a.c != 0.0) == 0) return a.s;  // every addition of the wave was exact
+  // t + r == s + c exactly; t rounded to odd at double precision stands for
+  // s + c in any rounding to 51 bits or fewer.  t != 0 whenever r != 0.
+  const double sd = static_cast<double>(a.s);
+  double t = sd + a.c;
+  const double bv = t - sd;
+  const double r = (sd - (t - bv)) + (a.c - bv);
+  if (a.c == 0.0) t = sd;  // sd + 0 would turn a -0 sum into +0
+  if (r != 0.0 && (__double_as_longlong(t) & 1) == 0) t = step_ulp(t, (r > 0.0) == (t > 0.0));
+  float f = static_cast<float>(t);  // nearest even of the exact sum
+  if constexpr (ODD) {
+    // nonzero: the terms are multiples of 2^-149, so a nonzero sum is at
+    // least 2^-149 in magnitude and never rounds to zero
+    const double back = static_cast<double>(f);
+    if (back != t && (__float_as_uint(f) & 1u) == 0) f = step_ulp(f, (t > back) == (f > 0.f));
+  }
+  return f;
 }
 
 }  // namespace rn

@@ -4,8 +4,9 @@
 // "QK Norm" section of "CuTeDSL at Perplexity", extended with a residual add
 // and an fp8 output whose readings are stated in include/rmsnorm_rows.h):
 //   h   = round_res(x + residual)         (or h = x without a residual)
-//         with x = ((p_0 + p_1) + p_2) + ...  in float32 for the variants that
-//         sum K partial inputs (KP slots, K <= KP) in front of the add
+//         for the variants that sum K partial inputs (KP slots, K <= KP):
+//         h = round_res(p_0 + ... + p_{K-1} + residual), the exact sum of all
+//         the terms rounded once (float32 without a residual)
 //   inv = rsqrt(sum(h^2) / H + eps)       (float32 accumulation)
 //   y   = (w + b) * (h * inv)             -> out (bf16 / f32), or
 //   fp8: p = (w + b) * h, amax = max|p| * inv, y = p * inv,
@@ -126,8 +127,14 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(NV, KP, QS)))) void rows_ker
 
   // Element offset of chunk (s, c) of this lane from the row start:
   // (((s * W + wave) * SUB + c) * 64 + lane) * U.  Chunks past the row end
-  // fall outside the row's buffer resources.
+  // fall outside the row's buffer resources.  The partial-input kernels write
+  // it as the lane's offset of chunk (0, 0) plus a per-chunk term, so that the
+  // chunk term of step 0 is a constant folded into the instructions' immediate
+  // offsets instead of one offset register per chunk and tensor (those
+  // kernels are the ones short of registers).
+  const uint32_t lane_elem = static_cast<uint32_t>((wave * SUB * 64 + lane) * U);
   auto elem_of = [&](int s, int c) -> uint32_t {
+    if constexpr (KP > 1) return lane_elem + static_cast<uint32_t>((s * nw * SUB + c) * 64 * U);
     return static_cast<uint32_t>((((s * nw + wave) * SUB + c) * 64 + lane) * U);
   };
 
@@ -154,6 +161,10 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(NV, KP, QS)))) void rows_ker
     uint32_t xw[NV][SUB][KP][XW];
     uint32_t rw[NV][SUB][HAS_RES ? RW : 1];
     uint32_t ww[NV][SUB][WW];
+    // The partial-input kernels load the weight only after the sums (it is a
+    // cache hit, first needed for the weighted products or the scaling): at
+    // the sums the loaded partials hold most of their registers.
+    constexpr bool LATE_W = KP > 1;
     if constexpr (KP > 1) {
 #pragma unroll
       for (int k = 0; k < KP; ++k) {
@@ -162,6 +173,24 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(NV, KP, QS)))) void rows_ker
         for (int s = 0; s < NV; ++s) {
 #pragma unroll
           for (int c = 0; c < SUB; ++c) buffer_load_words<XW * 4, true>(pr, elem_of(s, c) * XB, xw[s][c][k]);
+        }
+      }
+      // An unused slot loads zeros (an empty resource); its elements become
+      // -0, the identity of IEEE addition (x + -0 == x for every x, signed
+      // zeros included), so that the sums add every slot without a branch.
+      // The host launches a KP-slot kernel only for more than KP / 2
+      // partials, so the slots below that are always in use.
+      constexpr uint32_t kNegZeros = XD == kBF16 ? 0x80008000u : 0x80000000u;
+#pragma unroll
+      for (int k = KP / 2 + 1; k < KP; ++k) {
+        const uint32_t neg = k < a.num_parts ? 0u : kNegZeros;
+#pragma unroll
+        for (int s = 0; s < NV; ++s) {
+#pragma unroll
+          for (int c = 0; c < SUB; ++c) {
+#pragma unroll
+            for (int j = 0; j < XW; ++j) xw[s][c][k][j] |= neg;
+          }
         }
       }
     }
@@ -173,7 +202,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(NV, KP, QS)))) void rows_ker
         const uint32_t e = elem_of(s, c);
         if constexpr (KP == 1) buffer_load_words<XW * 4, true>(xr, e * XB, xw[s][c][0]);
         if constexpr (HAS_RES) buffer_load_words<RW * 4, true>(rr, e * RB, rw[s][c]);
-        buffer_load_words<WW * 4, false>(wr, e * WB, ww[s][c]);
+        if constexpr (!LATE_W) buffer_load_words<WW * 4, false>(wr, e * WB, ww[s][c]);
       }
     }
 
@@ -184,25 +213,43 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(NV, KP, QS)))) void rows_ker
     float h[NV][SUB][U];
     float ss = 0.f;
     float mx = 0.f;
+
 #pragma unroll
     for (int s = 0; s < NV; ++s) {
 #pragma unroll
       for (int c = 0; c < SUB; ++c) {
-        float xf[U];
-        unpack<XD, U>(xw[s][c][0], xf);
-        // partial inputs: added in slot order; the unused slots are skipped
-        // (adding their zeros would turn a -0 sum into +0)
+        if constexpr (KP > 1) {
+          // Partial inputs: the exact sum of the partials (and the residual),
+          // rounded once -- to the residual dtype, or to float32 without a
+          // residual.  Every slot is added, the unused ones as -0 (see the
+          // loads).  One element at a time, so that a single accumulator is
+          // live and each slot's words die as they are used.
+          float hr[U];
 #pragma unroll
-        for (int k = 1; k < KP; ++k) {
-          if (k < a.num_parts) {
-            float pf[U];
-            unpack<XD, U>(xw[s][c][k], pf);
+          for (int i = 0; i < U; ++i) {
+            ExactSum acc;
+            acc.init(element<XD>(xw[s][c][0], i));
 #pragma unroll
-            for (int i = 0; i < U; ++i) xf[i] += pf[i];
+            for (int k = 1; k < KP; ++k) acc.add(element<XD>(xw[s][c][k], i));
+            if constexpr (HAS_RES) {
+              acc.add(element<RD>(rw[s][c], i));
+              hr[i] = round_exact_sum<RD == kBF16>(acc);  // bf16: nearest even of this below
+            } else {
+              hr[i] = round_exact_sum<false>(acc);
+            }
           }
-        }
-        if constexpr (HAS_RES) {
-          float rf[U], sum[U];
+          if constexpr (HAS_RES) {
+            uint32_t hw[RW];
+            pack<RD, U>(hr, hw);
+            unpack<RD, U>(hw, h[s][c]);
+            buffer_store_words<RW * 4>(ror, elem_of(s, c) * RB, hw);
+          } else {
+#pragma unroll
+            for (int i = 0; i < U; ++i) h[s][c][i] = hr[i];
+          }
+        } else if constexpr (HAS_RES) {
+          float xf[U], rf[U], sum[U];
+          unpack<XD, U>(xw[s][c][0], xf);
           unpack<RD, U>(rw[s][c], rf);
 #pragma unroll
           for (int i = 0; i < U; ++i) sum[i] = xf[i] + rf[i];
@@ -211,12 +258,11 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(NV, KP, QS)))) void rows_ker
           unpack<RD, U>(hw, h[s][c]);
           buffer_store_words<RW * 4>(ror, elem_of(s, c) * RB, hw);
         } else {
-#pragma unroll
-          for (int i = 0; i < U; ++i) h[s][c][i] = xf[i];
+          unpack<XD, U>(xw[s][c][0], h[s][c]);
         }
 #pragma unroll
         for (int i = 0; i < U; ++i) ss += h[s][c][i] * h[s][c][i];
-        if constexpr (QUANT) {
+        if constexpr (QUANT && !LATE_W) {
           float wf[U];
           unpack<WD, U>(ww[s][c], wf);
 #pragma unroll
@@ -224,6 +270,29 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(NV, KP, QS)))) void rows_ker
             // (1 + w) h as one fused multiply-add w h + h: a single rounding
             h[s][c][i] = BIAS ? __builtin_fmaf(wf[i], h[s][c][i], h[s][c][i]) : wf[i] * h[s][c][i];
             if constexpr (QS == kQRow) mx = __builtin_fmaxf(mx, __builtin_fabsf(h[s][c][i]));
+          }
+        }
+      }
+    }
+
+    if constexpr (LATE_W) {
+#pragma unroll
+      for (int s = 0; s < NV; ++s) {
+#pragma unroll
+        for (int c = 0; c < SUB; ++c) buffer_load_words<WW * 4, false>(wr, elem_of(s, c) * WB, ww[s][c]);
+      }
+      if constexpr (QUANT) {
+#pragma unroll
+        for (int s = 0; s < NV; ++s) {
+#pragma unroll
+          for (int c = 0; c < SUB; ++c) {
+            float wf[U];
+            unpack<WD, U>(ww[s][c], wf);
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+              h[s][c][i] = BIAS ? __builtin_fmaf(wf[i], h[s][c][i], h[s][c][i]) : wf[i] * h[s][c][i];
+              if constexpr (QS == kQRow) mx = __builtin_fmaxf(mx, __builtin_fabsf(h[s][c][i]));
+            }
           }
         }
       }

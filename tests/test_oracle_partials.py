@@ -157,7 +157,7 @@ def test_exact_sum_recipe_makes_float32_sums_exact(x_dtype):
     prefix sum in slot order is exact, and torch's float32 sum equals the oracle's."""
     wl = W.PartialsWorkload(name="t", rows=16, hidden=1024, num_partials=8, x_dtype=x_dtype, res_dtype=None,
                             w_dtype="bf16", out_dtype="bf16", part_dist=W.Dist(0.0, 0.5), res_dist=None,
-                            w_dist=W.Dist(1.0, 0.1), weight_plus_one=False, eps=1e-6)
+                            w_dist=W.Dist(1.0, 0.1), weight_plus_one=False, eps=1e-6, exact_sum=True)
     inp = W.generate_partials(wl, seed=4)
     vals = [O.decode(p, x_dtype) for p in inp["partials"]]
     nz = np.abs(np.concatenate([v[v != 0] for v in vals]))

@@ -1,10 +1,12 @@
 """GPU parity of the partial-input entry point (rmsnorm_fwd_partials) against the oracle.
 
-Inputs come from ``workloads.generate_partials``.  Under its exact-sum recipe
-every float32 prefix sum of the partials is exact, so the kernel's sum order
-cannot show and the single-input rules apply (updated residual bit-exact,
-outputs to ``oracle.compare``'s tolerances).  General float32 partials are
-judged against the error bound of a float32 sum (``tests.gpu_util.partials_bounds``).
+Inputs come from ``workloads.generate_partials`` as plain draws (general
+inputs), plus one case of its exact-sum recipe and hand-made rows that put
+the exact sum where a float32 sum in slot order rounds differently: on or
+next to a rounding midpoint, under cancellation, and across wide magnitude
+spans.  The kernel must return the exact sum rounded once: the updated
+residual bit-exact, the outputs to ``oracle.compare``'s tolerances, every
+output scheme included.
 """
 
 import numpy as np
@@ -24,7 +26,7 @@ def _announce(msg):
     print(f"\n[case] {msg}", flush=True)
 
 
-def _wl(rows, hidden, k, x="bf16", res="f32", w="bf16", out="bf16", bias=False, exact=True, eps=1e-6,
+def _wl(rows, hidden, k, x="bf16", res="f32", w="bf16", out="bf16", bias=False, exact=False, eps=1e-6,
         part_std=0.5):
     return WL.PartialsWorkload(
         name="t", rows=rows, hidden=hidden, num_partials=k, x_dtype=x, res_dtype=res, w_dtype=w, out_dtype=out,
@@ -62,7 +64,7 @@ def judge(wl, inputs, r, rows=None, ref=None):
     scale = None if r.scale is None else to_host(r.scale)[sel]
     amax = None if r.amax is None else to_host(r.amax)[sel]
     return judge_partials_rows(sub, wl.x_dtype, wl.res_dtype, wl.w_dtype, wl.out_dtype, wl.eps, wl.weight_plus_one,
-                               out, res_out, scale, amax, exact_sum=wl.exact_sum, ref=ref)
+                               out, res_out, scale, amax, ref=ref)
 
 
 def test_workload_small():
@@ -105,7 +107,7 @@ def test_block_scaled_full_size_sampled():
     sub = {"partials": [p[rows] for p in inp["partials"]], "residual": inp["residual"][rows], "weight": inp["weight"]}
     rep = judge_partials_rows(sub, wl.x_dtype, wl.res_dtype, wl.w_dtype, "fp4_e2m1", wl.eps, wl.weight_plus_one,
                               to_host(r.out)[rows], to_host(r.residual_out)[rows], to_host(r.scale)[rows],
-                              to_host(r.amax)[rows], exact_sum=wl.exact_sum, scale_scheme="mx32")
+                              to_host(r.amax)[rows], scale_scheme="mx32")
     assert rep["ok"], rep
 
 CASES = [  # (x, res, w, out, bias)
@@ -152,13 +154,93 @@ def test_every_launch_variant(k, x, out):
 
 
 @pytest.mark.parametrize("x,k,res,out", [("f32", 8, "f32", "f32"), ("f32", 8, "f32", "bf16"), ("f32", 3, None, "f32"),
-                                         ("bf16", 5, "bf16", "bf16"), ("bf16", 8, "f32", "bf16")])
-def test_inexact_float32_sums_within_bound(x, k, res, out):
-    """General partials (no exact-sum recipe): each float32 addition may round."""
-    wl = _wl(64, 2048, k, x, res, "bf16", out, exact=False, part_std=1.0)
-    _announce(f"partials inexact {x} k={k} res={res} out={out}")
+                                         ("bf16", 5, "bf16", "bf16"), ("bf16", 8, "f32", "bf16"),
+                                         ("f32", 4, "f32", "fp8_e4m3fn"), ("bf16", 6, "bf16", "fp8_e4m3fn")])
+def test_wide_float32_partials(x, k, res, out):
+    """Partials N(0, 1) in float32: their float32 sum in slot order rounds at
+    most additions, so only an exact sum gives the oracle's bits."""
+    wl = _wl(64, 2048, k, x, res, "bf16", out, part_std=1.0)
+    _announce(f"partials general {x} k={k} res={res} out={out}")
     inp = WL.generate_partials(wl, seed=11)
     rep = judge(wl, inp, run_partials(wl, inp))
+    assert rep["ok"], rep
+
+
+def test_exact_sum_recipe():
+    """The narrowed inputs of the exact-sum recipe (every float32 prefix sum exact)."""
+    wl = _wl(64, 8192, 8, exact=True)
+    _announce("partials exact-sum recipe")
+    inp = WL.generate_partials(wl, seed=12)
+    rep = judge(wl, inp, run_partials(wl, inp))
+    assert rep["ok"], rep
+
+
+def _bf16_bits(vals):
+    bits = np.asarray(vals, dtype=np.float32).view(np.uint32)
+    assert (bits & 0xFFFF == 0).all(), "hazard terms must be bfloat16 values"
+    return (bits >> 16).astype(np.uint16)
+
+
+# Rows of (partials..., residual) terms, each chosen so that the exact sum and
+# a float32 sum in slot order round differently (or to exercise signed zeros):
+HAZARDS_F32_RES = [
+    # exact sum just above the float32 midpoint 1 + 2^-24: rounds up to 1 + 2^-23
+    ([1.0, 2.0 ** -24, 2.0 ** -60], 0.0),
+    ([1.0, 2.0 ** -24, -(2.0 ** -60)], 0.0),          # just below it: 1
+    ([1.0, 2.0 ** -24, 0.0], 0.0),                    # on it: nearest even, 1
+    ([1.0 + 2.0 ** -7, 2.0 ** -24, 0.0], 2.0 ** -22),  # the residual carries a float32 bit
+    ([-1.0, -(2.0 ** -24), -(2.0 ** -70)], 0.0),       # negative side, away from zero
+    ([2.0 ** 60, 1.0, -(2.0 ** 60)], 0.5),             # cancellation: 1.5
+    ([2.0 ** 40, 3.0, -(2.0 ** 40), 2.0 ** -30], 0.0), # 3 + 2^-30
+    ([-0.0, -0.0, -0.0], -0.0),                        # every term -0: -0
+    ([-0.0, 0.0, -0.0], -0.0),                         # a +0 term: +0
+    ([2.0 ** 30, 2.0 ** -30, -(2.0 ** 30), 2.0 ** -36], 2.0 ** -37),  # small terms survive cancellation
+]
+
+
+@pytest.mark.parametrize("res_dtype", ["f32", "bf16", None])
+@pytest.mark.parametrize("out,scheme", [("bf16", "row"), ("f32", "row"), ("fp8_e4m3fn", "row"), ("fp4_e2m1", "mx32")])
+def test_rounding_hazards(res_dtype, out, scheme):
+    """Hand-made terms where a float32 sum in slot order would round the
+    updated residual (or the normalized sum) differently from the exact sum."""
+    H, K = 128, 4
+    rows = len(HAZARDS_F32_RES) + 2
+    wl = _wl(rows, H, K, "bf16", res_dtype, "bf16", out, part_std=1.0)
+    inp = WL.generate_partials(wl, seed=21)
+    # one hazard per row, placed at a different column of each row; the other
+    # columns keep their random draws
+    for r, (terms, rv) in enumerate(HAZARDS_F32_RES):
+        col = (r * 37) % H
+        terms = list(terms) + [-0.0] * (K - len(terms))  # -0 leaves every sum unchanged
+        for k, t in enumerate(_bf16_bits(terms)):
+            inp["partials"][k][r, col] = t
+        if res_dtype == "f32":
+            inp["residual"][r, col] = np.float32(rv)
+        elif res_dtype == "bf16":
+            inp["residual"][r, col] = _bf16_bits([rv])[0]
+    # the bf16 residual's own midpoint hazard: 1 + 2^-8 (+ a tiny term) in the last rows
+    if res_dtype == "bf16":
+        for r, tiny in ((rows - 2, 2.0 ** -40), (rows - 1, 0.0)):
+            for k, t in enumerate(_bf16_bits([1.0, 2.0 ** -8, tiny, -0.0])):
+                inp["partials"][k][r, 5] = t
+            inp["residual"][r, 5] = 0
+    _announce(f"partials rounding hazards res={res_dtype} out={out}/{scheme}")
+    ref = oracle_ref(wl, inp)
+    ts = None
+    if scheme == "nv16":
+        from tests.gpu_util import nvfp4_tensor_scale
+        ts = nvfp4_tensor_scale(ref["y"])
+    parts = [to_dev(p, "bf16") for p in inp["partials"]]
+    res = None if res_dtype is None else to_dev(inp["residual"], res_dtype)
+    r = R.fused_partials_add_rmsnorm(parts, res, to_dev(inp["weight"], "bf16"), wl.eps,
+                                     out_dtype=TORCH_DTYPES[out], scale_scheme=scheme, tensor_scale=ts,
+                                     return_amax=out in ("fp8_e4m3fn", "fp4_e2m1"))
+    torch.cuda.synchronize()
+    rep = judge_partials_rows(inp, "bf16", res_dtype, "bf16", out, wl.eps, False, to_host(r.out),
+                              None if r.residual_out is None else to_host(r.residual_out),
+                              None if r.scale is None else to_host(r.scale),
+                              None if r.amax is None else to_host(r.amax), ref=ref, scale_scheme=scheme,
+                              tensor_scale=ts)
     assert rep["ok"], rep
 
 

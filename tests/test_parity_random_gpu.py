@@ -221,7 +221,7 @@ def _partials_cases(n=32, seed=77):
         hmax = (16384 if x == "bf16" else 8192) if k > 1 else 4096
         hidden = g * int(rng.integers(1, min(hmax, 6144) // g + 1))
         rows = int(rng.integers(1, 40))
-        exact = bool(rng.random() < 0.75) or out not in ("bf16", "f32")
+        exact = bool(rng.random() < 0.25)  # a quarter on the exact-sum recipe's narrowed inputs
         cases.append((i, x, res, w, out, scheme, bool(rng.integers(2)), k, hidden, rows, exact,
                       int(rng.integers(1 << 30))))
     return cases
@@ -229,8 +229,9 @@ def _partials_cases(n=32, seed=77):
 
 @pytest.mark.parametrize("case", _partials_cases(), ids=lambda c: f"p{c[0]}")
 def test_random_partials(case):
-    """Random partial-input calls; exact-sum inputs judged like single-input rows,
-    general ones against the float32 summation bound (bf16 / f32 outputs)."""
+    """Random partial-input calls, judged like single-input rows: the updated
+    residual is the exact sum rounded once (bit-exact), every output scheme
+    within its usual tolerance."""
     from tests.gpu_util import judge_partials_rows
 
     i, x, res, w, out, scheme, b, k, hidden, rows, exact, seed = case
@@ -272,5 +273,5 @@ def test_random_partials(case):
     rep = judge_partials_rows(inputs, x, res, w, out, wl.eps, b, to_host(r.out),
                               None if r.residual_out is None else to_host(r.residual_out),
                               None if r.scale is None else to_host(r.scale), None if r.amax is None else to_host(r.amax),
-                              exact_sum=exact, scale_scheme=scheme, tensor_scale=ts)
+                              scale_scheme=scheme, tensor_scale=ts)
     assert rep["ok"], rep
