@@ -195,7 +195,10 @@ rn_status rmsnorm_fwd_ex(const void* x, const void* residual, const void* weight
                          int64_t rows, int64_t hidden, float eps, uint32_t flags, void* stream);
 
 /* As rmsnorm_fwd_ex, with an explicit launch configuration instead of the
- * selector's (for tuning and for testing every kernel variant).  cfg->kernel
+ * selector's (for tuning and for testing every kernel variant).  The launch
+ * shape is the set of knobs the "Prefill & decode specialization" section of
+ * "CuTeDSL at Perplexity" varies (vector width, warps per block, one row per
+ * block or per warp); this entry point fixes them by hand.  cfg->kernel
  * must be RN_KERNEL_ROWS; waves_per_row in 1..16, vecs_per_lane in {1,2,4,8},
  * 64 * waves_per_row * vecs_per_lane * vec >= hidden, 1 <= grid <= rows;
  * block_threads, lanes_per_row and rows_per_lane are derived and ignored. */
@@ -251,7 +254,8 @@ rn_status rmsnorm_fwd_partials(const void* const* partials, int32_t num_partials
                                uint32_t flags, void* stream);
 
 /* As rmsnorm_fwd_partials with an explicit launch configuration (the rules of
- * rmsnorm_fwd_config; vecs_per_lane at most 2 when num_partials > 1). */
+ * rmsnorm_fwd_config, whose launch shape follows "Prefill & decode
+ * specialization"; vecs_per_lane at most 2 when num_partials > 1). */
 rn_status rmsnorm_fwd_partials_config(const void* const* partials, int32_t num_partials, const void* residual,
                                       const void* weight, void* out, void* residual_out, void* out_scale,
                                       float* out_amax, const float* tensor_scale, int64_t rows, int64_t hidden,
@@ -279,7 +283,10 @@ rn_status qknorm_fwd(const void* q, const void* k, const void* q_weight, const v
                      int64_t k_token_stride, float eps, uint32_t flags, void* stream);
 
 /* As qknorm_fwd, with an explicit launch configuration (for tuning and for
- * testing every variant): cfg->kernel must be RN_KERNEL_HEADS, rows_per_lane
+ * testing every variant).  The "QK Norm" section sizes its kernel by head_dim
+ * (threads per head, heads per block); "Prefill & decode specialization"
+ * describes the same kind of shape choice for the row norms.  Here
+ * cfg->kernel must be RN_KERNEL_HEADS, rows_per_lane
  * 1, 2 or 4, block_threads 64, 128 or 256; the grid is derived from those and
  * cfg's other fields are ignored. */
 rn_status qknorm_fwd_config(const void* q, const void* k, const void* q_weight, const void* k_weight,
@@ -318,27 +325,43 @@ rn_status qknorm_fwd_config(const void* q, const void* k, const void* q_weight, 
 rn_status silu_mul_fwd(const void* x, void* out, void* out_scale, float* out_amax, const float* tensor_scale,
                        int64_t rows, int64_t d, uint32_t flags, void* stream);
 
-/* As silu_mul_fwd with an explicit launch configuration (as rmsnorm_fwd_config). */
+/* As silu_mul_fwd with an explicit launch configuration (as rmsnorm_fwd_config;
+ * the launch shapes of "Prefill & decode specialization" applied to the
+ * activation rows). */
 rn_status silu_mul_fwd_config(const void* x, void* out, void* out_scale, float* out_amax,
                               const float* tensor_scale, int64_t rows, int64_t d, uint32_t flags,
                               const rn_launch_config* cfg, void* stream);
 
-/* Host-only: the launch configuration silu_mul_fwd would use. */
+/* Host-only: the launch configuration silu_mul_fwd would use: the selector of
+ * rmsnorm_query_config (below) applied to the activation rows, with its own
+ * measured table. */
 rn_status silu_mul_query_config(int64_t rows, int64_t d, uint32_t flags, int32_t num_cus,
                                 rn_launch_config* cfg);
 
 /* Host-only: the launch configuration rmsnorm_fwd would use for these sizes on
  * a device with num_cus compute units (num_cus <= 0: query the current device);
  * has_residual says whether the call passes a residual (its dtype bits are then
- * read from flags). */
+ * read from flags).  This is the selector of "Prefill & decode specialization"
+ * ("CuTeDSL at Perplexity"): the widest vector per lane first, then the warps
+ * per row, a decode shape with one warp per row when the rows are few, and a
+ * cap on warps per block that the page benchmarks; the compute-unit count
+ * plays the part of the SM count that, per "Blackwell support", the host-side
+ * launcher knows and sizes the grid by. */
 rn_status rmsnorm_query_config(int64_t rows, int64_t hidden, uint32_t flags, int32_t has_residual,
                                int32_t num_cus, rn_launch_config* cfg);
 
-/* The launch configuration rmsnorm_fwd_partials would use (host only when num_cus > 0). */
+/* The launch configuration rmsnorm_fwd_partials would use (host only when
+ * num_cus > 0): the selector of rmsnorm_query_config ("Prefill & decode
+ * specialization"; the compute-unit count as in "Blackwell support") for the
+ * partial-input kernels, with its own measured table. */
 rn_status rmsnorm_partials_query_config(int64_t rows, int64_t hidden, int32_t num_partials, uint32_t flags,
                                         int32_t has_residual, int32_t num_cus, rn_launch_config* cfg);
 
-/* Host-only: the launch configuration qknorm_fwd would use. */
+/* Host-only: the launch configuration qknorm_fwd would use: lanes per head
+ * from head_dim as in the "QK Norm" section's kernel, heads per lane group and
+ * the grid from the token count against the compute units, following the
+ * shape selection of "Prefill & decode specialization" (the host knows the
+ * compute-unit count, as the SM count in "Blackwell support"). */
 rn_status qknorm_query_config(int64_t tokens, int32_t num_q_heads, int32_t num_k_heads,
                               int32_t head_dim, uint32_t flags, int32_t num_cus,
                               rn_launch_config* cfg);

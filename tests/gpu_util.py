@@ -63,8 +63,9 @@ def judge_rows(inputs: dict, x_dtype: str, res_dtype, w_dtype: str, out_dtype: s
 
 
 def judge_y(y: np.ndarray, out_dtype: str, out: np.ndarray, scale=None, amax=None,
-            scale_scheme: str = "row", tensor_scale=None) -> dict:
-    """Judge an output tensor (host bits) against the exact pre-rounding values y [rows, n]."""
+            scale_scheme: str = "row", tensor_scale=None, f32_abs_floor: float = C.F32_ABS_FLOOR) -> dict:
+    """Judge an output tensor (host bits) against the exact pre-rounding values y [rows, n]
+    (``f32_abs_floor``: the absolute floor of float32 outputs, wider for SwiGLU's)."""
     rep = {"ok": True}
     if out_dtype == "bf16":
         r = C.check_bf16(out, y)
@@ -72,7 +73,7 @@ def judge_y(y: np.ndarray, out_dtype: str, out: np.ndarray, scale=None, amax=Non
         rep["out_frac_rne"] = float((out == O.bf16_encode(y)).mean())
         rep["ok"] &= r["ok"]
     elif out_dtype == "f32":
-        r = C.check_f32(out, y)
+        r = C.check_f32(out, y, abs_floor=f32_abs_floor)
         rep["out"] = r
         rep["ok"] &= r["ok"]
     elif scale_scheme in ("row", "group128"):

@@ -91,8 +91,17 @@ def test_f32_acceptance_rule_underflow_floor():
     # relative 1e-5 in the normal range ...
     assert C.check_f32(np.array([1.0 + 2e-6]), np.array([1.0]))["ok"]
     assert not C.check_f32(np.array([1.0 + 2e-5]), np.array([1.0]))["ok"]
-    # ... and the smallest normal float32 as the bound below it: an exact value
-    # of 1e-67 rounds to 0 in float32, which must be accepted; 1e-30 must not.
+    # ... and four subnormal quanta (4 * 2^-149) absolute below it: an exact
+    # value of 1e-67 rounds to 0 in float32, which must be accepted, and so
+    # must a correctly rounded subnormal; 0 for a subnormal of 3e-40 must not
+    # (about 2e5 quanta), nor 1e-30
+    q = 2.0 ** -149
     assert C.check_f32(np.array([0.0]), np.array([1e-67]))["ok"]
-    assert C.check_f32(np.array([-0.0]), np.array([-3e-40]))["ok"]
+    assert C.check_f32(np.array([0.0]), np.array([2.5 * q]))["ok"]
+    assert C.check_f32(np.array([1234 * q]), np.array([1236.9 * q]))["ok"]
+    assert not C.check_f32(np.array([1234 * q]), np.array([1239 * q]))["ok"]
+    assert not C.check_f32(np.array([-0.0]), np.array([-3e-40]))["ok"]
     assert not C.check_f32(np.array([0.0]), np.array([1e-30]))["ok"]
+    # the SwiGLU float32 output's wider floor, 2^-126, accepts 0 for that subnormal
+    assert C.check_f32(np.array([-0.0]), np.array([-3e-40]), abs_floor=C.SILU_F32_ABS_FLOOR)["ok"]
+    assert not C.check_f32(np.array([0.0]), np.array([1e-30]), abs_floor=C.SILU_F32_ABS_FLOOR)["ok"]

@@ -533,7 +533,8 @@ def judge_act(wl, x_np, r, scale_scheme, rows=None, tensor_scale=None):
     y = ACT.silu_mul_rows(O.decode(x_np[sel], wl.x_dtype), wl.d)
     scale = None if r.scale is None else to_host(r.scale)[sel]
     amax = None if r.amax is None else to_host(r.amax)[sel]
-    rep = judge_y(y, wl.out_dtype, to_host(r.out)[sel], scale, amax, scale_scheme, tensor_scale)
+    rep = judge_y(y, wl.out_dtype, to_host(r.out)[sel], scale, amax, scale_scheme, tensor_scale,
+                  f32_abs_floor=C.SILU_F32_ABS_FLOOR)
     rep["ok"] = rep.pop("y_ok")
     return rep
 

@@ -203,7 +203,7 @@ def test_random_silu_mul(case):
                    tensor_scale=ts, config=cfg)
     torch.cuda.synchronize()
     rep = judge_y(y, out, to_host(r.out), None if r.scale is None else to_host(r.scale),
-                  None if r.amax is None else to_host(r.amax), scheme, ts)
+                  None if r.amax is None else to_host(r.amax), scheme, ts, f32_abs_floor=C.SILU_F32_ABS_FLOOR)
     assert rep["y_ok"], rep
 
 
