@@ -13,16 +13,23 @@ The same line carries:
     bytes measured by rocprofv3 counters when profiles/ holds a counter
     summary taken on this very library build (same sha256), else null;
   * ``cpu_baseline``: the CPU oracle (numpy, float64) timed on a bounded
-    sample of the same workload on this host;
-  * ``secondary``: the other workloads -- decode calls (us/call against an
-    empty kernel launched the same way), per-head QK-norm, the fp8-output
-    prefill with per-row scales, the same prefill with block-scaled
-    outputs (fp8 per-128 scales, MXFP8, MXFP4, NVFP4), the sum of 8 partial
-    inputs in front of the add (one GPU's share of a tensor-parallel
-    reduce-scatter; bf16 and MXFP4 out, and a 64-token decode call), and the
-    SiLU-and-mul activation (bf16, MXFP8, MXFP4,
-    NVFP4 out) (GB/s, with rotating buffer sets larger than the 256 MB
-    Infinity Cache so that every call streams from HBM).
+    sample of the same workload, one process per host core (``cores``), and
+    ``cpu_baseline_1core`` the same in one process;
+  * ``decode``: the metric's second half, us/call of the decode workloads
+    (8 x 1024 and 256 x 4096, and an 8-partial 64-token call) against an
+    empty kernel launched the same way: in a HIP graph, eagerly from a native
+    loop through the C ABI, and eagerly from Python through the package's
+    prepared call;
+  * ``secondary``: the streaming lines in compact form -- per-head QK-norm
+    (and the same heads through the rows kernel), one GPU's 2048-row share of
+    the headline, the fp8-output prefill with per-row scales, the same
+    prefill with block-scaled outputs (fp8 per-128 scales, MXFP8, MXFP4,
+    NVFP4), the exact sum of 8 partial inputs in front of the add (one GPU's
+    share of a tensor-parallel reduce-scatter; bf16 and MXFP4 out), and the
+    SiLU-and-mul activation (bf16, MXFP8, MXFP4, NVFP4 out): us/call, GB/s,
+    fraction of peak, the same-size copy and the counter traffic ratio, with
+    rotating buffer sets larger than the 256 MB Infinity Cache so that every
+    call streams from HBM.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
 """
@@ -130,7 +137,7 @@ class RowCall:
     def __init__(self, wl, inputs, sets: int = 1, scale_scheme: str = "row", config=None):
         import torch
         from residual_add_rmsnorm_rows_amd import _lib as L
-        from tests.gpu_util import TORCH_DTYPES, to_dev
+        from workloads.device import TORCH_DTYPES, to_dev
 
         self.wl = wl
         quant = wl.out_dtype in ("fp8_e4m3fn", "fp4_e2m1")
@@ -305,6 +312,14 @@ def decode_metrics(name: str) -> dict:
     eager_empty = time_stream_loop(empty, 2000, 100) * 1000.0
     graph = time_graph_loop(call)
     graph_empty = time_graph_loop(empty)
+    # the package's prepared call (arguments marshalled once), eager from Python
+    from workloads.device import to_dev
+
+    inp = WL.generate_rownorm(wl, seed=0)
+    prepared = R.prepare_fused_add_rmsnorm(to_dev(inp["x"], wl.x_dtype), to_dev(inp["residual"], wl.res_dtype),
+                                           to_dev(inp["weight"], wl.w_dtype), wl.eps,
+                                           weight_plus_one=wl.weight_plus_one)
+    py_eager = time_stream_loop(lambda stream: prepared(), 2000, 100) * 1000.0
     # the one-wave-per-row decode shape (the whole row in one wave64's
     # registers, no LDS, no barrier), timed the same way for comparison
     vec = 8 if wl.x_dtype == "bf16" else 4
@@ -322,6 +337,7 @@ def decode_metrics(name: str) -> dict:
         "ratio_eager": round(eager / eager_empty, 3),
         "us_per_call_graph": round(graph, 3), "empty_us_per_call_graph": round(graph_empty, 3),
         "ratio_graph": round(graph / graph_empty, 3),
+        "us_per_call_python_prepared": round(py_eager, 3), "ratio_python_prepared": round(py_eager / eager_empty, 3),
         "one_wave_per_row": {"vecs_per_lane": cfg.vecs_per_lane, "us_per_call_graph": round(graph_one, 3),
                              "ratio_graph": round(graph_one / graph_empty, 3)},
         "algorithmic_bytes": rownorm_bytes(wl),
@@ -360,7 +376,7 @@ def qknorm_metrics(steps: int, warmup: int, sets: int = 8) -> dict:
 
     import workloads as WL
     from residual_add_rmsnorm_rows_amd import _lib as L
-    from tests.gpu_util import to_dev
+    from workloads.device import to_dev
 
     wl = WL.WORKLOADS["qknorm_4096x32x128"]
     inp = WL.generate_qknorm(wl, seed=0)
@@ -407,7 +423,7 @@ class PartialsCall:
 
         import workloads as WL
         from residual_add_rmsnorm_rows_amd import _lib as L
-        from tests.gpu_util import TORCH_DTYPES, to_dev
+        from workloads.device import TORCH_DTYPES, to_dev
 
         self.wl = wl
         inp = WL.generate_partials(wl, seed=0)
@@ -501,7 +517,7 @@ def act_metrics(steps: int, warmup: int, out_dtype: str = "bf16", scale_scheme: 
 
     import workloads as WL
     from residual_add_rmsnorm_rows_amd import _lib as L
-    from tests.gpu_util import TORCH_DTYPES, to_dev
+    from workloads.device import TORCH_DTYPES, to_dev
 
     wl = WL.WORKLOADS["silu_mul_8192x14336"]
     x0 = to_dev(WL.generate_act(wl, seed=0), wl.x_dtype)
@@ -542,6 +558,95 @@ def act_metrics(steps: int, warmup: int, out_dtype: str = "bf16", scale_scheme: 
             "us_per_call": round(ms * 1000, 3), "algorithmic_bytes": b,
             "GBps": round(b / (ms * 1e-3) / 1e9, 1), "frac_of_peak": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "buffer_sets": sets, "warmup": warmup, "launch_us": spread}
+
+
+def qknorm_vs_rows_metrics(steps: int, warmup: int, sets: int = 8) -> dict:
+    """The per-head QK-norm kernel against the rows kernel on the same data:
+    4096 tokens x 32 heads x 128 as qknorm_fwd, and as rmsnorm_fwd over its
+    [131072, 128] row view (no residual, bf16 in and out), timed interleaved.
+    The two write the same bits (a GPU parity test checks this)."""
+    import torch
+
+    import workloads as WL
+    import residual_add_rmsnorm_rows_amd as R
+    from residual_add_rmsnorm_rows_amd import _lib as L
+    from workloads.device import to_dev
+
+    wl = WL.WORKLOADS["qknorm_4096x32x128"]
+    inp = WL.generate_qknorm(wl, seed=0)
+    q0 = to_dev(inp["q"].reshape(wl.tokens, -1), wl.dtype)
+    w = to_dev(inp["q_weight"], wl.w_dtype)
+    bufs = [(q0 if i == 0 else q0.clone(), torch.empty_like(q0)) for i in range(sets)]
+    lib = L.lib()
+    qflags = L.DTYPE_CODES[wl.dtype] | (L.DTYPE_CODES[wl.w_dtype] << L.RN_FLAGS_W_SHIFT)
+    rflags = L.make_flags(wl.dtype, None, wl.w_dtype, wl.dtype, False)
+    rows = wl.tokens * wl.num_q_heads
+    state = {"i": 0}
+
+    def nxt():
+        b = bufs[state["i"]]
+        state["i"] = (state["i"] + 1) % sets
+        return b
+
+    def qk(stream):
+        q, o = nxt()
+        st = lib.qknorm_fwd(q.data_ptr(), None, w.data_ptr(), None, o.data_ptr(), None, wl.tokens, wl.num_q_heads,
+                            0, wl.head_dim, 0, 0, wl.eps, qflags, stream)
+        if st != 0:
+            L.check(st)
+
+    def rows_call(stream):
+        q, o = nxt()
+        st = lib.rmsnorm_fwd(q.data_ptr(), None, w.data_ptr(), o.data_ptr(), None, None, rows, wl.head_dim, wl.eps,
+                             rflags, stream)
+        if st != 0:
+            L.check(st)
+
+    t_qk, t_rows = [], []
+    for _ in range(3):
+        t_qk.append(time_stream_loop(qk, steps, warmup) * 1000.0)
+        t_rows.append(time_stream_loop(rows_call, steps, warmup) * 1000.0)
+    b = qknorm_bytes(wl)
+    uq, ur = min(t_qk), min(t_rows)
+    sel = R.query_config(rows, wl.head_dim, x_dtype=wl.dtype, res_dtype=None, w_dtype=wl.w_dtype,
+                         out_dtype=wl.dtype, num_cus=0)
+    return {"qknorm_us": round(uq, 3), "qknorm_GBps": round(b / uq / 1e3, 1),
+            "rows_kernel_us": round(ur, 3), "rows_kernel_GBps": round(b / ur / 1e3, 1),
+            "rows_kernel_launch": f"{sel['waves_per_row']}x{sel['vecs_per_lane']}",
+            "rows_over_qknorm_time": round(ur / uq, 3),
+            "pages_figure": "2-3x for the specialized QK-norm over a regular RMS-norm kernel (NVIDIA fleet; "
+                            "context only)"}
+
+
+def compact_stream(e: dict) -> dict:
+    """The figures of a streaming line kept in the JSON line."""
+    out = {"us": e["us_per_call"], "GBps": e["GBps"], "frac": e["frac_of_peak"]}
+    if "launch_us" in e:
+        out["launch_us_p50"] = e["launch_us"]["p50"]
+    if "copy_ceiling" in e:
+        out["copy_GBps"] = e["copy_ceiling"]["GBps"]
+        out["vs_copy"] = e["copy_ceiling"]["value_over_ceiling"]
+    if e.get("traffic_over_algorithmic") is not None:
+        out["traffic_ratio"] = e["traffic_over_algorithmic"]
+    return out
+
+
+def compact_decode(e: dict) -> dict:
+    """Decode us/call against an empty launch: graph, C-ABI eager (native loop)
+    and the package's prepared call (Python loop)."""
+    out = {"launch": f"{e['launch']['waves_per_row']}x{e['launch']['vecs_per_lane']}",
+           "graph_us": e["us_per_call_graph"], "empty_graph_us": e["empty_us_per_call_graph"],
+           "graph_ratio": e["ratio_graph"]}
+    c = e.get("c_abi_eager")
+    if c and "us_per_call" in c:
+        out.update({"c_abi_eager_us": c["us_per_call"], "empty_eager_us": c["empty_us_per_call"],
+                    "c_abi_eager_ratio": c["ratio"]})
+    if "us_per_call_python_prepared" in e:
+        out.update({"python_prepared_us": e["us_per_call_python_prepared"],
+                    "python_prepared_ratio": e["ratio_python_prepared"]})
+    if "one_wave_per_row" in e:
+        out["one_wave_per_row_graph_ratio"] = e["one_wave_per_row"]["ratio_graph"]
+    return out
 
 
 def host_cpu() -> dict:
@@ -618,13 +723,24 @@ def _oracle_worker(args):
     return done, time.perf_counter() - t0
 
 
-def cpu_baseline_parallel(wl, budget_s: float = 8.0, max_procs: int = 8) -> dict:
-    """The same oracle in one process per host core (at most `max_procs`), each on
-    its own rows; the rate is the sum of the processes' rates."""
+def host_cores(cap: int = 16) -> int:
+    """The host cores this process may run on (its CPU affinity), at most `cap`:
+    the GPU machines give one GPU's job a share of 16 CPUs whatever the machine has."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(cap, n))
+
+
+def cpu_baseline_parallel(wl, budget_s: float = 8.0, procs: int = 0) -> dict:
+    """The same oracle in one process per host core (`procs`, default every core
+    this process may use, up to 16), each on its own rows; the rate is the sum
+    of the processes' rates."""
     from concurrent.futures import ProcessPoolExecutor
     import multiprocessing as mp
 
-    n = max(1, min(max_procs, os.cpu_count() or 1))
+    n = procs or host_cores()
     with ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn")) as ex:
         parts = list(ex.map(_oracle_worker, [(wl.name, 64 * i, budget_s) for i in range(n)]))
     rate = sum(rownorm_bytes(wl, rows=r) / t for r, t in parts)
@@ -662,7 +778,7 @@ def main() -> int:
     # touches the GPU (no process is started from one that has initialised it).
     cpu_parallel = None
     if not args.no_cpu_baseline:
-        log("cpu baseline (oracle), one process per host core (at most 8)")
+        log(f"cpu baseline (oracle), one process per host core ({host_cores()})")
         cpu_parallel = cpu_baseline_parallel(WL.WORKLOADS[MAIN])
     # likewise the native decode-latency driver (its own GPU process, run to completion first)
     native = {}
@@ -752,13 +868,17 @@ def main() -> int:
         torch.cuda.empty_cache()
     if not args.no_secondary:
         sec = {}
+        decode = {}
         for name in () if args.no_decode else ("decode_8x1024", "decode_256x4096"):
             log(f"decode {name}")
-            sec[name] = decode_metrics(name)
+            d = decode_metrics(name)
             if name in native:
-                sec[name]["c_abi_eager"] = native[name]
+                d["c_abi_eager"] = native[name]
+            decode[name] = d
         log("qknorm_4096x32x128")
         sec["qknorm_4096x32x128"] = qknorm_metrics(args.steps * 4, args.warmup)
+        log("qknorm_fwd against rmsnorm_fwd on the same 4096 x 32 x 128 heads")
+        qk_vs_rows = qknorm_vs_rows_metrics(args.steps * 4, args.warmup)
         log("one GPU's share of the headline step over 8 GPUs (2048 x 8192)")
         sec["prefill_16384x8192_share_of_8"] = stream_metrics(MAIN, args.steps * 4, args.warmup, sets=3, rows=2048)
         log("prefill_fp8_8192x7168")
@@ -778,7 +898,7 @@ def main() -> int:
                                                              out_dtype="fp4_e2m1", scale_scheme="mx32")
         if not args.no_decode:
             log("partials_decode_8x64x8192")
-            sec["partials_decode_8x64x8192"] = partials_decode_metrics("partials_decode_8x64x8192")
+            decode["partials_decode_8x64x8192"] = partials_decode_metrics("partials_decode_8x64x8192")
         log("silu_mul_8192x14336")
         # the quantized variants do more arithmetic per byte; the GPU's power
         # management lowers clocks for a few ms after such a load starts, so
@@ -796,12 +916,30 @@ def main() -> int:
         for name, entry in sec.items():
             if "GBps" in entry:
                 attach_traffic(name, entry)
-        result["secondary"] = sec
+        # decode us/call (the metric's second half) right after the headline
+        # figures; the streaming lines in compact form
+        if decode:
+            result["decode"] = {k: compact_decode(v) for k, v in decode.items()}
+        result["secondary"] = {k: compact_stream(v) for k, v in sec.items()}
+        result["secondary"]["qknorm_vs_rows_4096x32x128"] = qk_vs_rows
     if not args.no_cpu_baseline:
-        log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(wl)
+        log("cpu baseline (oracle), one process")
+        one = cpu_baseline(wl)
         if cpu_parallel is not None:
-            result["cpu_baseline_parallel"] = cpu_parallel
+            result["cpu_baseline"] = cpu_parallel
+            result["cpu_baseline_1core"] = {k: one[k] for k in ("value", "unit", "cores", "sample")}
+        else:
+            result["cpu_baseline"] = one
+    # a closing summary on stderr (the end of a run's log): headline and decode ratios
+    log(f"headline {MAIN}: {result['value']} GB/s = {result['roofline']['frac']:.4f} of 8 TB/s, "
+        f"{result['ceiling']['value_over_ceiling']:.3f} of the same-run copy")
+    for k, v in result.get("decode", {}).items():
+        log(f"decode {k} ({v['launch']}): graph {v['graph_us']} us = {v['graph_ratio']}x empty; "
+            f"C-ABI eager {v.get('c_abi_eager_us')} us = {v.get('c_abi_eager_ratio')}x; "
+            f"Python prepared {v.get('python_prepared_us')} us = {v.get('python_prepared_ratio')}x")
+    order = ["metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
+             "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline", "decode", "ceiling"]
+    result = {**{k: result[k] for k in order if k in result}, **{k: v for k, v in result.items() if k not in order}}
     print(json.dumps(result), flush=True)
     return 0
 

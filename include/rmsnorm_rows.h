@@ -173,8 +173,10 @@ typedef struct rn_launch_config {
  * fp8 reading: amax and every y_i are float32 values computed from the same
  * products, scale = amax / 448 is an IEEE float32 division, an all-zero row has
  * scale 0 and all-zero codes.
- * Aliasing: out may equal x (in place) and residual_out may equal residual;
- * any other overlap is undefined, and out == residual_out is rejected.
+ * Aliasing: out may equal x (in place) when both have the same element width
+ * (else RN_ERR_INVALID_ARG: a narrower or wider out row would overlap other
+ * rows of x still being read), and residual_out may equal residual; any other
+ * overlap is undefined, and out == residual_out is rejected.
  * Range: the sum of squares accumulates in float32, as in the page's
  * listing.  So the tolerances hold while h^2 stays a float32 value
  * (|h| below about 1.8e19), and while the mean square does not underflow
@@ -244,9 +246,10 @@ rn_status rmsnorm_fwd_config(const void* x, const void* residual, const void* we
  * running sums stay below float32's largest value.  Outside that range the
  * sum can be off in its last bit.
  * num_partials == 1 is rmsnorm_fwd_ex on x = partials[0].
- * Aliasing: out may equal one of the partials (in place); residual_out may
- * equal residual; residual_out equal to a partial or to out is rejected; any
- * other overlap is undefined.
+ * Aliasing: out may equal one of the partials (in place) when out has the
+ * partials' element width (else RN_ERR_INVALID_ARG); residual_out may equal
+ * residual; residual_out equal to a partial or to out is rejected; any other
+ * overlap is undefined.
  */
 rn_status rmsnorm_fwd_partials(const void* const* partials, int32_t num_partials, const void* residual,
                                const void* weight, void* out, void* residual_out, void* out_scale,
@@ -314,13 +317,14 @@ rn_status qknorm_fwd_config(const void* q, const void* k, const void* q_weight, 
  *   (as for rmsnorm_fwd); other bits must be zero.  out may not overlap x.
  *
  * Range: the results hold the outputs' tolerances while |gate * up| is below
- * float32's largest value (about 3.4e38).  Past it, bf16 / fp8 / fp4 outputs
- * of a negative gate become -inf or NaN even where silu(gate) * up is finite,
- * because the product gate * up is formed first.  For f32 outputs,
- * exp(-|gate|) is a float32 subnormal beyond |gate| = 87.3 and carries fewer
- * bits.  The relative error then grows, which shows only where the result is
- * still a normal number (|up| above about 1e36).  Activations are many orders
- * of magnitude inside these limits.
+ * float32's largest value (about 3.4e38).  Past it, outputs of a negative gate
+ * become -inf or NaN even where silu(gate) * up is finite, because the product
+ * gate * up is formed first.  Below gate = -87.3 the factor 1 / (1 + exp(-gate))
+ * (bf16 / fp8 / fp4 outputs) or exp(-|gate|) (f32 outputs) is a float32
+ * subnormal and carries fewer bits, and for bf16 / fp8 / fp4 outputs it is
+ * zero below gate = -103; this shows only where the result is still a normal
+ * number (|up| above about 1e35).  Activations are many orders of magnitude
+ * inside these limits.
  */
 rn_status silu_mul_fwd(const void* x, void* out, void* out_scale, float* out_amax, const float* tensor_scale,
                        int64_t rows, int64_t d, uint32_t flags, void* stream);

@@ -24,6 +24,8 @@ __all__ = [
     "NormOutput",
     "fused_add_rmsnorm",
     "fused_partials_add_rmsnorm",
+    "prepare_fused_add_rmsnorm",
+    "PreparedCall",
     "rmsnorm",
     "qk_norm",
     "silu_mul",
@@ -167,8 +169,8 @@ def fused_add_rmsnorm(x: torch.Tensor, residual: Optional[torch.Tensor], weight:
     [rows, H/32]) or ``"nv16"`` (fp4; E4M3FN ``torch.float8_e4m3fn``
     [rows, H/16], with the per-tensor float32 ``tensor_scale``: a
     one-element device tensor, or a number copied to the device).
-    ``out=x`` and ``residual_out=residual`` are allowed (in place).
-    ``config`` forces a launch configuration.
+    ``out=x`` (when out has x's dtype width) and ``residual_out=residual`` are
+    allowed (in place).  ``config`` forces a launch configuration.
     """
     rows, H, out, residual_out, scale, amax, ts, flags = _rows_setup(
         x, residual, weight, weight_plus_one, out_dtype, out, residual_out, return_amax, scale_scheme, tensor_scale)
@@ -183,20 +185,73 @@ def fused_add_rmsnorm(x: torch.Tensor, residual: Optional[torch.Tensor], weight:
     return NormOutput(out, residual_out, scale, amax)
 
 
+class PreparedCall:
+    """One C-ABI call with every argument marshalled once.
+
+    For decode-sized calls issued many times on the same buffers (a serving
+    loop outside graph capture): the tensors, flags, sizes and stream are
+    converted to ctypes values when the object is built, so a call is a
+    single foreign-function call with no tensor inspection, output
+    allocation or stream lookup.  ``result`` holds the output tensors, which
+    every call overwrites.  The object keeps its tensors alive.
+    """
+
+    def __init__(self, fn, args, result, keep):
+        self._fn = fn
+        self._args = args
+        self.result = result
+        self._keep = keep
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st:
+            check(st)
+        return self.result
+
+
+def prepare_fused_add_rmsnorm(x: torch.Tensor, residual: Optional[torch.Tensor], weight: torch.Tensor,
+                              eps: float, *, weight_plus_one: bool = False,
+                              out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                              residual_out: Optional[torch.Tensor] = None, return_amax: bool = False,
+                              scale_scheme: str = "row", tensor_scale=None,
+                              stream: Optional[torch.cuda.Stream] = None) -> PreparedCall:
+    """``fused_add_rmsnorm`` over fixed buffers, prepared once and called many
+    times: ``call = prepare_fused_add_rmsnorm(...); call()`` launches it on
+    ``stream`` (default: the current stream when prepared) and returns the
+    ``NormOutput`` it writes.  The arguments and checks are those of
+    ``fused_add_rmsnorm``; the library re-checks them on every call."""
+    rows, H, out, residual_out, scale, amax, ts, flags = _rows_setup(
+        x, residual, weight, weight_plus_one, out_dtype, out, residual_out, return_amax, scale_scheme, tensor_scale)
+    s = stream.cuda_stream if stream is not None else _stream(x.device)
+    vp = ctypes.c_void_p
+    args = (vp(_p(x)), vp(_p(residual)), vp(_p(weight)), vp(_p(out)), vp(_p(residual_out)), vp(_p(scale)),
+            vp(_p(amax)), vp(_p(ts)), ctypes.c_int64(rows), ctypes.c_int64(H), ctypes.c_float(eps),
+            ctypes.c_uint32(flags), vp(s))
+    # the library's entry point without per-call argument conversion: every
+    # argument above is already a ctypes value of the declared C type
+    fn = ctypes.CFUNCTYPE(ctypes.c_int, *_lib._SIGNATURES["rmsnorm_fwd_ex"][0])(
+        ctypes.cast(lib().rmsnorm_fwd_ex, ctypes.c_void_p).value)
+    result = NormOutput(out, residual_out, scale, amax)
+    call = PreparedCall(fn, args, result, (x, residual, weight, ts))
+    call()  # a first call: any argument error is raised here
+    return call
+
+
 def fused_partials_add_rmsnorm(partials: Sequence[torch.Tensor], residual: Optional[torch.Tensor],
                                weight: torch.Tensor, eps: float, *, weight_plus_one: bool = False,
                                out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
                                residual_out: Optional[torch.Tensor] = None, return_amax: bool = False,
                                scale_scheme: str = "row", tensor_scale=None,
                                config: Optional[LaunchConfig] = None) -> NormOutput:
-    """``fused_add_rmsnorm`` with ``x = partials[0] + partials[1] + ...``, summed
-    in the kernel in float32 (slot order) without an intermediate rounding.
+    """``fused_add_rmsnorm`` with ``x = partials[0] + partials[1] + ...``: the
+    kernel takes the exact sum of the partials (and the residual) and rounds it
+    once, to the residual dtype (or float32 without a residual).
 
     ``partials`` holds 1..8 tensors of one shape and dtype (bf16 or f32): the
     partial outputs of a row-parallel projection, or the branch outputs of a
     parallel residual block.  Outputs, scale schemes and ``tensor_scale`` are
     those of ``fused_add_rmsnorm``.  ``out`` may be one of the partials (in
-    place).
+    place) when it has the partials' dtype width.
     """
     parts = list(partials)
     if not 1 <= len(parts) <= _lib.MAX_PARTIALS:

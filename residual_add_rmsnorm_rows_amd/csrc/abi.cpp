@@ -36,6 +36,9 @@ rn_status device_cus(int* num_cus) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Storage bits of an output element.
+int out_bits(int dt) { return dt == kBF16 ? 16 : dt == kF32 ? 32 : dt == kFP8 ? 8 : 4; }
+
 const void* pick_row_kernel(const RowKey& k) {
   const void* (*const pickers[])(const RowKey&) = {
       pick_row_kernel_bf16_bf16,    pick_row_kernel_bf16_f32,     pick_row_kernel_bf16_fp8_row,
@@ -126,6 +129,15 @@ rn_status rows_entry(bool parts_form, const void* x, const void* const* parts, i
     return fail(RN_ERR_INVALID_ARG, "residual and residual_out must both be given or both be NULL");
   if (residual_out != nullptr && residual_out == out)
     return fail(RN_ERR_INVALID_ARG, "out and residual_out must be different buffers");
+  // In place (out over x or over a partial) only with equal element widths:
+  // otherwise row r of out covers other rows of the input, which other
+  // workgroups may still be reading.
+  if (out_bits(key.out) != (key.x == kBF16 ? 16 : 32)) {
+    bool aliased = !parts_form && out == x;
+    for (int32_t k = 0; parts_form && k < num_parts; ++k) aliased |= out == parts[k];
+    if (aliased)
+      return fail(RN_ERR_INVALID_ARG, "out may equal x (or a partial) only when both have the same element width");
+  }
   const void* ptrs16[] = {x, residual, weight, out, residual_out};
   for (const void* p : ptrs16)
     if (p != nullptr && !aligned(p, 16)) return fail(RN_ERR_MISALIGNED, "tensor pointer %p is not 16-byte aligned", p);

@@ -36,12 +36,13 @@ constexpr int act_max(int a, int b) { return a > b ? a : b; }
 // Otherwise (bf16 / fp8 / fp4 outputs, whose rounding step is 2^-8 relative
 // or coarser): silu(g) u = g u / (1 + exp(-g)) evaluated as
 //     t = 2^(-g log2(e) - 64) = exp(-g) 2^-64,
-//     silu(g) u = (g u) * rcp(t + 2^-64) * 2^-64,
+//     silu(g) u = (g u) * (rcp(t + 2^-64) * 2^-64),
 // with the hardware exp2 and reciprocal (v_exp_f32, v_rcp_f32).  The 2^-64
-// offset keeps every intermediate a normal float32 for -132 < g (where the
-// plain form's exp(-g) overflows from g < -88, and its result, though tiny,
-// can still be a normal number once multiplied by u); the final power-of-two
-// multiply is exact and rounds only where the result itself is subnormal.
+// offset keeps t finite for -132 < g, where the plain form's exp(-g)
+// overflows from g < -88.  The factor in parentheses is 1 / (1 + exp(-g)):
+// in [1/2, 1) for g >= 0, so g u is never scaled up; for g < -87.3 it falls
+// into float32's subnormal range (fewer bits) and below g = -103 to zero,
+// where the true result is a normal number only if |u| exceeds about 1e35.
 // The argument's rounding near 64 costs about 2^-17 relative, far below those
 // formats' steps, in 7 instructions per element without compare or select.
 template <bool ACCURATE>
@@ -52,7 +53,7 @@ __device__ __forceinline__ float silu_mul_f32(float g, float u) {
     return (g * (g >= 0.f ? r : e * r)) * u;
   } else {
     const float t = __builtin_amdgcn_exp2f(__builtin_fmaf(g, -1.4426950408889634f, -64.0f));
-    return ((g * u) * __builtin_amdgcn_rcpf(t + 0x1p-64f)) * 0x1p-64f;
+    return (g * u) * (__builtin_amdgcn_rcpf(t + 0x1p-64f) * 0x1p-64f);
   }
 }
 

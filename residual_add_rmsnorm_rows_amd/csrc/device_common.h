@@ -329,7 +329,8 @@ __device__ __forceinline__ float group_reduce(float v) {
 // correctly rounded sums: proved algorithms using rounding to odd", IEEE
 // Transactions on Computers, 2008).  Double has 53 bits, float32 24, bfloat16
 // 8, so double -> float32 needs one such step and double -> bfloat16 two.
-// When every error of a wave is zero, s is the exact sum and no step is needed.
+// When no addition but the last one rounded in a wave, the last float32
+// addition alone rounds the exact sum (no step is needed for float32).
 // ---------------------------------------------------------------------------
 
 struct ExactSum {
@@ -360,25 +361,42 @@ __device__ __forceinline__ float step_ulp(float f, bool away) {
   return __uint_as_float(away ? b + 1u : b - 1u);
 }
 
-// The exact sum rounded once to float32: to nearest even (ODD == false), or
-// to odd (ODD == true) for a later nearest-even rounding to bfloat16.
+// The exact sum of the accumulated terms and a last term v, rounded once to
+// float32: to nearest even (ODD == false), or to odd (ODD == true) for a later
+// nearest-even rounding to bfloat16.
+//
+// When no earlier addition of the wave rounded (c == 0 in every lane), the
+// exact sum is s + v: float32 addition rounds it correctly by itself, and
+// only the round-to-odd form needs that addition's error.  Otherwise the
+// double-precision path: t + r == s + c exactly (a double TwoSum), t rounded
+// to odd at double precision stands for s + c in any rounding to 51 bits or
+// fewer.
 template <bool ODD>
-__device__ __forceinline__ float round_exact_sum(const ExactSum& a) {
-  if (__builtin_amdgcn_ballot_w64(a.c != 0.0) == 0) return a.s;  // every addition of the wave was exact
-  // t + r == s + c exactly; t rounded to odd at double precision stands for
-  // s + c in any rounding to 51 bits or fewer.  t != 0 whenever r != 0.
-  const double sd = static_cast<double>(a.s);
-  double t = sd + a.c;
-  const double bv = t - sd;
-  const double r = (sd - (t - bv)) + (a.c - bv);
-  if (a.c == 0.0) t = sd;  // sd + 0 would turn a -0 sum into +0
-  if (r != 0.0 && (__double_as_longlong(t) & 1) == 0) t = step_ulp(t, (r > 0.0) == (t > 0.0));
-  float f = static_cast<float>(t);  // nearest even of the exact sum
+__device__ __forceinline__ float add_last_and_round(const ExactSum& a, float v) {
+  const float t = a.s + v;
+  const float bv = t - a.s;
+  if (__builtin_amdgcn_ballot_w64(a.c != 0.0) == 0) {  // every earlier addition of the wave was exact
+    if constexpr (!ODD) {
+      return t;
+    } else {
+      const float e = (a.s - (t - bv)) + (v - bv);
+      // t != 0 when e != 0: a zero sum of two floats is exact
+      return e != 0.f && (__float_as_uint(t) & 1u) == 0 ? step_ulp(t, (e > 0.f) == (t > 0.f)) : t;
+    }
+  }
+  const double c = a.c + static_cast<double>((a.s - (t - bv)) + (v - bv));
+  const double sd = static_cast<double>(t);
+  double u = sd + c;
+  const double bu = u - sd;
+  const double r = (sd - (u - bu)) + (c - bu);
+  if (c == 0.0) u = sd;  // sd + 0 would turn a -0 sum into +0
+  if (r != 0.0 && (__double_as_longlong(u) & 1) == 0) u = step_ulp(u, (r > 0.0) == (u > 0.0));
+  float f = static_cast<float>(u);  // nearest even of the exact sum
   if constexpr (ODD) {
     // nonzero: the terms are multiples of 2^-149, so a nonzero sum is at
     // least 2^-149 in magnitude and never rounds to zero
     const double back = static_cast<double>(f);
-    if (back != t && (__float_as_uint(f) & 1u) == 0) f = step_ulp(f, (t > back) == (f > 0.f));
+    if (back != u && (__float_as_uint(f) & 1u) == 0) f = step_ulp(f, (u > back) == (f > 0.f));
   }
   return f;
 }

@@ -229,13 +229,14 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(NV, KP, QS)))) void rows_ker
           for (int i = 0; i < U; ++i) {
             ExactSum acc;
             acc.init(element<XD>(xw[s][c][0], i));
+            constexpr int LAST = HAS_RES ? KP : KP - 1;  // slots added before the last term
 #pragma unroll
-            for (int k = 1; k < KP; ++k) acc.add(element<XD>(xw[s][c][k], i));
+            for (int k = 1; k < LAST; ++k) acc.add(element<XD>(xw[s][c][k], i));
             if constexpr (HAS_RES) {
-              acc.add(element<RD>(rw[s][c], i));
-              hr[i] = round_exact_sum<RD == kBF16>(acc);  // bf16: nearest even of this below
+              // bf16: rounded to odd here, to nearest even by the pack below
+              hr[i] = add_last_and_round<RD == kBF16>(acc, element<RD>(rw[s][c], i));
             } else {
-              hr[i] = round_exact_sum<false>(acc);
+              hr[i] = add_last_and_round<false>(acc, element<XD>(xw[s][c][KP - 1], i));
             }
           }
           if constexpr (HAS_RES) {

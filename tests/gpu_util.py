@@ -1,36 +1,15 @@
-"""Moving the generator's numpy arrays to the device and results back, and
-judging a fused add+RMSNorm result against the oracle.  Test code only."""
+"""Judging a fused add+RMSNorm result against the oracle (and, re-exported
+from ``workloads.device``, moving arrays to the device and back).  Test code
+only."""
 
 from __future__ import annotations
 
 import numpy as np
-import torch
 
 from oracle import blockquant as BQ
 from oracle import compare as C
 from oracle import rownorm as O
-
-TORCH_DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8_e4m3fn": torch.float8_e4m3fn,
-                "fp4_e2m1": torch.float4_e2m1fn_x2}
-
-
-def to_dev(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
-    if dtype == "bf16":
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
-    if dtype == "f32":
-        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
-    raise ValueError(dtype)
-
-
-def to_host(t: torch.Tensor) -> np.ndarray:
-    """Stored bits/values: bf16 -> uint16 bits, f32 -> float32, fp8 / fp4 pairs / E8M0 -> uint8."""
-    if t.dtype == torch.bfloat16:
-        return t.view(torch.int16).cpu().numpy().view(np.uint16)
-    if t.dtype in (torch.float8_e4m3fn, torch.float4_e2m1fn_x2, torch.float8_e8m0fnu):
-        return t.view(torch.uint8).cpu().numpy()
-    if t.dtype == torch.float32:
-        return t.cpu().numpy()
-    raise ValueError(t.dtype)
+from workloads.device import TORCH_DTYPES, to_dev, to_host  # noqa: F401  (re-exported for the tests)
 
 
 def nvfp4_tensor_scale(y: np.ndarray) -> float:

@@ -49,6 +49,7 @@ def test_abi_version_and_status_strings(lib):
 
 FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced (every call below fails first)
 BF = L.make_flags("bf16", "bf16", "bf16", "bf16", False)
+FP4_MX_FLAGS = L.make_flags("bf16", "bf16", "bf16", "fp4_e2m1", False, "mx32")
 
 
 def _fwd(lib, x=FAKE, res=FAKE, w=FAKE, out=FAKE + 0x1000, res_out=FAKE + 0x2000, scale=None, amax=None,
@@ -79,6 +80,12 @@ def _fwd(lib, x=FAKE, res=FAKE, w=FAKE, out=FAKE + 0x1000, res_out=FAKE + 0x2000
     (dict(x=FAKE + 8), L.RN_ERR_MISALIGNED),
     (dict(res_out=FAKE + 0x2004), L.RN_ERR_MISALIGNED),
     (dict(flags=L.make_flags("bf16", "bf16", "bf16", "fp8_e4m3fn", False), scale=FAKE + 2), L.RN_ERR_MISALIGNED),
+    # in place only with equal element widths (a wider or narrower out row overlaps other rows of x)
+    (dict(out=FAKE, flags=L.make_flags("bf16", "bf16", "bf16", "f32", False)), L.RN_ERR_INVALID_ARG),
+    (dict(out=FAKE, flags=L.make_flags("f32", "f32", "bf16", "bf16", False)), L.RN_ERR_INVALID_ARG),
+    (dict(out=FAKE, flags=L.make_flags("bf16", "bf16", "bf16", "fp8_e4m3fn", False), scale=FAKE + 0x3000),
+     L.RN_ERR_INVALID_ARG),
+    (dict(out=FAKE, flags=FP4_MX_FLAGS, scale=FAKE + 0x3000), L.RN_ERR_INVALID_ARG),
 ])
 def test_rmsnorm_rejects_before_any_hip_call(lib, kw, status):
     assert _fwd(lib, **kw) == status
@@ -391,6 +398,9 @@ def _pfwd(lib, parts=(P0, P1), n=None, res=FAKE, w=FAKE, out=FAKE + 0x1000, res_
     (dict(flags=_qflags("fp4_e2m1", "mx32"), scale=FAKE + 0x3000, ts=FAKE + 0x4000), L.RN_ERR_INVALID_ARG),
     (dict(flags=L.make_flags("bf16", "bf16", "bf16", "fp8_e4m3fn", False)), L.RN_ERR_INVALID_ARG),  # no scale
     (dict(eps=float("nan")), L.RN_ERR_INVALID_ARG),
+    (dict(out=P1, flags=L.make_flags("bf16", "bf16", "bf16", "fp8_e4m3fn", False), scale=FAKE + 0x3000),
+     L.RN_ERR_INVALID_ARG),  # in place over a partial of another width
+    (dict(out=P0, flags=L.make_flags("bf16", "f32", "bf16", "f32", False)), L.RN_ERR_INVALID_ARG),
 ])
 def test_partials_reject_before_any_hip_call(lib, kw, status):
     assert _pfwd(lib, **kw) == status

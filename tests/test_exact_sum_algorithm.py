@@ -19,38 +19,58 @@ from oracle import rownorm as O
 f32, f64 = np.float32, np.float64
 
 
-def replay(terms, odd=False):
+def _two_sum_err(a, b, t):
+    bv = t - a
+    return (a - (t - bv)) + (b - bv)
+
+
+def _step(bits, step, away):
+    return bits + np.where(step, np.where(away, 1, -1), 0)
+
+
+def replay(terms, odd=False, wave_fast_path=True):
     """The kernels' sum of float32 terms, rounded once to float32 (nearest
-    even), or to odd at float32 precision when ``odd`` (for bf16 targets)."""
+    even), or to odd at float32 precision when ``odd`` (for bf16 targets).
+
+    Every term but the last goes through float32 TwoSum with the error added
+    to a double; the last term is added in float32, and where no earlier
+    addition rounded, that sum (made odd with its own error for ``odd``) is
+    the result.  Elsewhere the double path: a double TwoSum of the float32
+    sum and all the errors, round-to-odd at double precision, then float32
+    (and round-to-odd at float32 for ``odd``).  ``wave_fast_path=False``
+    takes the double path for every element (the kernels take it for a whole
+    wave when any of its lanes needs it); both give the same bits.
+    """
     with np.errstate(over="ignore", invalid="ignore"):
         s = np.asarray(terms[0], dtype=f32).copy()
         c = np.zeros(s.shape, dtype=f64)
-        for v in terms[1:]:
+        for v in terms[1:-1]:
             v = np.asarray(v, dtype=f32)
             t = s + v
-            bv = t - s
-            e = (s - (t - bv)) + (v - bv)
+            c = c + _two_sum_err(s, v, t).astype(f64)
             s = t
-            c = c + e.astype(f64)
-        sd = s.astype(f64)
-        t = sd + c
-        bv = t - sd
-        r = (sd - (t - bv)) + (c - bv)
-        t = np.where(c == 0, sd, t)
-        bits = t.view(np.int64).copy()
-        step = (r != 0) & ((bits & 1) == 0)
-        away = (r > 0) == (t > 0)
-        bits += np.where(step, np.where(away, 1, -1), 0)
-        t = bits.view(f64)
-        f = t.astype(f32)
+        v = np.asarray(terms[-1], dtype=f32)
+        t = s + v
+        e = _two_sum_err(s, v, t)
+        # fast path (no earlier rounding)
+        fast = t.copy()
         if odd:
-            back = f.astype(f64)
-            fb = f.view(np.uint32).copy()
-            step = (back != t) & ((fb & 1) == 0)
-            away = (t > back) == (f > 0)
-            fb = (fb.astype(np.int64) + np.where(step, np.where(away, 1, -1), 0)).astype(np.uint32)
-            f = fb.view(f32)
-        return f
+            tb = fast.view(np.uint32).astype(np.int64)
+            fast = _step(tb, (e != 0) & ((tb & 1) == 0), (e > 0) == (t > 0)).astype(np.uint32).view(f32)
+        # double path
+        cc = c + e.astype(f64)
+        sd = t.astype(f64)
+        u = sd + cc
+        r = _two_sum_err(sd, cc, u)
+        u = np.where(cc == 0, sd, u)
+        ub = u.view(np.int64).copy()
+        u = _step(ub, (r != 0) & ((ub & 1) == 0), (r > 0) == (u > 0)).view(f64)
+        slow = u.astype(f32)
+        if odd:
+            back = slow.astype(f64)
+            fb = slow.view(np.uint32).astype(np.int64)
+            slow = _step(fb, (back != u) & ((fb & 1) == 0), (u > back) == (slow > 0)).astype(np.uint32).view(f32)
+        return np.where((c == 0) & wave_fast_path, fast, slow)
 
 
 def expected(terms, fmt):
@@ -83,11 +103,13 @@ def test_random_terms_round_like_the_exact_sum(bf16_terms, span):
     rng = np.random.default_rng(span + 1000 * bf16_terms)
     for k in range(2, 10):
         terms = random_terms(rng, 20000, k, bf16_terms, span)
-        got = replay(terms)
-        want = expected(terms, O.F32)
-        assert np.array_equal(got.view(np.uint32), want.astype(f32).view(np.uint32)), k
-        got16 = O.bf16_encode(replay(terms, odd=True).astype(f64))
-        assert np.array_equal(got16, O.bf16_encode(expected(terms, O.BF16))), k
+        want = expected(terms, O.F32).astype(f32).view(np.uint32)
+        want16 = O.bf16_encode(expected(terms, O.BF16))
+        for fast in (True, False):
+            got = replay(terms, wave_fast_path=fast)
+            assert np.array_equal(got.view(np.uint32), want), (k, fast)
+            got16 = O.bf16_encode(replay(terms, odd=True, wave_fast_path=fast).astype(f64))
+            assert np.array_equal(got16, want16), (k, fast)
 
 
 def test_near_midpoints():

@@ -555,6 +555,35 @@ def test_silu_mul_parity(out, scheme, x, rows, d):
     assert rep["ok"], rep
 
 
+# (gate, up) pairs far from the usual activations: products beyond 2^64
+# with a positive gate (silu(g) u close to g u), and negative gates whose
+# result is small but still a normal float32.
+SILU_LARGE = [(2.0 ** 33, 2.0 ** 33), (2.0 ** 40, 2.0 ** 20), (100.0, 2.0 ** 70), (10240.0, 2.0 ** 60),
+              (-20.0, 2.0 ** 60), (-80.0, 2.0 ** 60), (3.5, -(2.0 ** 80)), (0.75, 2.0 ** 100), (-1.5, -(2.0 ** 90))]
+
+
+@pytest.mark.parametrize("out,scheme", ACT_OUTS)
+@pytest.mark.parametrize("x", ["bf16", "f32"])
+def test_silu_mul_large_products(out, scheme, x):
+    """|gate * up| up to 2^100: every intermediate stays finite where the result is."""
+    rows, d = 3, 1024
+    wl = WL.ActWorkload(name="actl", rows=rows, d=d, x_dtype=x, out_dtype=out, x_dist=WL.Dist(0, 1))
+    xn = WL.generate_act(wl, seed=23)
+    vals = np.array(SILU_LARGE, dtype=np.float32)  # every value is a bf16 value too
+    for r in range(rows):
+        cols = (np.arange(len(SILU_LARGE)) * 97 + 13 * r) % d
+        if x == "bf16":
+            xn[r, cols] = (vals[:, 0].view(np.uint32) >> 16).astype(np.uint16)
+            xn[r, d + cols] = (vals[:, 1].view(np.uint32) >> 16).astype(np.uint16)
+        else:
+            xn[r, cols] = vals[:, 0]
+            xn[r, d + cols] = vals[:, 1]
+    _announce(f"silu_mul large products x={x} out={out} scheme={scheme}")
+    ts = act_tensor_scale(wl, xn, scheme)
+    rep = judge_act(wl, xn, run_act(wl, xn, scheme, tensor_scale=ts), scheme, tensor_scale=ts)
+    assert rep["ok"], rep
+
+
 @pytest.mark.parametrize("out,scheme", [("bf16", "row"), ("fp8_e4m3fn", "row"), ("fp4_e2m1", "mx32"),
                                         ("fp4_e2m1", "nv16")])
 def test_silu_mul_every_launch_variant(out, scheme):
