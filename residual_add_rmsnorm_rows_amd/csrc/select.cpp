@@ -152,30 +152,20 @@ static bool rows_variant_ok(int waves, int nv, int64_t nvec, int kp) {
 
 static const int64_t kMaxGrid = 0x7FFFFFFF;
 
-// Partial-input kernels (bf16 partials, f32 residual, bf16 out), measured on
-// MI355X at about 0.6 GB of traffic per call over every variant within two
-// waves of the exact fit at 1 and 2 vectors per lane (three interleaved
-// repetitions): the entries where the exact fit with the fewest vectors per
-// lane lost 2% or more.  Key: partial-input slots (2, 4, 8), hidden size.
-struct TunedParts {
-  int kp;
-  int hidden;
-  int waves, nv;
-};
-static const TunedParts kTunedParts[] = {
-    {2, 7168, 16, 1}, {4, 4096, 4, 2}, {4, 7168, 8, 2}, {4, 8192, 8, 2}, {8, 7168, 8, 2},
-};
-
 // Fastest (waves, vectors per lane) measured on MI355X for prefill-sized row
-// counts with a bf16 weight: each entry won an interleaved sweep of the
-// variants covering at most 1.5 times the row (five repetitions each, then
-// seven for the close calls), scored by the geometric mean of the throughput
-// at 1.2 GB and at 0.4 GB of traffic per call (kernel with nontemporal input
-// loads and output stores).
-// The 4608..6144 wide entries come from a later sweep of six dtype classes
-// at 1536..6144 wide (three repetitions, same score), entered where the
-// winner beat the selector's previous choice by at least 2% (the other
-// winners of that sweep are the rule below select_row_config's tables).
+// counts with a bf16 weight, where they beat the shape the rules below give.
+// Every entry was re-timed against that shape in one interleaved run (five
+// repetitions, median; the geometric mean of the times at 1.2 GB and 0.4 GB
+// of traffic per call) and is kept where it won by at least 2% -- the box-to-
+// box spread.  The shapes of the benchmark's own workloads were also timed
+// at those workloads' sizes (nine interleaved repetitions) and are kept
+// where they won there by at least 1%, that A/B's resolution: 4 x 4 for the
+// 16384 x 8192 prefill with an f32 residual (+2.9%; earlier A/Bs +0.5% to
+// +1.05%; 16 x 1 is within 0.8% of it at 2-16 rows per CU), and 8 x 2 for
+// the 8192 x 7168 fp8 prefill (+1.45%: 8 waves fill a CU's 32 wave slots in
+// 4 workgroups; the exact fit's 7 leave 4 idle).  The re-timing removed 31
+// of 45 entries (17 chose the rules' own shape, 4 were slower than it, 10
+// were within 2%); the 4 x 4 entry is new.
 // Key: x dtype, residual dtype (kNone: no residual), whether the output is
 // quantized (fp8 / fp4), hidden size.
 struct Tuned {
@@ -185,49 +175,28 @@ struct Tuned {
   int waves, nv;
 };
 static const Tuned kTuned[] = {
-    // bf16 x, f32 residual stream, bf16/f32 out
-    {kBF16, kF32, false, 2048, 6, 1},    {kBF16, kF32, false, 4096, 8, 1},
-    {kBF16, kF32, false, 5120, 11, 1},   {kBF16, kF32, false, 7168, 16, 1},
-    {kBF16, kF32, false, 8192, 16, 1},   {kBF16, kF32, false, 12288, 16, 2},
-    {kBF16, kF32, false, 16384, 16, 2},
-    // bf16 x, bf16 residual, bf16/f32 out
-    {kBF16, kBF16, false, 2048, 5, 1},   {kBF16, kBF16, false, 4096, 9, 1},
-    {kBF16, kBF16, false, 5120, 9, 2},   {kBF16, kBF16, false, 7168, 9, 2},
-    {kBF16, kBF16, false, 8192, 16, 1},  {kBF16, kBF16, false, 12288, 16, 2},
-    {kBF16, kBF16, false, 16384, 16, 2},
-    // bf16 x, bf16 residual, fp8/fp4 out
-    {kBF16, kBF16, true, 2048, 4, 1},    {kBF16, kBF16, true, 4096, 8, 1},
-    {kBF16, kBF16, true, 5120, 5, 2},    {kBF16, kBF16, true, 7168, 8, 2},
-    {kBF16, kBF16, true, 8192, 8, 2},    {kBF16, kBF16, true, 12288, 12, 2},
-    {kBF16, kBF16, true, 16384, 8, 4},   {kBF16, kBF16, true, 4608, 5, 2},
-    {kBF16, kBF16, true, 5376, 6, 2},    {kBF16, kBF16, true, 6144, 8, 2},
-    // bf16 x, f32 residual stream, fp8/fp4 out
-    {kBF16, kF32, true, 2048, 5, 1},     {kBF16, kF32, true, 4096, 8, 1},
-    {kBF16, kF32, true, 5120, 8, 2},     {kBF16, kF32, true, 7168, 16, 1},
-    {kBF16, kF32, true, 8192, 16, 1},    {kBF16, kF32, true, 12288, 12, 2},
-    {kBF16, kF32, true, 16384, 8, 4},
-    // bf16 x, no residual, bf16/f32 out
-    {kBF16, kNone, false, 2048, 3, 2},   {kBF16, kNone, false, 4096, 5, 2},
-    {kBF16, kNone, false, 5120, 2, 8},   {kBF16, kNone, false, 7168, 4, 4},
-    {kBF16, kNone, false, 8192, 8, 2},   {kBF16, kNone, false, 12288, 8, 4},
-    {kBF16, kNone, false, 16384, 8, 4},
-    // f32 x, f32 residual, f32/bf16 out
-    {kF32, kF32, false, 2048, 9, 1},     {kF32, kF32, false, 4096, 9, 2},
-    {kF32, kF32, false, 5120, 16, 2},    {kF32, kF32, false, 7168, 11, 4},
-    {kF32, kF32, false, 8192, 12, 4},    {kF32, kF32, false, 12288, 16, 4},
-    {kF32, kF32, false, 16384, 16, 4},
+    {kBF16, kF32, false, 5120, 11, 1}, {kBF16, kF32, false, 7168, 16, 1}, {kBF16, kF32, false, 8192, 4, 4},
+    {kBF16, kF32, false, 12288, 16, 2},
+    {kBF16, kBF16, false, 7168, 9, 2}, {kBF16, kBF16, true, 6144, 8, 2}, {kBF16, kBF16, true, 7168, 8, 2},
+    {kBF16, kF32, true, 7168, 16, 1},
+    {kBF16, kF32, true, 16384, 8, 4}, {kBF16, kNone, false, 2048, 3, 2}, {kBF16, kNone, false, 4096, 5, 2},
+    {kBF16, kNone, false, 12288, 8, 4}, {kBF16, kNone, false, 16384, 8, 4}, {kF32, kF32, false, 4096, 9, 2},
+    {kF32, kF32, false, 5120, 16, 2},
 };
 
 // Mid-size calls (more rows than compute units, at most 16 per CU: chunked
 // prefill, large decode batches): fastest (waves, vectors per lane) measured
-// on MI355X, scored by the geometric mean of a cache-warm call (one buffer
-// set, reused) and a cold one (buffers rotated past the 256 MB Infinity
-// Cache), three interleaved repetitions, at 2, 4, 8 and 16 rows per CU;
-// entered where it beat the streaming-prefill choice by at least 3%.  Fewer
-// waves holding more vectors per lane win here: with at most 16 rows per CU
-// the whole grid is resident at once, and each lane keeps more loads in
-// flight.  Key as kTuned, plus cu_mult: the entry serves rows in
-// ((cu_mult / 2) * CUs, cu_mult * CUs].
+// on MI355X at 2, 4, 8 and 16 rows per CU.  Fewer waves holding more vectors
+// per lane win here: with at most 16 rows per CU the whole grid is resident
+// at once, and each lane keeps more loads in flight.  Every entry was
+// re-timed at 3/4 of its bucket's largest row count against the shape the
+// selector gives without it (kTuned's, else the rules'), in HIP graphs (GPU
+// time; these calls take 3-40 us, where eager launches would time the
+// launch path), scored by the geometric mean of a cache-warm call (one
+// buffer set) and a cold one (buffers rotated past the 256 MB Infinity
+// Cache), five interleaved repetitions; kept where it won by at least 2%
+// (55 of 80; most by 4-28%).  Key as kTuned, plus cu_mult: the entry serves
+// rows in ((cu_mult / 2) * CUs, cu_mult * CUs].
 struct TunedMid {
   int x, res;
   bool fp8;
@@ -236,59 +205,48 @@ struct TunedMid {
   int waves, nv;
 };
 static const TunedMid kTunedMid[] = {
-    {kBF16, kBF16, false, 2048, 2, 2, 2}, {kBF16, kBF16, false, 2048, 4, 2, 2}, {kBF16, kBF16, false, 2048, 8, 1, 4},
-    {kBF16, kBF16, false, 4096, 2, 5, 2}, {kBF16, kBF16, false, 4096, 4, 1, 8}, {kBF16, kBF16, false, 4096, 8, 1, 8},
-    {kBF16, kBF16, false, 5120, 2, 5, 2}, {kBF16, kBF16, false, 5120, 4, 2, 8}, {kBF16, kBF16, false, 5120, 8, 8, 2},
-    {kBF16, kBF16, false, 7168, 2, 7, 2}, {kBF16, kBF16, false, 7168, 4, 2, 8}, {kBF16, kBF16, false, 8192, 2, 8, 2},
-    {kBF16, kBF16, false, 8192, 4, 2, 8}, {kBF16, kBF16, false, 8192, 8, 2, 8}, {kBF16, kBF16, false, 12288, 2, 3, 8},
-    {kBF16, kBF16, false, 12288, 4, 3, 8}, {kBF16, kBF16, false, 16384, 2, 4, 8}, {kBF16, kBF16, false, 16384, 4, 4, 8},
-    {kBF16, kF32, false, 2048, 2, 1, 4}, {kBF16, kF32, false, 2048, 4, 1, 4}, {kBF16, kF32, false, 2048, 8, 1, 4},
-    {kBF16, kF32, false, 2048, 16, 1, 4}, {kBF16, kF32, false, 4096, 2, 1, 8}, {kBF16, kF32, false, 4096, 4, 1, 8},
-    {kBF16, kF32, false, 4096, 8, 1, 8}, {kBF16, kF32, false, 5120, 2, 2, 8}, {kBF16, kF32, false, 5120, 4, 2, 8},
-    {kBF16, kF32, false, 7168, 2, 2, 8}, {kBF16, kF32, false, 7168, 4, 2, 8}, {kBF16, kF32, false, 8192, 2, 2, 8},
-    {kBF16, kF32, false, 12288, 2, 3, 8}, {kBF16, kBF16, true, 2048, 8, 1, 4}, {kBF16, kBF16, true, 5120, 8, 8, 2},
-    {kBF16, kBF16, true, 16384, 2, 4, 8}, {kBF16, kBF16, true, 16384, 4, 16, 2}, {kBF16, kBF16, true, 16384, 8, 16, 2},
-    {kBF16, kF32, true, 2048, 2, 4, 1}, {kBF16, kF32, true, 2048, 4, 1, 4}, {kBF16, kF32, true, 2048, 8, 1, 4},
-    {kBF16, kF32, true, 2048, 16, 4, 1}, {kBF16, kF32, true, 4096, 4, 2, 4}, {kBF16, kF32, true, 4096, 8, 1, 8},
-    {kBF16, kF32, true, 5120, 2, 3, 4}, {kBF16, kF32, true, 5120, 4, 2, 8}, {kBF16, kF32, true, 7168, 2, 4, 4},
+    {kBF16, kBF16, false, 2048, 8, 1, 4}, {kBF16, kBF16, false, 4096, 4, 1, 8}, {kBF16, kBF16, false, 4096, 8, 1, 8},
+    {kBF16, kBF16, false, 5120, 4, 2, 8}, {kBF16, kBF16, false, 5120, 8, 8, 2}, {kBF16, kBF16, false, 7168, 4, 2, 8},
+    {kBF16, kBF16, false, 8192, 2, 8, 2}, {kBF16, kBF16, false, 8192, 4, 2, 8}, {kBF16, kBF16, false, 8192, 8, 2, 8},
+    {kBF16, kBF16, false, 12288, 4, 3, 8}, {kBF16, kBF16, false, 16384, 4, 4, 8}, {kBF16, kF32, false, 2048, 4, 1, 4},
+    {kBF16, kF32, false, 2048, 8, 1, 4}, {kBF16, kF32, false, 4096, 4, 1, 8}, {kBF16, kF32, false, 5120, 4, 2, 8},
+    {kBF16, kF32, false, 7168, 4, 2, 8}, {kBF16, kF32, false, 12288, 2, 3, 8}, {kBF16, kBF16, true, 5120, 8, 8, 2},
+    {kBF16, kBF16, true, 16384, 2, 4, 8}, {kBF16, kF32, true, 2048, 4, 1, 4}, {kBF16, kF32, true, 2048, 8, 1, 4},
+    {kBF16, kF32, true, 4096, 4, 2, 4}, {kBF16, kF32, true, 4096, 8, 1, 8}, {kBF16, kF32, true, 5120, 4, 2, 8},
     {kBF16, kF32, true, 7168, 4, 2, 8}, {kBF16, kF32, true, 8192, 2, 4, 4}, {kBF16, kF32, true, 8192, 4, 2, 8},
-    {kBF16, kF32, true, 12288, 2, 4, 8}, {kBF16, kF32, true, 16384, 2, 4, 8}, {kBF16, kNone, false, 2048, 2, 1, 4},
-    {kBF16, kNone, false, 2048, 4, 1, 4}, {kBF16, kNone, false, 2048, 8, 2, 2}, {kBF16, kNone, false, 2048, 16, 1, 4},
-    {kBF16, kNone, false, 4096, 2, 8, 1}, {kBF16, kNone, false, 4096, 4, 1, 8}, {kBF16, kNone, false, 4096, 8, 1, 8},
-    {kBF16, kNone, false, 5120, 2, 3, 4}, {kBF16, kNone, false, 5120, 4, 5, 2}, {kBF16, kNone, false, 5120, 8, 3, 4},
-    {kBF16, kNone, false, 5120, 16, 5, 2}, {kBF16, kNone, false, 7168, 4, 2, 8}, {kBF16, kNone, false, 8192, 2, 4, 4},
-    {kBF16, kNone, false, 8192, 4, 2, 8}, {kBF16, kNone, false, 8192, 8, 2, 8}, {kBF16, kNone, false, 12288, 2, 3, 8},
-    {kBF16, kNone, false, 12288, 4, 3, 8}, {kBF16, kNone, false, 16384, 2, 4, 8}, {kF32, kF32, false, 2048, 2, 1, 8},
-    {kF32, kF32, false, 2048, 4, 1, 8}, {kF32, kF32, false, 2048, 8, 1, 8}, {kF32, kF32, false, 4096, 2, 2, 8},
-    {kF32, kF32, false, 4096, 4, 2, 8}, {kF32, kF32, false, 4096, 8, 2, 8}, {kF32, kF32, false, 5120, 2, 3, 8},
-    {kF32, kF32, false, 5120, 4, 5, 4}, {kF32, kF32, false, 7168, 2, 4, 8}, {kF32, kF32, false, 7168, 4, 4, 8},
-    {kF32, kF32, false, 8192, 2, 4, 8}, {kF32, kF32, false, 8192, 4, 4, 8},
+    {kBF16, kNone, false, 2048, 2, 1, 4}, {kBF16, kNone, false, 2048, 4, 1, 4}, {kBF16, kNone, false, 2048, 8, 2, 2},
+    {kBF16, kNone, false, 2048, 16, 1, 4}, {kBF16, kNone, false, 4096, 2, 8, 1}, {kBF16, kNone, false, 4096, 4, 1, 8},
+    {kBF16, kNone, false, 4096, 8, 1, 8}, {kBF16, kNone, false, 5120, 2, 3, 4}, {kBF16, kNone, false, 5120, 8, 3, 4},
+    {kBF16, kNone, false, 7168, 4, 2, 8}, {kBF16, kNone, false, 8192, 2, 4, 4}, {kBF16, kNone, false, 8192, 4, 2, 8},
+    {kBF16, kNone, false, 8192, 8, 2, 8}, {kBF16, kNone, false, 12288, 2, 3, 8}, {kBF16, kNone, false, 12288, 4, 3, 8},
+    {kBF16, kNone, false, 16384, 2, 4, 8}, {kF32, kF32, false, 2048, 2, 1, 8}, {kF32, kF32, false, 2048, 4, 1, 8},
+    {kF32, kF32, false, 2048, 8, 1, 8}, {kF32, kF32, false, 4096, 2, 2, 8}, {kF32, kF32, false, 4096, 4, 2, 8},
+    {kF32, kF32, false, 4096, 8, 2, 8}, {kF32, kF32, false, 5120, 2, 3, 8}, {kF32, kF32, false, 5120, 4, 5, 4},
+    {kF32, kF32, false, 7168, 2, 4, 8}, {kF32, kF32, false, 7168, 4, 4, 8}, {kF32, kF32, false, 8192, 2, 4, 8},
+    {kF32, kF32, false, 8192, 4, 4, 8},
 };
 
 // SwiGLU (bf16 x): fastest (waves, vectors per lane) measured on MI355X,
-// scored like kTuned (geometric mean at 1.2 GB and 0.4 GB per call, five
-// interleaved repetitions), entered where it beat the exact fit by more than
-// half a percent.  A later sweep of intermediate sizes 4096-27648 (three
-// repetitions) added 5632, 6144, 8960, 9728 and 27648, where the winner beat
-// the exact fit by 2.4-6.2%.  Output class: 0 bf16 / f32, 1 fp8 (measured
-// with MX scales), 2 fp4 (measured with NVFP4 scales).
+// re-timed like kTuned against the exact fit and kept where it won by at
+// least 2% (15 of 21; fp4 outputs by 4-9%), plus, as for kTuned, the
+// benchmark workload's 14336-wide shapes, which won at its own size
+// (8192 tokens): 13 x 4 for bf16 out (+1.1%), 9 x 4 for fp8 (+1.9%).
+// Output class: 0 bf16 / f32, 1 fp8 (measured with MX scales), 2 fp4
+// (measured with NVFP4 scales).
 struct TunedAct {
   int out_class;
   int d;
   int waves, nv;
 };
 static const TunedAct kTunedAct[] = {
-    {0, 4096, 9, 1},   {0, 8192, 12, 2},  {0, 11008, 14, 2}, {0, 13824, 13, 4},
-    {0, 14336, 13, 4}, {0, 18944, 14, 4}, {0, 28672, 16, 4},
-    {1, 13824, 9, 4},  {1, 14336, 9, 4},  {1, 28672, 8, 8},
-    {2, 8192, 8, 2},   {2, 11008, 6, 4},  {2, 13824, 4, 8},  {2, 14336, 4, 8},
-    {2, 28672, 16, 4},
-    {0, 6144, 13, 1},  {0, 27648, 16, 4}, {2, 5632, 4, 4},   {2, 6144, 6, 2},
-    {2, 8960, 5, 4},   {2, 9728, 6, 4},
+    {0, 14336, 13, 4}, {1, 14336, 9, 4},
+    {0, 4096, 9, 1}, {0, 8192, 12, 2}, {0, 11008, 14, 2}, {0, 18944, 14, 4}, {0, 28672, 16, 4},
+    {1, 13824, 9, 4}, {2, 8192, 8, 2}, {2, 11008, 6, 4}, {2, 13824, 4, 8}, {2, 14336, 4, 8},
+    {0, 6144, 13, 1}, {0, 27648, 16, 4}, {2, 5632, 4, 4}, {2, 8960, 5, 4}, {2, 9728, 6, 4},
 };
 
-// SwiGLU mid-size calls (CUs < rows <= 16 x CUs), measured and entered as
-// kTunedMid (warm/cold geometric mean, at least 3% over kTunedAct's choice).
+// SwiGLU mid-size calls (CUs < rows <= 16 x CUs), re-timed and kept as
+// kTunedMid (27 of 33, against kTunedAct's shape or the exact fit).
 struct TunedActMid {
   int out_class;
   int d;
@@ -296,15 +254,13 @@ struct TunedActMid {
   int waves, nv;
 };
 static const TunedActMid kTunedActMid[] = {
-    {0, 4096, 4, 8, 1}, {0, 4096, 8, 1, 8}, {0, 8192, 2, 8, 2}, {0, 8192, 4, 2, 8},
-    {0, 8192, 8, 8, 2}, {0, 11008, 2, 3, 8}, {0, 11008, 4, 6, 4}, {0, 13824, 2, 4, 8},
-    {0, 13824, 4, 16, 2}, {0, 13824, 8, 16, 2}, {0, 14336, 2, 4, 8}, {0, 14336, 4, 16, 2},
+    {0, 4096, 8, 1, 8}, {0, 8192, 2, 8, 2}, {0, 8192, 4, 2, 8}, {0, 8192, 8, 8, 2},
+    {0, 11008, 4, 6, 4}, {0, 13824, 4, 16, 2}, {0, 13824, 8, 16, 2}, {0, 14336, 4, 16, 2},
     {0, 14336, 8, 16, 2}, {0, 18944, 2, 12, 4}, {1, 11008, 4, 6, 4}, {1, 13824, 2, 16, 2},
-    {1, 13824, 4, 8, 4}, {1, 13824, 8, 8, 4}, {1, 13824, 16, 8, 4}, {1, 14336, 2, 16, 2},
-    {1, 14336, 4, 8, 4}, {1, 14336, 8, 8, 4}, {1, 18944, 2, 12, 4}, {1, 18944, 4, 12, 4},
-    {2, 8192, 2, 16, 1}, {2, 11008, 2, 12, 2}, {2, 13824, 2, 15, 2}, {2, 13824, 4, 7, 4},
-    {2, 13824, 8, 8, 4}, {2, 13824, 16, 8, 4}, {2, 14336, 2, 16, 2}, {2, 14336, 4, 7, 4},
-    {2, 14336, 8, 8, 4},
+    {1, 13824, 4, 8, 4}, {1, 13824, 8, 8, 4}, {1, 13824, 16, 8, 4}, {1, 14336, 4, 8, 4},
+    {1, 18944, 2, 12, 4}, {1, 18944, 4, 12, 4}, {2, 8192, 2, 16, 1}, {2, 11008, 2, 12, 2},
+    {2, 13824, 2, 15, 2}, {2, 13824, 4, 7, 4}, {2, 13824, 8, 8, 4}, {2, 13824, 16, 8, 4},
+    {2, 14336, 2, 16, 2}, {2, 14336, 4, 7, 4}, {2, 14336, 8, 8, 4},
 };
 
 // Launch shape for rows of `hidden` elements: the tabulated (waves, nv) when
@@ -350,8 +306,53 @@ static rn_status select_rows_shape(int64_t rows, int64_t hidden, const RowKey& k
   return RN_OK;
 }
 
+// Partial-input kernels (KP > 1, exact sums).  A sweep of every shape of up
+// to 16 waves and 1-2 vectors per lane on MI355X (2, 4 and 8 bf16 partials;
+// f32 or bf16 residual; bf16, per-row fp8 and MXFP4 outputs; 2048-16384 wide;
+// 8, 64, 256, 512 and 1024 rows and ~0.6 GB prefill calls; 150 cases) found
+// the exact fit at one vector per lane best or within 3% in most cases, and
+// no table needed:
+//   * the exact fit at one vector per lane (two past 16 waves), at every
+//     row count -- the exact sums give a lane more arithmetic than the
+//     single-input kernel, so decode rows spread over up to 16 waves (16 x 1
+//     beat 8 x 2 by 6-13% at 8 and 64 rows x 8192 with 4-8 partials);
+//   * block-scaled outputs past 8 waves, with more rows than CUs: 8 waves
+//     with 2 vectors per lane.  Their kernels take too many registers for
+//     two such workgroups per CU (8 x 2 measured 4-15% faster than 16 x 1
+//     from 512 rows on; 16 x 1 was 6% faster at 256);
+//   * a fit of 9-15 waves with more than 2 rows per CU: 8 waves x 2 vectors
+//     when they hold the row.  Such workgroups leave wave slots of a CU idle
+//     (14 x 1 at 7168 wide ran 9-15% behind 8 x 2 at 1024 rows, 2-6% at
+//     prefill sizes).
+// Against each case's best shape: geometric mean 1.003, worst 1.047 (the
+// replaced table and rules: 1.026 and 1.225).
+static rn_status select_parts_shape(int64_t rows, int64_t hidden, const RowKey& key, int num_cus,
+                                    rn_launch_config* cfg) {
+  if (num_cus < 1) return fail(RN_ERR_INVALID_ARG, "num_cus must be >= 1");
+  const int vec = 16 / (key.x == kBF16 ? 2 : 4);
+  const int64_t nvec = hidden / vec;
+  int64_t w = (nvec + 63) / 64;
+  int nv = 1;
+  if (w > kMaxWavesPerRow) {
+    w = (nvec + 127) / 128;
+    nv = 2;
+  }
+  if (w > kMaxWavesPerRow)
+    return fail(RN_ERR_UNSUPPORTED, "no partial-input variant holds %lld lane vectors", (long long)nvec);
+  const bool block_scaled = (key.out == kFP8 || key.out == kFP4) && key.qs != kQRow;
+  // one vector per lane over 9-16 waves: 8 x 2 holds the row too (nvec <= 1024)
+  if (nv == 1 && w > 8 &&
+      ((block_scaled && rows > num_cus) || (w < kMaxWavesPerRow && rows > 2 * static_cast<int64_t>(num_cus)))) {
+    w = 8;
+    nv = 2;
+  }
+  fill_rows_cfg(vec, static_cast<int>(w), nv, rows, rows < kMaxGrid ? rows : kMaxGrid, cfg);
+  return RN_OK;
+}
+
 rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int num_cus,
                             rn_launch_config* cfg) {
+  if (key.kp > 1) return select_parts_shape(rows, hidden, key, num_cus, cfg);
   int tw = 0, tnv = 0;
   const bool quant = key.out == kFP8 || key.out == kFP4;
   // the tables were measured with a bf16 weight and a single x input
@@ -421,39 +422,7 @@ rn_status select_row_config(int64_t rows, int64_t hidden, const RowKey& key, int
       }
     }
   }
-  if (key.kp > 1 && key.x == kBF16 && num_cus >= 1 && rows > num_cus) {
-    for (const TunedParts& t : kTunedParts) {
-      if (t.kp == key.kp && t.hidden == hidden) {
-        tw = t.waves;
-        tnv = t.nv;
-        break;
-      }
-    }
-  }
-  // Partial inputs from more than half the CUs busy up to 3 rows per CU, where
-  // the whole grid is resident at once: 2 vectors per lane and the fewest
-  // waves (measured 2-14% faster than the decode rule's shape at 256 rows x
-  // 4096 / 8192 wide, 2-8 partials, and up to 11% faster than the exact fit
-  // at 300-700 rows; at 64 rows the decode rule's shape is as fast).
-  if (key.kp > 1 && num_cus >= 1 && 2 * rows > num_cus && rows <= 3 * static_cast<int64_t>(num_cus) &&
-      tw == 0) {
-    const int vec = 16 / (key.x == kBF16 ? 2 : 4);
-    const int64_t w = (hidden / vec + 127) / 128;
-    if (w >= 1 && w <= kMaxWavesPerRow) {
-      fill_rows_cfg(vec, static_cast<int>(w), 2, rows, rows, cfg);
-      return RN_OK;
-    }
-  }
-  const rn_status st = select_rows_shape(rows, hidden, key, num_cus, tw, tnv, true, cfg);
-  // Partial inputs with block-scaled outputs (per-128 fp8, MX, NVFP4): their
-  // kernels take too many registers for two workgroups of more than 8 waves
-  // per CU, so a row of one vector per lane over more than 8 waves runs as
-  // half the waves with 2 vectors per lane (bf16 partials, f32 residual,
-  // 2 and 8 partials, 7168 and 8192 wide: 8 x 2 measured 12-17% faster than
-  // 14-16 x 1; at 4096 wide 8 x 1 and 4 x 2 are within 2%).
-  if (st == RN_OK && key.kp > 1 && key.qs != kQRow && cfg->vecs_per_lane == 1 && cfg->waves_per_row > 8)
-    fill_rows_cfg(cfg->vec, (cfg->waves_per_row + 1) / 2, 2, rows, cfg->grid, cfg);
-  return st;
+  return select_rows_shape(rows, hidden, key, num_cus, tw, tnv, true, cfg);
 }
 
 rn_status check_row_config(int64_t rows, int64_t hidden, const RowKey& key,

@@ -240,8 +240,8 @@ def test_selector_shapes_of_the_workloads():
     c = _cfg(8, 32768)
     assert (c["waves_per_row"], c["vecs_per_lane"]) == (8, 8)
     # prefill: the measured table (bf16 x with an f32 or bf16 residual stream)
-    c3 = _cfg_res(16384, 8192, "f32")
-    assert (c3["waves_per_row"], c3["vecs_per_lane"]) == (16, 1)
+    c3 = _cfg_res(16384, 8192, "f32")  # 4 x 4: +2.9% over 16 x 1 at this size
+    assert (c3["waves_per_row"], c3["vecs_per_lane"]) == (4, 4)
     c5 = _cfg_res(8192, 7168, "bf16", out="fp8_e4m3fn")
     assert (c5["waves_per_row"], c5["vecs_per_lane"]) == (8, 2)
     # outside the table: the exact fit with the fewest vectors per lane
@@ -429,29 +429,29 @@ def test_partials_selector():
                     W, NV = c["waves_per_row"], c["vecs_per_lane"]
                     assert NV in (1, 2) and 1 <= W <= 16 and 64 * W * NV * vec >= hidden, (x, n, hidden, rows, c)
                     assert c["grid"] == rows
-    c = R.query_partials_config(2048, 8192, 8, res_dtype="f32")
-    assert (c["waves_per_row"], c["vecs_per_lane"]) == (16, 1)
-    c = R.query_partials_config(3840, 8192, 4, res_dtype="f32")  # measured: 8 x 2 beats 16 x 1 by 7%
-    assert (c["waves_per_row"], c["vecs_per_lane"]) == (8, 2)
-    c = R.query_partials_config(3072, 7168, 7, res_dtype="f32")  # 8 slots: 8 x 2 beats 14 x 1 by 6%
-    assert (c["waves_per_row"], c["vecs_per_lane"]) == (8, 2)
-    c = R.query_partials_config(256, 4096, 4, res_dtype="f32")  # decode, chip more than half busy: 2 vectors
-    assert (c["waves_per_row"], c["vecs_per_lane"]) == (4, 2)
-    c = R.query_partials_config(32, 8192, 8, res_dtype="f32")  # decode: at most 8 waves
-    assert (c["waves_per_row"], c["vecs_per_lane"]) == (8, 2)
-    # block-scaled outputs: more than 8 waves of one vector run as half the
-    # waves with 2 vectors (measured 12-17% faster); per-row fp8 keeps 16 x 1
+    # the rule (no table): the exact fit at one vector per lane at every row
+    # count; 9-15 waves past 2 rows per CU, and block-scaled outputs past 8
+    # waves with more rows than CUs, as 8 x 2
+    def shape(rows, hidden, n, **kw):
+        c = R.query_partials_config(rows, hidden, n, res_dtype="f32", num_cus=256, **kw)
+        return c["waves_per_row"], c["vecs_per_lane"]
+
+    assert shape(2048, 8192, 8) == (16, 1)
+    assert shape(3840, 8192, 4) == (16, 1)
+    assert shape(3072, 7168, 7) == (8, 2)   # 14 x 1 leaves wave slots idle
+    assert shape(512, 7168, 4) == (14, 1)   # up to 2 rows per CU: the exact fit
+    assert shape(256, 4096, 4) == (8, 1)
+    assert shape(32, 8192, 8) == (16, 1)    # decode: up to 16 waves
+    assert shape(8, 2048, 2) == (4, 1)
+    assert shape(64, 16384, 8) == (16, 2)
     for od, scheme in (("fp8_e4m3fn", "group128"), ("fp8_e4m3fn", "mx32"), ("fp4_e2m1", "mx32"),
                        ("fp4_e2m1", "nv16")):
         for n, hidden in ((8, 8192), (2, 8192), (2, 7168)):
-            c = R.query_partials_config(2048, hidden, n, res_dtype="f32", out_dtype=od, scale_scheme=scheme)
-            assert (c["waves_per_row"], c["vecs_per_lane"]) == (8, 2), (od, scheme, n, hidden, c)
-        c = R.query_partials_config(4096, 4096, 8, res_dtype="f32", out_dtype=od, scale_scheme=scheme)
-        assert (c["waves_per_row"], c["vecs_per_lane"]) == (8, 1)
-        c = R.query_partials_config(2048, 12288, 8, res_dtype="f32", out_dtype=od, scale_scheme=scheme)
-        assert (c["waves_per_row"], c["vecs_per_lane"]) == (12, 2)
-    c = R.query_partials_config(2048, 8192, 8, res_dtype="f32", out_dtype="fp8_e4m3fn")
-    assert (c["waves_per_row"], c["vecs_per_lane"]) == (16, 1)
+            assert shape(2048, hidden, n, out_dtype=od, scale_scheme=scheme) == (8, 2), (od, scheme, n, hidden)
+            assert shape(256, hidden, n, out_dtype=od, scale_scheme=scheme)[1] == 1
+        assert shape(4096, 4096, 8, out_dtype=od, scale_scheme=scheme) == (8, 1)
+        assert shape(2048, 12288, 8, out_dtype=od, scale_scheme=scheme) == (12, 2)
+    assert shape(2048, 8192, 8, out_dtype="fp8_e4m3fn") == (16, 1)
     # one partial is the single-input kernel and its tables
     assert R.query_partials_config(8192, 7168, 1, res_dtype="bf16", out_dtype="fp8_e4m3fn") == \
         R.query_config(8192, 7168, res_dtype="bf16", out_dtype="fp8_e4m3fn")
