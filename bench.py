@@ -620,7 +620,7 @@ def qknorm_vs_rows_metrics(steps: int, warmup: int, sets: int = 8) -> dict:
 
 def compact_stream(e: dict) -> dict:
     """The figures of a streaming line kept in the JSON line."""
-    out = {"us": e["us_per_call"], "GBps": e["GBps"], "frac": e["frac_of_peak"]}
+    out = {"us": e["us_per_call"], "bytes": e["algorithmic_bytes"], "GBps": e["GBps"], "frac": e["frac_of_peak"]}
     if "launch_us" in e:
         out["launch_us_p50"] = e["launch_us"]["p50"]
     if "copy_ceiling" in e:

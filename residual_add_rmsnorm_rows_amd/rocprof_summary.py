@@ -108,9 +108,10 @@ def traffic(fetch_csv: str, write_csv: str, kernel: str, bench_out: str, command
     fetch_b = statistics.mean(fetch_k) * 1024 * fetch_factor
     write_b = statistics.mean(write_k) * 1024 * write_factor
     bench = _last_json(bench_out)
-    if entry:  # a secondary workload of the benchmark
-        alg = bench["secondary"][entry]["algorithmic_bytes"]
-        workload = f"{entry}: {bench['secondary'][entry]['workload']}"
+    if entry:  # a secondary workload of the benchmark (full or compact form)
+        e = bench["secondary"][entry]
+        alg = e["algorithmic_bytes"] if "algorithmic_bytes" in e else e["bytes"]
+        workload = f"{entry}: {e['workload']}" if "workload" in e else entry
     else:
         alg = bench["config"]["algorithmic_bytes_per_step"]
         workload = bench["config"]["workload"]
