@@ -75,17 +75,16 @@ constexpr int storage_bits(int dt) {
 
 constexpr int max_of(int a, int b) { return a > b ? a : b; }
 
-// The 8-slot partial-input variant at one vector per lane fits 8 waves per
-// SIMD in VGPRs but, left alone, takes more SGPRs than 8 waves allow (eight
-// buffer resources next to the kernel arguments); asking for 8 waves moves
-// the excess into VGPR lanes, which keeps two 16-wave workgroups per CU.
-// Not for the block-scaled outputs, whose extra registers would then spill
-// to scratch memory.
-constexpr int min_waves_per_eu(int nv, int kp, int qs) { return kp == 8 && nv == 1 && qs == kQRow ? 8 : 1; }
+// The partial-input variants at one vector per lane fit 8 waves per SIMD in
+// VGPRs but, left alone, can take more SGPRs than 8 waves allow (a buffer
+// resource per slot next to the kernel arguments, plus the scale and amax
+// resources of the block-scaled outputs); asking for 8 waves moves the excess
+// into VGPR lanes, which keeps two 16-wave workgroups per CU.
+constexpr int min_waves_per_eu(int nv, int kp) { return kp > 1 && nv == 1 ? 8 : 1; }
 
 template <int XD, int RD, int WD, int OD, int QS, int BIAS, int NV, int KP>
 __global__ __launch_bounds__(max_threads_for_nv(NV))
-__attribute__((amdgpu_waves_per_eu(min_waves_per_eu(NV, KP, QS)))) void rows_kernel(const RowArgs a) {
+__attribute__((amdgpu_waves_per_eu(min_waves_per_eu(NV, KP)))) void rows_kernel(const RowArgs a) {
   constexpr int XB = storage_bits(XD) / 8;
   constexpr int VEC = 16 / XB;
   constexpr bool HAS_RES = RD != kNone;
@@ -131,10 +130,13 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(NV, KP, QS)))) void rows_ker
   // it as the lane's offset of chunk (0, 0) plus a per-chunk term, so that the
   // chunk term of step 0 is a constant folded into the instructions' immediate
   // offsets instead of one offset register per chunk and tensor (those
-  // kernels are the ones short of registers).
+  // kernels are the ones short of registers).  They also rebuild the lane
+  // offset before the output stage (le below), so that the store and scale
+  // offsets are derived there instead of being held across the whole row.
   const uint32_t lane_elem = static_cast<uint32_t>((wave * SUB * 64 + lane) * U);
+  uint32_t le = lane_elem;
   auto elem_of = [&](int s, int c) -> uint32_t {
-    if constexpr (KP > 1) return lane_elem + static_cast<uint32_t>((s * nw * SUB + c) * 64 * U);
+    if constexpr (KP > 1) return le + static_cast<uint32_t>((s * nw * SUB + c) * 64 * U);
     return static_cast<uint32_t>((((s * nw + wave) * SUB + c) * 64 + lane) * U);
   };
 
@@ -161,9 +163,12 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(NV, KP, QS)))) void rows_ker
     uint32_t xw[NV][SUB][KP][XW];
     uint32_t rw[NV][SUB][HAS_RES ? RW : 1];
     uint32_t ww[NV][SUB][WW];
-    // The partial-input kernels load the weight only after the sums (it is a
-    // cache hit, first needed for the weighted products or the scaling): at
-    // the sums the loaded partials hold most of their registers.
+    // The partial-input kernels load the weight after the first chunk's sums
+    // (it is a cache hit, first needed for the weighted products or the
+    // scaling): before them the loaded partials hold most of their registers.
+    // The loads go ahead of the first residual store, because the vector
+    // memory counter retires in issue order: a weight load issued after the
+    // stores could only be waited for together with them.
     constexpr bool LATE_W = KP > 1;
     if constexpr (KP > 1) {
 #pragma unroll
@@ -239,6 +244,13 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(NV, KP, QS)))) void rows_ker
               hr[i] = add_last_and_round<false>(acc, element<XD>(xw[s][c][KP - 1], i));
             }
           }
+          if (s == 0 && c == 0) {
+#pragma unroll
+            for (int s2 = 0; s2 < NV; ++s2) {
+#pragma unroll
+              for (int c2 = 0; c2 < SUB; ++c2) buffer_load_words<WW * 4, false>(wr, elem_of(s2, c2) * WB, ww[s2][c2]);
+            }
+          }
           if constexpr (HAS_RES) {
             uint32_t hw[RW];
             pack<RD, U>(hr, hw);
@@ -277,11 +289,6 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(NV, KP, QS)))) void rows_ker
     }
 
     if constexpr (LATE_W) {
-#pragma unroll
-      for (int s = 0; s < NV; ++s) {
-#pragma unroll
-        for (int c = 0; c < SUB; ++c) buffer_load_words<WW * 4, false>(wr, elem_of(s, c) * WB, ww[s][c]);
-      }
       if constexpr (QUANT) {
 #pragma unroll
         for (int s = 0; s < NV; ++s) {
@@ -322,6 +329,13 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_eu(NV, KP, QS)))) void rows_ker
     // 4. Scale and store.  Scale groups (per 128, 32 or 16 elements) are GL
     //    neighbouring lanes of one chunk: their max is a DPP group reduction,
     //    and the group's first lane stores its scale (and amax).
+    if constexpr (KP > 1) {
+      // an empty asm that hides le's value from the optimizer: offsets
+      // derived from it below stay here instead of being hoisted out of the
+      // row loop (where they would occupy VGPRs through the loads)
+      le = lane_elem;
+      asm volatile("" : "+v"(le));
+    }
     float amax = 0.f, qmul = 0.f;
     if constexpr (ROW_MAX) {
       amax = mx * inv;  // == max |p * inv|: multiplying by inv > 0 is monotone

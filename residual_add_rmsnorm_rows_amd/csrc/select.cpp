@@ -339,10 +339,13 @@ static rn_status select_parts_shape(int64_t rows, int64_t hidden, const RowKey& 
   }
   if (w > kMaxWavesPerRow)
     return fail(RN_ERR_UNSUPPORTED, "no partial-input variant holds %lld lane vectors", (long long)nvec);
-  const bool block_scaled = (key.out == kFP8 || key.out == kFP4) && key.qs != kQRow;
-  // one vector per lane over 9-16 waves: 8 x 2 holds the row too (nvec <= 1024)
-  if (nv == 1 && w > 8 &&
-      ((block_scaled && rows > num_cus) || (w < kMaxWavesPerRow && rows > 2 * static_cast<int64_t>(num_cus)))) {
+  // One vector per lane over 9-15 waves, the count not a multiple of 4, past
+  // 2 rows per CU: 8 x 2, which holds the row too (nvec <= 1024).  Measured
+  // on MI355X with 2-8 partials and bf16, fp8 per-128 and MXFP4 outputs:
+  // 14 x 1 ran up to 14% behind 8 x 2 there, while 12 x 1 and 16 x 1 ran
+  // level with it or ahead (to 9%), and every exact fit was level or ahead
+  // at up to 2 rows per CU.
+  if (nv == 1 && w > 8 && w % 4 != 0 && rows > 2 * static_cast<int64_t>(num_cus)) {
     w = 8;
     nv = 2;
   }

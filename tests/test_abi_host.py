@@ -429,28 +429,30 @@ def test_partials_selector():
                     W, NV = c["waves_per_row"], c["vecs_per_lane"]
                     assert NV in (1, 2) and 1 <= W <= 16 and 64 * W * NV * vec >= hidden, (x, n, hidden, rows, c)
                     assert c["grid"] == rows
-    # the rule (no table): the exact fit at one vector per lane at every row
-    # count; 9-15 waves past 2 rows per CU, and block-scaled outputs past 8
-    # waves with more rows than CUs, as 8 x 2
+    # the rule (no table), the same for every output type: the exact fit at
+    # one vector per lane, except 9-15 waves that are not a multiple of 4,
+    # past 2 rows per CU, as 8 x 2
     def shape(rows, hidden, n, **kw):
         c = R.query_partials_config(rows, hidden, n, res_dtype="f32", num_cus=256, **kw)
         return c["waves_per_row"], c["vecs_per_lane"]
 
-    assert shape(2048, 8192, 8) == (16, 1)
-    assert shape(3840, 8192, 4) == (16, 1)
-    assert shape(3072, 7168, 7) == (8, 2)   # 14 x 1 leaves wave slots idle
-    assert shape(512, 7168, 4) == (14, 1)   # up to 2 rows per CU: the exact fit
-    assert shape(256, 4096, 4) == (8, 1)
-    assert shape(32, 8192, 8) == (16, 1)    # decode: up to 16 waves
+    for kw in ({}, {"out_dtype": "fp8_e4m3fn"}, {"out_dtype": "fp8_e4m3fn", "scale_scheme": "group128"},
+               {"out_dtype": "fp8_e4m3fn", "scale_scheme": "mx32"}, {"out_dtype": "fp4_e2m1", "scale_scheme": "mx32"},
+               {"out_dtype": "fp4_e2m1", "scale_scheme": "nv16"}):
+        assert shape(2048, 8192, 8, **kw) == (16, 1), kw
+        assert shape(5120, 8192, 2, **kw) == (16, 1), kw
+        assert shape(3840, 8192, 4, **kw) == (16, 1), kw
+        assert shape(3072, 7168, 7, **kw) == (8, 2), kw    # 14 x 1 runs behind
+        assert shape(513, 7168, 2, **kw) == (8, 2), kw
+        assert shape(512, 7168, 4, **kw) == (14, 1), kw   # up to 2 rows per CU: the exact fit
+        assert shape(4096, 6144, 8, **kw) == (12, 1), kw  # 12 x 1 runs level or ahead
+        assert shape(4096, 5120, 8, **kw) == (8, 2), kw   # 10 waves
+        assert shape(256, 4096, 4, **kw) == (8, 1), kw
+        assert shape(4096, 4096, 8, **kw) == (8, 1), kw
+        assert shape(32, 8192, 8, **kw) == (16, 1), kw    # decode: up to 16 waves
+        assert shape(64, 16384, 8, **kw) == (16, 2), kw
+        assert shape(2048, 12288, 8, **kw) == (12, 2), kw
     assert shape(8, 2048, 2) == (4, 1)
-    assert shape(64, 16384, 8) == (16, 2)
-    for od, scheme in (("fp8_e4m3fn", "group128"), ("fp8_e4m3fn", "mx32"), ("fp4_e2m1", "mx32"),
-                       ("fp4_e2m1", "nv16")):
-        for n, hidden in ((8, 8192), (2, 8192), (2, 7168)):
-            assert shape(2048, hidden, n, out_dtype=od, scale_scheme=scheme) == (8, 2), (od, scheme, n, hidden)
-            assert shape(256, hidden, n, out_dtype=od, scale_scheme=scheme)[1] == 1
-        assert shape(4096, 4096, 8, out_dtype=od, scale_scheme=scheme) == (8, 1)
-        assert shape(2048, 12288, 8, out_dtype=od, scale_scheme=scheme) == (12, 2)
     assert shape(2048, 8192, 8, out_dtype="fp8_e4m3fn") == (16, 1)
     # one partial is the single-input kernel and its tables
     assert R.query_partials_config(8192, 7168, 1, res_dtype="bf16", out_dtype="fp8_e4m3fn") == \

@@ -90,13 +90,13 @@ def test_workload_full_size_sampled():
 
 def test_block_scaled_full_size_sampled():
     """2048 x 8192 with 8 partials and MXFP4 output in the selector's launch
-    configuration (8 waves x 2 vectors per lane); the oracle checks sampled
+    configuration (16 waves x 1 vector per lane); the oracle checks sampled
     rows, including the first and the last."""
     from dataclasses import replace
 
     wl = replace(WL.WORKLOADS["partials_8x2048x8192"], out_dtype="fp4_e2m1")
     cfg = R.query_partials_config(wl.rows, wl.hidden, 8, res_dtype="f32", out_dtype="fp4_e2m1", scale_scheme="mx32")
-    assert (cfg["waves_per_row"], cfg["vecs_per_lane"]) == (8, 2)
+    assert (cfg["waves_per_row"], cfg["vecs_per_lane"]) == (16, 1)
     _announce(f"partials full size MXFP4 cfg={cfg}")
     inp = WL.generate_partials(wl, seed=0)
     parts = [to_dev(p, wl.x_dtype) for p in inp["partials"]]
