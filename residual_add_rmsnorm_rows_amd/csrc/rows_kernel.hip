@@ -75,16 +75,18 @@ constexpr int storage_bits(int dt) {
 
 constexpr int max_of(int a, int b) { return a > b ? a : b; }
 
-// The partial-input variants at one vector per lane fit 8 waves per SIMD in
-// VGPRs but, left alone, can take more SGPRs than 8 waves allow (a buffer
-// resource per slot next to the kernel arguments, plus the scale and amax
-// resources of the block-scaled outputs); asking for 8 waves moves the excess
-// into VGPR lanes, which keeps two 16-wave workgroups per CU.
-constexpr int min_waves_per_eu(int nv, int kp) { return kp > 1 && nv == 1 ? 8 : 1; }
+// At one vector per lane a row takes up to 16 waves, and two such workgroups
+// per CU need 8 waves per SIMD.  Every variant fits that in VGPRs, but some,
+// left alone, take more SGPRs than 8 waves allow (a buffer resource per
+// partial-input slot, the scale and amax resources of the block-scaled
+// outputs, next to the kernel arguments) and then run one workgroup per CU:
+// on MI355X the block-scaled outputs with a float32 residual at 16 x 1 ran
+// 11% slower that way.  Asking for 8 waves moves the excess into VGPR lanes.
+constexpr int min_waves_per_eu(int nv) { return nv == 1 ? 8 : 1; }
 
 template <int XD, int RD, int WD, int OD, int QS, int BIAS, int NV, int KP>
 __global__ __launch_bounds__(max_threads_for_nv(NV))
-__attribute__((amdgpu_waves_per_eu(min_waves_per_eu(NV, KP)))) void rows_kernel(const RowArgs a) {
+__attribute__((amdgpu_waves_per_eu(min_waves_per_eu(NV)))) void rows_kernel(const RowArgs a) {
   constexpr int XB = storage_bits(XD) / 8;
   constexpr int VEC = 16 / XB;
   constexpr bool HAS_RES = RD != kNone;

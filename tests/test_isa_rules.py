@@ -83,19 +83,23 @@ def test_no_packed_fp32_instructions(device_asm):
     assert not {k: v for k, v in bad.items() if v}
 
 
-# rows_kernel<x, res, w, out, scheme, bias, NV, KP> with KP in {2, 4, 8}
-PARTIAL_INPUT_ROWS_KERNEL = re.compile(r"rows_kernelI(?:Li\d+E){7}Li[248]EEEvNS_7RowArgsE$")
+# rows_kernel<x, res, w, out, scheme, bias, NV, KP> with NV == 1 (these ask
+# for 8 waves per SIMD) or KP in {2, 4, 8} (a buffer resource per slot): the
+# compiler may move SGPRs past the budget into VGPR lanes (v_writelane /
+# v_readlane, no memory); VGPR spills and scratch memory stay forbidden
+# everywhere
+SGPR_LANE_SPILL_OK = re.compile(r"rows_kernelI(?:Li\d+E){6}(?:Li1ELi\d+|Li\d+ELi[248])EEEvNS_7RowArgsE$")
 
 
 def test_no_register_spills(device_asm):
-    n_partial = 0
+    n_exempt = 0
     for name, text in device_asm.items():
         kernels = KERNEL_NAME.findall(text)
-        n_partial += sum(1 for k in kernels if PARTIAL_INPUT_ROWS_KERNEL.search(k))
+        n_exempt += sum(1 for k in kernels if SGPR_LANE_SPILL_OK.search(k))
         for key, pat in META.items():
             values = [int(v) for v in pat.findall(text)]
             assert len(values) == len(kernels), f"{name}: {key} missing for some kernel"
             bad = [k for k, v in zip(kernels, values)
-                   if v and not (key == "sgpr_spill_count" and PARTIAL_INPUT_ROWS_KERNEL.search(k))]
+                   if v and not (key == "sgpr_spill_count" and SGPR_LANE_SPILL_OK.search(k))]
             assert not bad, f"{name}: nonzero {key} in {bad}"
-    assert n_partial > 0  # the exemption names kernels that exist
+    assert n_exempt > 0  # the exemption names kernels that exist
