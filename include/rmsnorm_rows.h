@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define RN_ABI_VERSION 3
+#define RN_ABI_VERSION 4
 
 typedef enum rn_status {
   RN_OK = 0,
@@ -195,6 +195,34 @@ rn_status rmsnorm_fwd(const void* x, const void* residual, const void* weight, v
 rn_status rmsnorm_fwd_ex(const void* x, const void* residual, const void* weight, void* out,
                          void* residual_out, void* out_scale, float* out_amax, const float* tensor_scale,
                          int64_t rows, int64_t hidden, float eps, uint32_t flags, void* stream);
+
+/*
+ * One rmsnorm_fwd_ex call described by a record, for the decode path of
+ * "Prefill & decode specialization" (a call whose cost should stay near that
+ * of a bare launch): a caller that issues the same call many times (a serving
+ * loop outside graph capture) fills the record once and passes its address,
+ * one argument to marshal per call instead of thirteen.  Each field means
+ * what the rmsnorm_fwd_ex argument of the same name means, with the same
+ * checks and errors; the library reads the record during the call only and
+ * keeps no pointer to it.  call == NULL gives RN_ERR_INVALID_ARG.
+ */
+typedef struct rn_rmsnorm_call {
+  const void* x;
+  const void* residual;
+  const void* weight;
+  void* out;
+  void* residual_out;
+  void* out_scale;
+  float* out_amax;
+  const float* tensor_scale;
+  int64_t rows;
+  int64_t hidden;
+  float eps;
+  uint32_t flags;
+  void* stream;
+} rn_rmsnorm_call;
+
+rn_status rmsnorm_fwd_call(const rn_rmsnorm_call* call);
 
 /* As rmsnorm_fwd_ex, with an explicit launch configuration instead of the
  * selector's (for tuning and for testing every kernel variant).  The launch

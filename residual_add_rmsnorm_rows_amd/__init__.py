@@ -190,20 +190,21 @@ class PreparedCall:
 
     For decode-sized calls issued many times on the same buffers (a serving
     loop outside graph capture): the tensors, flags, sizes and stream are
-    converted to ctypes values when the object is built, so a call is a
-    single foreign-function call with no tensor inspection, output
-    allocation or stream lookup.  ``result`` holds the output tensors, which
-    every call overwrites.  The object keeps its tensors alive.
+    written into the library's call record (``rn_rmsnorm_call``) when the
+    object is built, so a call is a single foreign-function call with one
+    argument, and no tensor inspection, output allocation or stream lookup.
+    ``result`` holds the output tensors, which every call overwrites.  The
+    object keeps its tensors alive.
     """
 
-    def __init__(self, fn, args, result, keep):
+    def __init__(self, fn, arg, result, keep):
         self._fn = fn
-        self._args = args
+        self._arg = arg
         self.result = result
         self._keep = keep
 
     def __call__(self):
-        st = self._fn(*self._args)
+        st = self._fn(self._arg)
         if st:
             check(st)
         return self.result
@@ -223,16 +224,14 @@ def prepare_fused_add_rmsnorm(x: torch.Tensor, residual: Optional[torch.Tensor],
     rows, H, out, residual_out, scale, amax, ts, flags = _rows_setup(
         x, residual, weight, weight_plus_one, out_dtype, out, residual_out, return_amax, scale_scheme, tensor_scale)
     s = stream.cuda_stream if stream is not None else _stream(x.device)
-    vp = ctypes.c_void_p
-    args = (vp(_p(x)), vp(_p(residual)), vp(_p(weight)), vp(_p(out)), vp(_p(residual_out)), vp(_p(scale)),
-            vp(_p(amax)), vp(_p(ts)), ctypes.c_int64(rows), ctypes.c_int64(H), ctypes.c_float(eps),
-            ctypes.c_uint32(flags), vp(s))
-    # the library's entry point without per-call argument conversion: every
-    # argument above is already a ctypes value of the declared C type
-    fn = ctypes.CFUNCTYPE(ctypes.c_int, *_lib._SIGNATURES["rmsnorm_fwd_ex"][0])(
-        ctypes.cast(lib().rmsnorm_fwd_ex, ctypes.c_void_p).value)
+    rec = _lib.RmsnormCall(_p(x), _p(residual), _p(weight), _p(out), _p(residual_out), _p(scale), _p(amax), _p(ts),
+                           rows, H, eps, flags, s)
+    # the entry point called through a prototype whose argument is already of
+    # the declared type: no conversion per call
+    fn = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.POINTER(_lib.RmsnormCall))(
+        ctypes.cast(lib().rmsnorm_fwd_call, ctypes.c_void_p).value)
     result = NormOutput(out, residual_out, scale, amax)
-    call = PreparedCall(fn, args, result, (x, residual, weight, ts))
+    call = PreparedCall(fn, ctypes.pointer(rec), result, (x, residual, weight, ts, rec))
     call()  # a first call: any argument error is raised here
     return call
 

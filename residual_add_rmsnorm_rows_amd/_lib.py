@@ -45,8 +45,9 @@ EXPORTED_SYMBOLS = (
     "rmsnorm_query_config", "qknorm_query_config", "silu_mul_fwd", "silu_mul_fwd_config",
     "silu_mul_query_config", "rn_launch_empty", "rn_launch_copy", "rn_status_string", "rn_last_error",
     "rn_abi_version", "rmsnorm_fwd_partials", "rmsnorm_fwd_partials_config", "rmsnorm_partials_query_config",
+    "rmsnorm_fwd_call",
 )
-ABI_VERSION = 3
+ABI_VERSION = 4
 MAX_PARTIALS = 8
 
 
@@ -79,6 +80,25 @@ class LaunchConfig(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
 
 
+class RmsnormCall(ctypes.Structure):
+    """rn_rmsnorm_call: the arguments of one rmsnorm_fwd_ex call."""
+    _fields_ = [
+        ("x", ctypes.c_void_p),
+        ("residual", ctypes.c_void_p),
+        ("weight", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("residual_out", ctypes.c_void_p),
+        ("out_scale", ctypes.c_void_p),
+        ("out_amax", ctypes.c_void_p),
+        ("tensor_scale", ctypes.c_void_p),
+        ("rows", ctypes.c_int64),
+        ("hidden", ctypes.c_int64),
+        ("eps", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
@@ -89,6 +109,7 @@ _fp = ctypes.POINTER(ctypes.c_float)
 _SIGNATURES = {
     "rmsnorm_fwd": ([_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _u32, _vp], ctypes.c_int),
     "rmsnorm_fwd_ex": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _u32, _vp], ctypes.c_int),
+    "rmsnorm_fwd_call": ([ctypes.POINTER(RmsnormCall)], ctypes.c_int),
     "rmsnorm_fwd_config": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _u32,
                             ctypes.POINTER(LaunchConfig), _vp], ctypes.c_int),
     "qknorm_fwd": ([_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i64, _f32, _u32, _vp],

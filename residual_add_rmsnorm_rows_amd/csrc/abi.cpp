@@ -298,6 +298,15 @@ rn_status rmsnorm_fwd_ex(const void* x, const void* residual, const void* weight
                     rows, hidden, eps, flags, nullptr, stream);
 }
 
+rn_status rmsnorm_fwd_call(const rn_rmsnorm_call* c) {
+  if (c == nullptr) {
+    clear_error();
+    return fail(RN_ERR_INVALID_ARG, "call record is NULL");
+  }
+  return rows_entry(false, c->x, nullptr, 0, c->residual, c->weight, c->out, c->residual_out, c->out_scale,
+                    c->out_amax, c->tensor_scale, c->rows, c->hidden, c->eps, c->flags, nullptr, c->stream);
+}
+
 rn_status rmsnorm_fwd_config(const void* x, const void* residual, const void* weight, void* out,
                              void* residual_out, void* out_scale, float* out_amax,
                              const float* tensor_scale, int64_t rows, int64_t hidden, float eps,

@@ -309,23 +309,18 @@ static rn_status select_rows_shape(int64_t rows, int64_t hidden, const RowKey& k
 // Partial-input kernels (KP > 1, exact sums).  A sweep of every shape of up
 // to 16 waves and 1-2 vectors per lane on MI355X (2, 4 and 8 bf16 partials;
 // f32 or bf16 residual; bf16, per-row fp8 and MXFP4 outputs; 2048-16384 wide;
-// 8, 64, 256, 512 and 1024 rows and ~0.6 GB prefill calls; 150 cases) found
-// the exact fit at one vector per lane best or within 3% in most cases, and
-// no table needed:
+// 8-1024 rows and ~0.6 GB prefill calls; 150 cases) found the exact fit at
+// one vector per lane best or within 3% in most cases, and no table needed:
 //   * the exact fit at one vector per lane (two past 16 waves), at every
 //     row count -- the exact sums give a lane more arithmetic than the
 //     single-input kernel, so decode rows spread over up to 16 waves (16 x 1
 //     beat 8 x 2 by 6-13% at 8 and 64 rows x 8192 with 4-8 partials);
-//   * block-scaled outputs past 8 waves, with more rows than CUs: 8 waves
-//     with 2 vectors per lane.  Their kernels take too many registers for
-//     two such workgroups per CU (8 x 2 measured 4-15% faster than 16 x 1
-//     from 512 rows on; 16 x 1 was 6% faster at 256);
-//   * a fit of 9-15 waves with more than 2 rows per CU: 8 waves x 2 vectors
-//     when they hold the row.  Such workgroups leave wave slots of a CU idle
-//     (14 x 1 at 7168 wide ran 9-15% behind 8 x 2 at 1024 rows, 2-6% at
-//     prefill sizes).
+//   * a fit of 9-15 waves, not a multiple of 4, with more than 2 rows per
+//     CU: 8 waves x 2 vectors, which hold the row too.
 // Against each case's best shape: geometric mean 1.003, worst 1.047 (the
-// replaced table and rules: 1.026 and 1.225).
+// replaced table and rules: 1.026 and 1.225).  Every output type takes the
+// same rule since the one-vector kernels all fit two 16-wave workgroups per
+// CU (a second sweep: 6144-8192 wide, 384 rows to ~0.6 GB calls).
 static rn_status select_parts_shape(int64_t rows, int64_t hidden, const RowKey& key, int num_cus,
                                     rn_launch_config* cfg) {
   if (num_cus < 1) return fail(RN_ERR_INVALID_ARG, "num_cus must be >= 1");

@@ -43,6 +43,17 @@ int main(void) {
   EXPECT(rmsnorm_fwd(p, p, p, q, q, NULL, 4, 1001, 1e-6f, flags, NULL) == RN_ERR_UNSUPPORTED);
   EXPECT(rmsnorm_fwd(NULL, NULL, NULL, NULL, NULL, NULL, 0, 1024, 1e-6f, flags, NULL) == RN_OK);
   EXPECT(rn_launch_copy(p, q, 1000, NULL) == RN_ERR_INVALID_ARG);
+  /* the call-record form: the same checks */
+  rn_rmsnorm_call call;
+  memset(&call, 0, sizeof call);
+  call.x = p; call.residual = p; call.weight = p; call.out = q; call.rows = 4; call.hidden = 1024;
+  call.eps = 1e-6f; call.flags = flags;
+  EXPECT(rmsnorm_fwd_call(&call) == RN_ERR_INVALID_ARG); /* residual_out missing */
+  call.residual_out = q; call.hidden = 1001;
+  EXPECT(rmsnorm_fwd_call(&call) == RN_ERR_UNSUPPORTED);
+  EXPECT(rmsnorm_fwd_call(NULL) == RN_ERR_INVALID_ARG);
+  call.rows = 0; call.hidden = 1024;
+  EXPECT(rmsnorm_fwd_call(&call) == RN_OK);
 
   /* partial inputs: a host array of device pointers */
   const void* parts[3] = {p, p, (const void*)(uintptr_t)0x30008};

@@ -82,6 +82,48 @@ def test_workload_parity_small(name):
     assert rep["ok"], rep
 
 
+@pytest.mark.parametrize("name,out_dtype,scheme", [("decode_8x1024", None, "row"), ("decode_256x4096", None, "row"),
+                                                    ("prefill_fp8_8192x7168", None, "row"),
+                                                    ("prefill_fp8_8192x7168", "fp8_e4m3fn", "mx32"),
+                                                    ("prefill_fp8_8192x7168", "fp4_e2m1", "nv16")])
+def test_prepared_call(name, out_dtype, scheme):
+    """prepare_fused_add_rmsnorm (the library's call record, rmsnorm_fwd_call):
+    every call re-reads its buffers, so new inputs copied into them between
+    calls give the oracle's outputs for those inputs, bit-identical to
+    fused_add_rmsnorm's on the same inputs."""
+    from dataclasses import replace
+
+    wl = WL.WORKLOADS[name]
+    if out_dtype is not None:
+        wl = replace(wl, out_dtype=out_dtype)
+    wl = wl.with_rows(min(wl.rows, 64))
+    quant = wl.out_dtype in ("fp8_e4m3fn", "fp4_e2m1")
+    _announce(f"prepared call {name} out={wl.out_dtype}/{scheme} rows={wl.rows}")
+    seeds = [WL.generate_rownorm(wl, seed=s) for s in (0, 1, 2)]
+    for inputs in seeds[1:]:
+        inputs["weight"] = seeds[0]["weight"]  # the weight buffer is part of the prepared call
+    ts = nvfp4_tensor_scale(oracle_y(wl, seeds[0])) if scheme == "nv16" else None
+    x = to_dev(seeds[0]["x"], wl.x_dtype)
+    res = to_dev(seeds[0]["residual"], wl.res_dtype)
+    w = to_dev(seeds[0]["weight"], wl.w_dtype)
+    call = R.prepare_fused_add_rmsnorm(x, res, w, wl.eps, weight_plus_one=wl.weight_plus_one,
+                                       out_dtype=TORCH_DTYPES[wl.out_dtype], return_amax=quant, scale_scheme=scheme,
+                                       tensor_scale=ts)
+    for inputs in seeds[1:] + seeds[:1]:
+        x.copy_(to_dev(inputs["x"], wl.x_dtype))
+        res.copy_(to_dev(inputs["residual"], wl.res_dtype))
+        r = call()
+        torch.cuda.synchronize()
+        rep = judge(wl, inputs, r, scale_scheme=scheme, tensor_scale=ts)
+        assert rep["ok"], rep
+        ref = run_rownorm(wl, inputs, scale_scheme=scheme, tensor_scale=ts)
+        for a, b in ((r.out, ref.out), (r.residual_out, ref.residual_out), (r.scale, ref.scale),
+                     (r.amax, ref.amax)):
+            assert (a is None) == (b is None)
+            if a is not None:
+                assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
 @pytest.mark.parametrize("name", ["prefill_16384x8192", "prefill_fp8_8192x7168", "decode_256x4096"])
 def test_workload_parity_full_size_sampled(name):
     """Full-size workload in the benchmark's launch configuration (the
