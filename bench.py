@@ -108,7 +108,7 @@ SCHEME_TEXT = {"row": "a float32 scale amax/448 per row", "group128": "a float32
                "nv16": "an E4M3FN scale per 16 elements and a float32 tensor scale (NVFP4)"}
 # NVFP4 tensor scales: fixed values near amax / (6 * 448) of each workload's
 # outputs (any positive value is a valid input; the traffic does not depend on it).
-ACT_WARMUP = 200  # launches before the SwiGLU lines are timed (about 20 ms of load)
+POWER_WARMUP = 200  # launches before the SwiGLU and partial-input lines are timed (15-20 ms of load)
 NV_TENSOR_SCALE = {"prefill_fp8_8192x7168": 2.0 ** -5, "silu_mul_8192x14336": 2.0 ** -7}
 QUANT_TEXT = {"fp8_e4m3fn": "fp8 e4m3fn", "fp4_e2m1": "fp4 e2m1"}
 
@@ -478,7 +478,8 @@ def partials_metrics(name: str, steps: int, warmup: int, sets: int = 2, out_dtyp
     b = partials_bytes(wl, scale_scheme)
     return {"workload": desc, "out": wl.out_dtype, "scale_scheme": scale_scheme, "us_per_call": round(ms * 1000, 3),
             "algorithmic_bytes": b, "GBps": round(b / (ms * 1e-3) / 1e9, 1),
-            "frac_of_peak": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "buffer_sets": sets, "launch_us": spread}
+            "frac_of_peak": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "buffer_sets": sets, "warmup": warmup,
+            "launch_us": spread}
 
 
 def partials_decode_metrics(name: str) -> dict:
@@ -892,18 +893,19 @@ def main() -> int:
                                                         out_dtype="fp4_e2m1", scale_scheme="mx32")
         sec["prefill_8192x7168_nvfp4"] = stream_metrics("prefill_fp8_8192x7168", args.steps, args.warmup, sets=3,
                                                         out_dtype="fp4_e2m1", scale_scheme="nv16")
+        # the kernels of the next two groups do more arithmetic per byte (exact
+        # sums; silu and block scales): the GPU's power management lowers clocks
+        # for a few ms once such a load starts, so these lines are timed after a
+        # warm-up long enough to reach steady state
+        aw = max(args.warmup, POWER_WARMUP)
         log("partials_8x2048x8192")
-        sec["partials_8x2048x8192"] = partials_metrics("partials_8x2048x8192", args.steps * 2, args.warmup)
-        sec["partials_8x2048x8192_mxfp4"] = partials_metrics("partials_8x2048x8192", args.steps * 2, args.warmup,
+        sec["partials_8x2048x8192"] = partials_metrics("partials_8x2048x8192", args.steps * 2, aw)
+        sec["partials_8x2048x8192_mxfp4"] = partials_metrics("partials_8x2048x8192", args.steps * 2, aw,
                                                              out_dtype="fp4_e2m1", scale_scheme="mx32")
         if not args.no_decode:
             log("partials_decode_8x64x8192")
             decode["partials_decode_8x64x8192"] = partials_decode_metrics("partials_decode_8x64x8192")
         log("silu_mul_8192x14336")
-        # the quantized variants do more arithmetic per byte; the GPU's power
-        # management lowers clocks for a few ms after such a load starts, so
-        # these lines are timed after a warm-up long enough to reach steady state
-        aw = max(args.warmup, ACT_WARMUP)
         sec["silu_mul_8192x14336"] = act_metrics(args.steps, aw)
         sec["silu_mul_8192x14336_mxfp8"] = act_metrics(args.steps, aw, "fp8_e4m3fn", "mx32")
         sec["silu_mul_8192x14336_mxfp4"] = act_metrics(args.steps, aw, "fp4_e2m1", "mx32")
