@@ -1,11 +1,12 @@
 /* Randomized host-side calls of the C ABI (C99), meant to run under
  * AddressSanitizer and UBSan: the configuration queries and the argument checks
- * of the rows, partial-input, SwiGLU and per-head entry points, with random
- * sizes, flags, counts and explicit configurations.  Every pointer is a fake,
- * never-dereferenced address.  No call can reach a kernel launch: every
- * explicit configuration has grid = rows + 1, which the checks reject (and
- * rows == 0 returns before launching), so this is safe on a machine with a
- * GPU and needs none.  Checks that every configuration the queries accept
+ * of the rows (also through the call record), partial-input, SwiGLU and
+ * per-head entry points, with random sizes, flags, counts and explicit
+ * configurations.  Every pointer is a fake, never-dereferenced address.  No
+ * call can reach a kernel launch: every explicit configuration has
+ * grid = rows + 1 and every call record a residual without residual_out,
+ * which the checks reject (and rows == 0 returns before launching), so this
+ * is safe on a machine with a GPU and needs none.  Checks that every configuration the queries accept
  * covers the row.  Exit status 0 on success. */
 #include <stdio.h>
 #include <stdint.h>
@@ -37,6 +38,11 @@ int main(void) {
     rn_launch_config c = {0, 0, (int32_t)(rnd() % 20) - 2, 1 << (rnd() % 5), 0, 0, 0, 0, rows + 1};
     rmsnorm_fwd_config((void*)0x1000, NULL, (void*)0x1000, (void*)0x2000, NULL, NULL, NULL, NULL, rows, hidden, 1e-6f,
                        flags, &c, NULL);
+    /* the call record: a residual without residual_out is always rejected (rows == 0 returns first) */
+    rn_rmsnorm_call rec = {(void*)0x1000, (void*)0x3000, (void*)0x1000, (void*)0x2000, NULL, NULL, NULL, NULL,
+                           rows, hidden, 1e-6f, flags, NULL};
+    if (rmsnorm_fwd_call(&rec) == RN_OK && rows != 0) { printf("call record bug\n"); return 1; }
+    if (rmsnorm_fwd_call(NULL) != RN_ERR_INVALID_ARG) { printf("call record NULL bug\n"); return 1; }
     /* partial inputs: random counts (including out of range), explicit configs, queries */
     const void* parts[9] = {(void*)0x10000, (void*)0x20000, (void*)0x30000, (void*)0x40000, (void*)0x50000,
                             (void*)0x60000, (void*)0x70000, (void*)0x80000, (void*)0x90000};
