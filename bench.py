@@ -203,6 +203,24 @@ def time_stream_loop(fn, steps: int, warmup: int) -> float:
     return start.elapsed_time(end) / steps
 
 
+def time_prepared_loop(call, steps: int, warmup: int) -> float:
+    """time_stream_loop for a prepared call (its stream is bound when it is
+    prepared): the loop calls it the way a caller does, call()."""
+    import torch
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        call()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
 def launch_percentiles(fn, launches: int = 50) -> dict:
     """p10 / p50 / p90 of single-launch durations (each launch between its own
     pair of events on the launch stream), in microseconds."""
@@ -319,7 +337,7 @@ def decode_metrics(name: str) -> dict:
     prepared = R.prepare_fused_add_rmsnorm(to_dev(inp["x"], wl.x_dtype), to_dev(inp["residual"], wl.res_dtype),
                                            to_dev(inp["weight"], wl.w_dtype), wl.eps,
                                            weight_plus_one=wl.weight_plus_one)
-    py_eager = time_stream_loop(lambda stream: prepared(), 2000, 100) * 1000.0
+    py_eager = time_prepared_loop(prepared, 2000, 100) * 1000.0
     # the one-wave-per-row decode shape (the whole row in one wave64's
     # registers, no LDS, no barrier), timed the same way for comparison
     vec = 8 if wl.x_dtype == "bf16" else 4

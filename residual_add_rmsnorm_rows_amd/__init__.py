@@ -197,6 +197,8 @@ class PreparedCall:
     object keeps its tensors alive.
     """
 
+    __slots__ = ("_fn", "_arg", "result", "_keep")
+
     def __init__(self, fn, arg, result, keep):
         self._fn = fn
         self._arg = arg
