@@ -22,7 +22,8 @@
  * block-scaled schemes of RN_SCALE_* below (fp8 per 128 elements; MX per 32,
  * fp8 or fp4 E2M1; NVFP4 per 16).  Neither the residual add nor the quantized
  * outputs' formulas are on the pages; both follow the plain reading stated
- * for each entry point below.
+ * for each entry point below.  rmsnorm_fwd_call takes the same call as one
+ * record, for callers that repeat a decode call on fixed buffers.
  *
  * qknorm_fwd applies the same RMSNorm to every (token, head) row of Q and K
  * over head_dim, with one weight vector per tensor shared by all heads, as in
