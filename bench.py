@@ -954,9 +954,12 @@ def main() -> int:
     log(f"headline {MAIN}: {result['value']} GB/s = {result['roofline']['frac']:.4f} of 8 TB/s, "
         f"{result['ceiling']['value_over_ceiling']:.3f} of the same-run copy")
     for k, v in result.get("decode", {}).items():
-        log(f"decode {k} ({v['launch']}): graph {v['graph_us']} us = {v['graph_ratio']}x empty; "
-            f"C-ABI eager {v.get('c_abi_eager_us')} us = {v.get('c_abi_eager_ratio')}x; "
-            f"Python prepared {v.get('python_prepared_us')} us = {v.get('python_prepared_ratio')}x")
+        parts = [f"graph {v['graph_us']} us = {v['graph_ratio']}x empty"]
+        if v.get("c_abi_eager_us") is not None:
+            parts.append(f"C-ABI eager {v['c_abi_eager_us']} us = {v['c_abi_eager_ratio']}x")
+        if v.get("python_prepared_us") is not None:
+            parts.append(f"Python prepared {v['python_prepared_us']} us = {v['python_prepared_ratio']}x")
+        log(f"decode {k} ({v['launch']}): " + "; ".join(parts))
     order = ["metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
              "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline", "decode", "ceiling"]
     result = {**{k: result[k] for k in order if k in result}, **{k: v for k, v in result.items() if k not in order}}
