@@ -57,7 +57,7 @@ def _fwd(lib, x=FAKE, res=FAKE, w=FAKE, out=FAKE + 0x1000, res_out=FAKE + 0x2000
     return lib.rmsnorm_fwd_ex(x, res, w, out, res_out, scale, amax, ts, rows, hidden, eps, flags, None)
 
 
-@pytest.mark.parametrize("kw,status", [
+REJECT_CASES = [
     (dict(rows=-1), L.RN_ERR_INVALID_ARG),
     (dict(hidden=0), L.RN_ERR_INVALID_ARG),
     (dict(flags=BF | (1 << 9)), L.RN_ERR_INVALID_ARG),
@@ -86,10 +86,30 @@ def _fwd(lib, x=FAKE, res=FAKE, w=FAKE, out=FAKE + 0x1000, res_out=FAKE + 0x2000
     (dict(out=FAKE, flags=L.make_flags("bf16", "bf16", "bf16", "fp8_e4m3fn", False), scale=FAKE + 0x3000),
      L.RN_ERR_INVALID_ARG),
     (dict(out=FAKE, flags=FP4_MX_FLAGS, scale=FAKE + 0x3000), L.RN_ERR_INVALID_ARG),
-])
+]
+
+
+@pytest.mark.parametrize("kw,status", REJECT_CASES)
 def test_rmsnorm_rejects_before_any_hip_call(lib, kw, status):
     assert _fwd(lib, **kw) == status
     assert lib.rn_last_error().decode() != ""
+
+
+def _call(lib, x=FAKE, res=FAKE, w=FAKE, out=FAKE + 0x1000, res_out=FAKE + 0x2000, scale=None, amax=None,
+          ts=None, rows=4, hidden=1024, eps=1e-6, flags=BF):
+    rec = L.RmsnormCall(x, res, w, out, res_out, scale, amax, ts, rows, hidden, eps, flags, None)
+    return lib.rmsnorm_fwd_call(ctypes.byref(rec))
+
+
+@pytest.mark.parametrize("kw,status", REJECT_CASES)
+def test_call_record_checks_like_rmsnorm_fwd_ex(lib, kw, status):
+    assert _call(lib, **kw) == status
+    assert lib.rn_last_error().decode() != ""
+
+
+def test_call_record_null_and_zero_rows(lib):
+    assert lib.rmsnorm_fwd_call(None) == L.RN_ERR_INVALID_ARG
+    assert _call(lib, x=None, res=None, w=None, out=None, res_out=None, rows=0) == L.RN_OK
 
 
 def _qflags(out, scheme, x="bf16", res="bf16"):
